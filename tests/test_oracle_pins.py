@@ -1,0 +1,279 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compares the oracle with itself: each check is a hand-expanded
+closed form, an algebraic identity stated on the pages, a special case that
+reduces to a library routine, or an invariant that follows from the
+definition of the transition H_t = I - beta_t w_t w_t^T.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import oracle
+
+
+def _rand(seed, L, d, *, gate=False, BH=1, unit_w=True):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((BH, L, d))
+    k = rng.standard_normal((BH, L, d))
+    v = rng.standard_normal((BH, L, d))
+    w = rng.standard_normal((BH, L, d))
+    if unit_w:
+        w /= np.linalg.norm(w, axis=-1, keepdims=True)
+    beta = 2.0 / (1.0 + np.exp(-rng.standard_normal((BH, L))))
+    log_f = -np.logaddexp(0.0, -(3.0 + rng.standard_normal((BH, L)))) if gate else None
+    return q, k, v, w, beta, log_f
+
+
+def _all_rows(L, BH=1):
+    h, r = np.meshgrid(np.arange(BH), np.arange(L), indexing="ij")
+    return h.ravel(), r.ravel()
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_two_transition_closed_form(gate):
+    """k_0^T H_1 H_2 q_2 expanded by hand (order matters through the cross
+    term beta_1 beta_2 (k.w1)(w1.w2)(w2.q)); PaTH logit definition, Dutch
+    summary section 2 and Chinese notes, overall framework."""
+    q, k, v, w, beta, log_f = _rand(3, 3, 5, gate=gate)
+    q, k, v, w, beta = q[0], k[0], v[0], w[0], beta[0]
+    lf = log_f[0] if gate else np.zeros(3)
+    s = 0.37
+    b1, b2 = beta[1], beta[2]
+    w1, w2 = w[1], w[2]
+    exp = np.full((3, 3), np.nan)
+    exp[0, 0] = s * k[0] @ q[0]
+    exp[1, 0] = s * (k[0] @ q[1] - b1 * (k[0] @ w1) * (w1 @ q[1])) + lf[1]
+    exp[1, 1] = s * k[1] @ q[1]
+    exp[2, 0] = s * (k[0] @ q[2] - b1 * (k[0] @ w1) * (w1 @ q[2])
+                     - b2 * (k[0] @ w2) * (w2 @ q[2])
+                     + b1 * b2 * (k[0] @ w1) * (w1 @ w2) * (w2 @ q[2])) + lf[1] + lf[2]
+    exp[2, 1] = s * (k[1] @ q[2] - b2 * (k[1] @ w2) * (w2 @ q[2])) + lf[2]
+    exp[2, 2] = s * k[2] @ q[2]
+    # the wrong product order gives a different value (the pin is sensitive)
+    wrong = s * (k[0] @ q[2] - b1 * (k[0] @ w1) * (w1 @ q[2])
+                 - b2 * (k[0] @ w2) * (w2 @ q[2])
+                 + b1 * b2 * (k[0] @ w2) * (w2 @ w1) * (w1 @ q[2])) + lf[1] + lf[2]
+    assert abs(wrong - exp[2, 0]) > 1e-6
+
+    lfa = log_f if gate else None
+    _, _, lg, _ = oracle.rows(q[None], k[None], v[None], w[None], beta[None], lfa,
+                              s, [0, 0, 0], [0, 1, 2], want_logits=True)
+    low = np.tril_indices(3)
+    np.testing.assert_allclose(lg[low], exp[low], rtol=0, atol=1e-13)
+    bf = oracle.bruteforce_logits(q, k, w, beta, lf if gate else None, s)
+    np.testing.assert_allclose(bf[low], exp[low], rtol=0, atol=1e-13)
+
+    # outputs and lse against a library softmax of the closed-form logits
+    out, lse, _, _ = oracle.recurrent(q[None], k[None], v[None], w[None],
+                                      beta[None], lfa, s)
+    for i in range(3):
+        p = softmax(exp[i, :i + 1])
+        np.testing.assert_allclose(out[0, i], p @ v[:i + 1], atol=1e-13)
+        np.testing.assert_allclose(lse[0, i], logsumexp(exp[i, :i + 1]), atol=1e-13)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_recurrent_rows_and_explicit_products_agree(gate, seed):
+    """Three evaluations of the same quantity: explicit d x d matrix products
+    (the definition), the query carried leftwards (the definition evaluated
+    as matrix-vector products) and the in-place key-update recurrence (the
+    pages' inference form)."""
+    L, d, BH = 24, 6, 2
+    q, k, v, w, beta, log_f = _rand(10 + seed, L, d, gate=gate, BH=BH)
+    s = 1.0 / np.sqrt(d)
+    out_r, lse_r, _, _ = oracle.recurrent(q, k, v, w, beta, log_f, s)
+    hi, ri = _all_rows(L, BH)
+    out_w, lse_w, lg_w, _ = oracle.rows(q, k, v, w, beta, log_f, s, hi, ri,
+                                        want_logits=True)
+    for h in range(BH):
+        bf = oracle.bruteforce_logits(q[h], k[h], w[h], beta[h],
+                                      None if log_f is None else log_f[h], s)
+        o_bf, lse_bf = oracle.softmax_from_logits(bf, v[h])
+        np.testing.assert_allclose(out_r[h], o_bf, atol=1e-12)
+        np.testing.assert_allclose(lse_r[h], lse_bf, atol=1e-12)
+        sl = slice(h * L, (h + 1) * L)
+        np.testing.assert_allclose(out_w[sl], o_bf, atol=1e-12)
+        np.testing.assert_allclose(lse_w[sl], lse_bf, atol=1e-12)
+        m = np.isfinite(bf)
+        np.testing.assert_allclose(lg_w[sl][m], bf[m], atol=1e-12)
+        assert np.all(np.isnan(lg_w[sl][~m]))
+        # library logsumexp of the explicit logits
+        np.testing.assert_allclose(lse_bf, logsumexp(bf, axis=-1), atol=1e-12)
+
+
+def test_ut_identity_orientation():
+    """UT transform: I - W^T T^{-1} W with T^{-1} = (I + strictLower(DWW^T))^{-1}
+    D equals the product of the transitions (Chinese notes, training strategy).
+    With strictLower the product is H_{L-1} ... H_0 (H_0 applied first)."""
+    rng = np.random.default_rng(5)
+    L, d = 9, 6
+    w = rng.standard_normal((L, d))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    beta = rng.uniform(0.05, 1.95, L)
+    P = np.eye(d)
+    for t in range(L):
+        P = oracle.transition(w[t], beta[t]) @ P
+    np.testing.assert_allclose(oracle.ut_product(w, beta), P, atol=1e-13)
+    Pr = np.eye(d)
+    for t in range(L):
+        Pr = Pr @ oracle.transition(w[t], beta[t])
+    assert np.max(np.abs(oracle.ut_product(w, beta) - Pr)) > 1e-2
+    # T^{-1} is lower triangular with diagonal beta
+    tinv = oracle.ut_tinv(w, beta)
+    np.testing.assert_allclose(np.triu(tinv, 1), 0.0, atol=0)
+    np.testing.assert_allclose(np.diag(tinv), beta, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_full_matrix_form_matches_definition(seed):
+    """lower(QK^T) - lower(QW^T) T^{-1} strictLower(WK^T) (Chinese notes,
+    training strategy) equals the explicit-product logits."""
+    L, d = 20, 5
+    q, k, v, w, beta, _ = _rand(20 + seed, L, d)
+    s = 0.5
+    fm = oracle.full_matrix_logits(q[0], k[0], w[0], beta[0], s)
+    bf = oracle.bruteforce_logits(q[0], k[0], w[0], beta[0], None, s)
+    m = np.isfinite(bf)
+    assert np.array_equal(m, np.isfinite(fm))
+    np.testing.assert_allclose(fm[m], bf[m], atol=1e-12)
+
+
+def _sdpa_f64(q, k, v, scale, bias=None):
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    L = q.shape[-2]
+    causal = torch.ones(L, L, dtype=torch.bool).tril()
+    mask = torch.zeros(L, L, dtype=torch.float64).masked_fill(~causal, float("-inf"))
+    if bias is not None:
+        mask = mask + torch.from_numpy(bias)
+    return torch.nn.functional.scaled_dot_product_attention(
+        q, k, v, attn_mask=mask, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_beta_zero_is_softmax_attention(gate):
+    """beta = 0 makes every H_t the identity: PaTH reduces to causal softmax
+    attention, and PaTH-FoX to softmax attention with the additive forget-gate
+    bias sum_{s=j+1}^{i} log f_s (Chinese notes, PaTH-FoX)."""
+    L, d, BH = 40, 8, 3
+    q, k, v, w, beta, log_f = _rand(7, L, d, gate=gate, BH=BH)
+    beta = np.zeros_like(beta)
+    s = 1.0 / np.sqrt(d)
+    out, _, _, _ = oracle.recurrent(q, k, v, w, beta, log_f, s)
+    hi, ri = _all_rows(L, BH)
+    out_w, _, _, _ = oracle.rows(q, k, v, w, beta, log_f, s, hi, ri)
+    for h in range(BH):
+        bias = None
+        if gate:
+            F = np.cumsum(log_f[h])
+            bias = F[:, None] - F[None, :]
+            bias = np.where(np.tril(np.ones((L, L), bool)), bias, 0.0)
+        ref = _sdpa_f64(q[h], k[h], v[h], s, bias)
+        np.testing.assert_allclose(out[h], ref, atol=1e-12)
+        np.testing.assert_allclose(out_w[h * L:(h + 1) * L], ref, atol=1e-12)
+
+
+def test_zero_log_gate_equals_ungated():
+    L, d = 30, 8
+    q, k, v, w, beta, _ = _rand(8, L, d)
+    s = 0.3
+    a, la, _, _ = oracle.recurrent(q, k, v, w, beta, None, s)
+    b, lb, _, _ = oracle.recurrent(q, k, v, w, beta, np.zeros_like(beta), s)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(la, lb)
+
+
+def test_reflection_preserves_key_norms():
+    """beta = 2 with unit w makes H_t a reflection (orthogonal), so the
+    in-place updated keys keep their norms."""
+    L, d = 50, 8
+    q, k, v, w, beta, _ = _rand(9, L, d)
+    beta = np.full_like(beta, 2.0)
+    _, _, kc, _ = oracle.recurrent(q, k, v, w, beta, None, 0.3, Lcache=L)
+    np.testing.assert_allclose(np.linalg.norm(kc[0], axis=-1),
+                               np.linalg.norm(k[0], axis=-1), rtol=1e-13)
+    # and the cache really changed (the update is not a no-op)
+    assert np.max(np.abs(kc[0, :-1] - k[0, :-1])) > 0.1
+
+
+@pytest.mark.parametrize("b", [0.7, 1.0, 1.6])
+def test_repeated_direction_closed_form(b):
+    """With w_t = u (unit) and beta_t = b for every t, H^n = I + ((1-b)^n - 1)
+    u u^T, so cache entry j after step T is k_j + ((1-b)^(T-j) - 1)(u.k_j) u.
+    b = 1 is the projection case (H^2 = H)."""
+    L, d = 40, 6
+    q, k, v, w, beta, _ = _rand(11, L, d)
+    u = w[0, 0].copy()
+    w[0, :] = u
+    beta[:] = b
+    T = L - 1
+    _, _, kc, _ = oracle.recurrent(q, k, v, w, beta, None, 0.3, Lcache=L)
+    n = T - np.arange(L)
+    exp = k[0] + (((1 - b) ** n - 1) * (k[0] @ u))[:, None] * u[None, :]
+    np.testing.assert_allclose(kc[0], exp, atol=1e-12)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_first_transition_never_enters(gate):
+    """The product runs over s = j+1..i (0-based), so H_0, beta_0 and f_0 never
+    enter any logit."""
+    L, d = 32, 8
+    q, k, v, w, beta, log_f = _rand(12, L, d, gate=gate)
+    s = 0.35
+    a, la, _, _ = oracle.recurrent(q, k, v, w, beta, log_f, s)
+    w2, b2 = w.copy(), beta.copy()
+    w2[0, 0] = -w2[0, 0][::-1]
+    b2[0, 0] = 1.9 - b2[0, 0] * 0.5
+    f2 = None
+    if gate:
+        f2 = log_f.copy()
+        f2[0, 0] = -50.0
+    b, lb, _, _ = oracle.recurrent(q, k, v, w2, b2, f2, s)
+    np.testing.assert_allclose(a, b, atol=1e-13)
+    np.testing.assert_allclose(la, lb, atol=1e-13)
+    hi, ri = _all_rows(L)
+    c, lc, _, _ = oracle.rows(q, k, v, w2, b2, f2, s, hi, ri)
+    np.testing.assert_allclose(a[0], c, atol=1e-13)
+
+
+def test_forget_gate_cuts_the_past():
+    """f_t = 0 (log f_t = -1e4) hides every key j < t from queries i >= t but
+    keeps key t itself (its weight carries f_{t+1}..f_i only); those rows then
+    equal PaTH over the suffix starting at t, whose own first gate is unused."""
+    L, d, t = 36, 8, 13
+    q, k, v, w, beta, log_f = _rand(13, L, d, gate=True)
+    s = 0.35
+    lf = log_f.copy()
+    lf[0, t] = -1e4
+    full, _, _, _ = oracle.recurrent(q, k, v, w, beta, lf, s)
+    sub_f = lf[:, t:].copy()
+    sub_f[0, 0] = 0.0
+    sub, _, _, _ = oracle.recurrent(q[:, t:], k[:, t:], v[:, t:], w[:, t:],
+                                    beta[:, t:], sub_f, s)
+    np.testing.assert_allclose(full[0, t:], sub[0], atol=1e-12)
+
+
+def test_decode_continuation_and_cache():
+    """Inference form: the cache after the prefill holds H_{L-1}...H_{j+1} k_j
+    (each key carried forward one transition at a time), and decode rows
+    t >= L equal the definition's rows."""
+    L, extra, d, BH = 40, 9, 8, 2
+    q, k, v, w, beta, log_f = _rand(14, L + extra, d, BH=BH)
+    s = 0.3
+    out, lse, kc, _ = oracle.recurrent(q, k, v, w, beta, None, s, Lcache=L)
+    hi, ki = _all_rows(L, BH)
+    tk = oracle.transported_keys(k, w, beta, L - 1, hi, ki)
+    np.testing.assert_allclose(kc.reshape(-1, d), tk, atol=1e-12)
+    # explicit matrices for a couple of cache entries
+    for j in (0, 17, L - 1):
+        M = np.eye(d)
+        for t in range(j + 1, L):
+            M = oracle.transition(w[1, t], beta[1, t]) @ M
+        np.testing.assert_allclose(kc[1, j], M @ k[1, j], atol=1e-12)
+    rr = np.arange(L, L + extra)
+    for h in range(BH):
+        o2, l2, _, _ = oracle.rows(q, k, v, w, beta, None, s, [h] * extra, rr)
+        np.testing.assert_allclose(out[h, L:], o2, atol=1e-12)
+        np.testing.assert_allclose(lse[h, L:], l2, atol=1e-12)
