@@ -1,0 +1,235 @@
+#!/usr/bin/env python
+"""Throughput of the PaTH attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one full forward pass (path_attn_fwd_prepare: per-chunk UT
+transform; path_attn_fwd_scan: right-to-left scan) over one batch of
+synthetic inputs already resident in HBM.  Default workload: PaTH-FoX,
+B=8, H=24, L=4096, d=64, bf16.  With --workload d128_L8k_decode the step is
+one decode step (in-place key-cache update + one-token attention) and the
+256 steps after an L=8192, d=128 prefill are timed.
+
+Prints one JSON line: effective TFLOP/s (2*B*H*L^2*d per forward), tokens/s,
+the roofline of the dominant kernel (HIP events on its launch stream) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+MFMA_BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
+
+
+def flop_model(B, H, L, d, C=64):
+    """Algorithmic FLOPs of one forward (per the blockwise method with chunk C):
+    attention over the causal triangle, the low-rank query transport through
+    every full chunk strictly between query and key chunk, the diagonal-chunk
+    extras done by the scan kernel, and the per-chunk UT work of prepare."""
+    N = (L + C - 1) // C
+    f_eff = 2.0 * L * L * d
+    f_transport = 4.0 * C * C * d * (N - 1) * (N - 2) / 2.0
+    f_diag = N * (4.0 * C * C * d + 2.0 * C ** 3)
+    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3)
+    BH = B * H
+    return {"eff": BH * f_eff, "scan": BH * (f_eff + f_transport + f_diag),
+            "alg": BH * (f_eff + f_transport + f_prep)}
+
+
+def _kernel_sha(name):
+    with open(os.path.join(ROOT, "softmax_attention_ut_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(profile_md, kernel_src):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, only if
+    it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", profile_md)
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    if not m or not h or h.group(1) != _kernel_sha(kernel_src):
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(inp, cfg, threads):
+    """The fp64 oracle (recurrent form), unmodified, on the first `threads`
+    heads of the same inputs; extrapolated to the whole job."""
+    import oracle
+    n = threads
+    sl = lambda t: None if t is None else t.reshape(-1, *t.shape[2:])[:n]
+    t0 = time.perf_counter()
+    _, _, _, used = oracle.recurrent(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.w), sl(inp.beta),
+                                     sl(inp.log_f), cfg.scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    BH = cfg.B * cfg.H
+    t_full = dt * BH / n
+    f = flop_model(cfg.B, cfg.H, cfg.L, cfg.d)
+    return {"value": f["eff"] / t_full / 1e12, "unit": "TFLOP/s (effective)",
+            "cores": used, "kind": "oracle",
+            "tokens_per_s": cfg.B * cfg.L / t_full,
+            "sample": f"{n} of {BH} heads, all {cfg.L} rows, fp64 recurrent oracle, "
+                      f"{dt:.2f} s wall; job time extrapolated x{BH / n:.1f}"}
+
+
+def bench_fwd(args, cfg, torch, pa, inputs):
+    inp = inputs.generate_config(cfg)
+    g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    nbytes = pa.path_attn_fwd_workspace_bytes(B, H, L, d, pa.PATH_BF16, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(g["q"])
+    lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        pa.path_attn_fwd_prepare(g["k"], g["v"], g["w"], g["beta"], g["log_f"], 0, ws, stream)
+        if ev:
+            ev[1].record(stream)
+        pa.path_attn_fwd_scan(g["q"], g["k"], g["v"], g["w"], g["log_f"], out, lse, cfg.scale,
+                              0, ws, stream)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    f = flop_model(B, H, L, d)
+    achieved = f["scan"] / (scan_ms * 1e-3) / 1e12
+    traffic = _traffic("path_fwd_bf16_fox_L4k.md", "path_fwd_bf16.hip")
+    res = {
+        "metric": "PaTH fwd effective TFLOP/s + tokens/s (bf16, L=4096, d=64) and % MFMA peak",
+        "value": f["eff"] / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: 2*B*H*L^2*d per forward)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: PaTH-FoX forward B={B} H={H} L={L} d={d} "
+                               f"bf16, chunk 64" if cfg.gate else
+                               f"{cfg.name}: PaTH forward B={B} H={H} L={L} d={d} bf16",
+                   "global_batch": B, "seq_len": L, "heads": H, "head_dim": d,
+                   "forget_gate": cfg.gate, "parallelism": "single GPU"},
+        "tokens_per_s": B * L / (ms * 1e-3),
+        "tflops_algorithmic": f["alg"] / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac_algorithmic": f["alg"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "stage_ms": {"prepare(path_ut)": prep_ms, "scan(path_fwd)": scan_ms},
+        "roofline": {"kernel": "path_fwd_bf16_kernel<64,gate>", "bound": "mfma",
+                     "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic,
+                     "algorithmic_flops_per_launch": f["scan"]},
+    }
+    return res, inp
+
+
+def bench_decode(args, cfg, torch, pa, inputs):
+    inp = inputs.generate_config(cfg)
+    g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
+    B, H, L, T, d = cfg.B, cfg.H, cfg.L, cfg.L_total, cfg.d
+    pre = lambda t: t[:, :, :L].contiguous()
+    kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
+    steps_in = [{k: g[k][:, :, t].contiguous() for k in ("q", "k", "v", "w", "beta")}
+                for t in range(L, T)]
+    ws = pa.decode_workspace(B, H, T, d, pa.PATH_BF16, kc.device)
+    o = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
+    ls = torch.empty(B, H, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    kc0, vc0 = kc.clone(), vc.clone()
+    n = min(args.steps, T - L) if args.steps else T - L
+    n = T - L if n <= 0 else n
+    # warmup on a copy of the cache, then restore
+    for i in range(min(args.warmup, n)):
+        s = steps_in[i]
+        pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, L + i,
+                            cfg.scale, ws, stream)
+    kc.copy_(kc0)
+    vc.copy_(vc0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(n):
+        s = steps_in[i]
+        pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, L + i,
+                            cfg.scale, ws, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / n
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    bytes_total = sum(B * H * ((L + i) * d * 2 * 3 + 4 * d * 2) for i in range(n))
+    gbs = bytes_total / (sum(step_ms) * 1e-3) / 1e9
+    res = {
+        "metric": "PaTH decode tokens/s and HBM GB/s (bf16, d=128, in-place key update)",
+        "value": B * n / (wall), "unit": "tokens/s",
+        "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {n} PaTH decode steps after a prefill of "
+                               f"L={L}, B={B} H={H} d={d}, bf16 K/V cache",
+                   "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
+        "roofline": {"kernel": "path_decode_split_kernel<128> + combine", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+    }
+    return res, None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="fox_L4k")
+    ap.add_argument("--cpu-threads", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the PaTH hot path is data-parallel over "
+              "independent (batch, head) pairs and this build runs on a single MI355X; "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import softmax_attention_ut_amd as pa
+    from softmax_attention_ut_amd import inputs
+    pa.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cfg = inputs.CONFIGS[args.workload]
+    if args.workload == "d128_L8k_decode":
+        res, inp = bench_decode(args, cfg, torch, pa, inputs)
+    else:
+        res, inp = bench_fwd(args, cfg, torch, pa, inputs)
+    if inp is not None and not args.no_cpu_baseline:
+        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, cfg.B * cfg.H))
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, threads)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * path_attn.h -- C ABI of the MI355X (gfx950) PaTH attention library
+ * (libpath_attn.so).
+ *
+ * PaTH attention ("PaTH Attention: Position Encoding via Accumulating
+ * Householder Transformations"): causal softmax attention whose logit between
+ * query i and key j <= i is
+ *
+ *     scale * k_j^T (H_{j+1} H_{j+2} ... H_i) q_i  [+ sum_{s=j+1}^{i} log f_s]
+ *
+ * with data-dependent transitions H_t = I - beta_t w_t w_t^T (Dutch technical
+ * summary section 2, "Kernmechanisme"; Chinese notes, "overall framework" and
+ * "key design"), the optional bracketed term being the PaTH-FoX forget gate
+ * (Chinese notes, "PaTH-FoX").  Indices are 0-based, so H_0, beta_0 and f_0
+ * never enter a logit.  The scale multiplies only the bilinear term.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named q/k/v/w/out/k_cache/v_cache/workspace/beta/log_f/lse are
+ *     DEVICE pointers (HIP device memory, or any pointer the device can
+ *     read/write); all sizes are element counts unless named *_bytes.
+ *   - Tensors are contiguous, row-major, [B][H][L][d] (per-token vectors) or
+ *     [B][H][L] (per-token scalars).  Rows must be 16-byte aligned (d * elem
+ *     size is a multiple of 16 for every supported d).
+ *   - dtype: PATH_F32 (q,k,v,w,out in float32) or PATH_BF16 (bfloat16).
+ *     beta, log_f and lse are always float32.
+ *   - The caller owns every buffer, including the workspace; the library
+ *     allocates nothing and keeps no global state, so calls on different
+ *     streams with different workspaces may run concurrently.  Calls that
+ *     share a workspace or a cache race unless ordered by the caller.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Argument checks run on the host before any HIP call;
+ *     a negative path_status_t is returned and nothing is launched.  A failed
+ *     launch returns PATH_ERR_HIP.
+ *   - beta is used as given (no clipping); log_f holds log f_t (<= 0 for a
+ *     forget gate, any finite value is accepted).
+ */
+#ifndef PATH_ATTN_H
+#define PATH_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PATH_F32 = 0, PATH_BF16 = 1 } path_dtype_t;
+
+typedef enum {
+    PATH_OK = 0,
+    PATH_ERR_INVALID = -1,      /* null pointer, bad size, bad dtype */
+    PATH_ERR_UNSUPPORTED = -2,  /* valid but not implemented (d, chunk) */
+    PATH_ERR_HIP = -3,          /* a HIP launch or runtime call failed */
+    PATH_ERR_WORKSPACE = -4     /* workspace missing or too small */
+} path_status_t;
+
+/* Human-readable text for a status code (static storage). */
+const char* path_status_string(int status);
+
+/* Library version string (static storage). */
+const char* path_version(void);
+
+/*
+ * Workspace size in bytes needed by path_attn_fwd for these sizes, or 0 if
+ * the arguments are invalid/unsupported.  chunk: 0 = library default.
+ */
+size_t path_attn_fwd_workspace_bytes(int B, int H, int L, int d, int dtype,
+                                     int chunk);
+
+/*
+ * PaTH attention forward (prefill) for all B*H heads.
+ *
+ * Computes, per head and every row i < L,
+ *     out_i = sum_{j<=i} softmax_j(logit_ij) v_j,   lse_i = log sum_j exp(logit_ij)
+ * with logit_ij as in the file header, using the pages' blockwise algorithm:
+ * per chunk of `chunk` tokens the product of its transitions is held in the
+ * UT-transform form I - W^T T^{-1} W, T^{-1} = (I + strictLower(D W W^T))^{-1} D
+ * (Chinese notes, training strategy), and each query tile scans the key
+ * chunks right to left, carrying the query through every chunk it passes
+ * (Dutch summary section 3, FlashAttention-style algorithm).
+ *
+ *   q, k, v, w  [B][H][L][d] dtype.  w need not be unit-norm.
+ *   beta        [B][H][L] float32.
+ *   log_f       [B][H][L] float32, or NULL for PaTH without the forget gate.
+ *   out         [B][H][L][d] dtype (written).
+ *   lse         [B][H][L] float32 natural-log log-sum-exp, or NULL.
+ *   d           PATH_BF16: 64 or 128.  PATH_F32: 16, 32, 64 (and 128 with
+ *               chunk <= 32).
+ *   chunk       0 = default (64 for bf16, 16 for f32 with d <= 32, else 32);
+ *               PATH_BF16 supports 64, PATH_F32 supports 16, 32, 64.
+ *   L >= 1 (any length: a ragged last chunk is padded internally); B, H >= 1.
+ *   workspace   at least path_attn_fwd_workspace_bytes(...) bytes, 256-byte
+ *               aligned; its contents on entry are ignored.
+ * Inputs are not modified.
+ */
+int path_attn_fwd(const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_f,
+                  void* out, float* lse,
+                  int B, int H, int L, int d, float scale,
+                  int dtype, int chunk,
+                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * The two stages of path_attn_fwd, for callers that time or schedule them
+ * separately.  Same arguments, layouts and errors as path_attn_fwd.
+ *
+ * path_attn_fwd_prepare: the per-chunk stage (the pages' boundary-adjusted
+ *   keys computed beforehand, Dutch summary section 3): the UT transform of
+ *   every chunk and the chunk-local forget-gate sums, written to `workspace`.
+ *   Reads k, v, w, beta, log_f.
+ * path_attn_fwd_scan: the right-to-left scan of each query tile over the key
+ *   chunks (Dutch summary section 3), reading q and the workspace written by
+ *   a preceding path_attn_fwd_prepare with the same B, H, L, d, dtype, chunk
+ *   and the same log_f presence (the workspace must not be modified in
+ *   between).  Writes out and lse.
+ */
+int path_attn_fwd_prepare(const void* k, const void* v, const void* w,
+                          const float* beta, const float* log_f,
+                          int B, int H, int L, int d, int dtype, int chunk,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* w,
+                       const float* log_f, void* out, float* lse,
+                       int B, int H, int L, int d, float scale,
+                       int dtype, int chunk,
+                       const void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for path_kcache_from_prefill, or 0 if invalid.
+ */
+size_t path_kcache_workspace_bytes(int B, int H, int L, int d, int dtype);
+
+/*
+ * Key/value cache after a prefill of L tokens, for the decode steps that
+ * follow (Dutch summary section 3, "Inferentie": cached keys are updated in
+ * place, so no separate cache of transition vectors is kept).
+ *
+ *   k_cache[b][h][j] = H_{L-1} ... H_{j+1} k_j   for j < L   (written)
+ *   v_cache[b][h][j] = v_j                       for j < L   (written)
+ * Slots j >= L are not touched.
+ *   k, v, w     [B][H][L][d] dtype;  beta [B][H][L] float32.
+ *   k_cache, v_cache  [B][H][T_max][d] dtype, T_max >= L.
+ *   dtype       PATH_BF16 with d in {64, 128}.
+ *   workspace   >= path_kcache_workspace_bytes(B,H,L,d,dtype) bytes.
+ */
+int path_kcache_from_prefill(const void* k, const void* v, const void* w,
+                             const float* beta, void* k_cache, void* v_cache,
+                             int B, int H, int L, int T_max, int d, int dtype,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for path_decode_step, or 0 if invalid.
+ */
+size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype);
+
+/*
+ * One decode step at position t (Dutch summary section 3, "Inferentie";
+ * Chinese notes, inference paragraph): every cached key is first updated in
+ * place with the new transition,
+ *     k_cache[j] <- (I - beta_t w_t w_t^T) k_cache[j]     for j < t,
+ * then k_t, v_t are stored at slot t, and q_t attends over slots 0..t:
+ *     out_t = sum_{j<=t} softmax_j(scale * q_t . k_cache[j]) v_cache[j].
+ * The updated keys are written back in the cache dtype (rounded to nearest
+ * even for bf16).  No forget gate.
+ *
+ *   k_cache, v_cache  [B][H][T_max][d] dtype; slots [0,t) updated in place,
+ *                     slot t written.
+ *   q_t, k_t, v_t, w_t  [B][H][d] dtype;  beta_t [B][H] float32.
+ *   out_t       [B][H][d] dtype;  lse_t [B][H] float32 or NULL.
+ *   0 <= t < T_max.  dtype PATH_BF16 with d in {64, 128}.
+ *   workspace   >= path_decode_workspace_bytes(B,H,T_max,d,dtype) bytes.
+ */
+int path_decode_step(void* k_cache, void* v_cache,
+                     const void* q_t, const void* k_t, const void* v_t,
+                     const void* w_t, const float* beta_t,
+                     void* out_t, float* lse_t,
+                     int B, int H, int t, int T_max, int d, float scale,
+                     int dtype, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PATH_ATTN_H */

@@ -1,0 +1,229 @@
+"""PaTH attention for MI355X (gfx950): Python binding of libpath_attn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libpath_attn.so (C ABI in include/path_attn.h).  PyTorch provides
+device memory and streams.  There is no CPU fallback: if the library is
+missing or no GPU is present, calls raise.
+
+Functions with the C names take torch tensors (device memory) and pass raw
+pointers; ``attention`` / ``kcache_from_prefill`` / ``decode_step`` are
+conveniences that allocate outputs and workspaces with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libpath_attn.so")
+
+PATH_F32, PATH_BF16 = 0, 1
+PATH_OK = 0
+STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size or chunk",
+          -3: "HIP runtime or launch error", -4: "workspace missing or too small"}
+
+# every symbol declared in include/path_attn.h
+EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes",
+           "path_attn_fwd", "path_attn_fwd_prepare", "path_attn_fwd_scan",
+           "path_kcache_workspace_bytes", "path_kcache_from_prefill",
+           "path_decode_workspace_bytes", "path_decode_step")
+
+
+class PathError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(status, 'unknown')} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpath_attn.so (torch is imported first so that the library binds
+    to the same HIP runtime as torch)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m softmax_attention_ut_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.path_status_string.restype = ctypes.c_char_p
+    lib.path_status_string.argtypes = [I]
+    lib.path_version.restype = ctypes.c_char_p
+    lib.path_version.argtypes = []
+    lib.path_attn_fwd_workspace_bytes.restype = S
+    lib.path_attn_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.path_attn_fwd.restype = I
+    lib.path_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
+    lib.path_attn_fwd_prepare.restype = I
+    lib.path_attn_fwd_prepare.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, S, P]
+    lib.path_attn_fwd_scan.restype = I
+    lib.path_attn_fwd_scan.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
+    lib.path_kcache_workspace_bytes.restype = S
+    lib.path_kcache_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.path_kcache_from_prefill.restype = I
+    lib.path_kcache_from_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, S, P]
+    lib.path_decode_workspace_bytes.restype = S
+    lib.path_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.path_decode_step.restype = I
+    lib.path_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    _lib = lib
+    return lib
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PATH_F32
+    if t.dtype == torch.bfloat16:
+        return PATH_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(st: int, where: str):
+    if st != PATH_OK:
+        raise PathError(st, where)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+# ---------------------------------------------------------------------------
+# C-ABI names
+# ---------------------------------------------------------------------------
+
+def path_attn_fwd_workspace_bytes(B, H, L, d, dtype, chunk=0) -> int:
+    return load_library().path_attn_fwd_workspace_bytes(B, H, L, d, dtype, chunk)
+
+
+def path_attn_fwd(q, k, v, w, beta, log_f, out, lse, scale, chunk=0,
+                  workspace=None, stream=None):
+    """q,k,v,w,out [B,H,L,d]; beta, log_f (or None), lse (or None) [B,H,L]."""
+    lib = load_library()
+    _require_cuda(q, k, v, w, beta, log_f, out, lse, workspace)
+    B, H, L, d = q.shape
+    dt = _dt(q)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_attn_fwd(_p(q), _p(k), _p(v), _p(w), _p(beta), _p(log_f), _p(out),
+                           _p(lse), B, H, L, d, float(scale), dt, int(chunk),
+                           _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_attn_fwd")
+
+
+def path_attn_fwd_prepare(k, v, w, beta, log_f, chunk=0, workspace=None, stream=None):
+    """The per-chunk UT-transform stage of path_attn_fwd (fills workspace)."""
+    lib = load_library()
+    _require_cuda(k, v, w, beta, log_f, workspace)
+    B, H, L, d = k.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_attn_fwd_prepare(_p(k), _p(v), _p(w), _p(beta), _p(log_f), B, H, L, d,
+                                   _dt(k), int(chunk), _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_attn_fwd_prepare")
+
+
+def path_attn_fwd_scan(q, k, v, w, log_f, out, lse, scale, chunk=0, workspace=None,
+                       stream=None):
+    """The right-to-left scan stage of path_attn_fwd (reads workspace)."""
+    lib = load_library()
+    _require_cuda(q, k, v, w, log_f, out, lse, workspace)
+    B, H, L, d = q.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_attn_fwd_scan(_p(q), _p(k), _p(v), _p(w), _p(log_f), _p(out), _p(lse),
+                                B, H, L, d, float(scale), _dt(q), int(chunk), _p(workspace),
+                                ws_bytes, _stream(stream))
+    _check(st, "path_attn_fwd_scan")
+
+
+def path_kcache_workspace_bytes(B, H, L, d, dtype) -> int:
+    return load_library().path_kcache_workspace_bytes(B, H, L, d, dtype)
+
+
+def path_kcache_from_prefill(k, v, w, beta, k_cache, v_cache, workspace=None, stream=None):
+    """k,v,w [B,H,L,d]; beta [B,H,L]; k_cache, v_cache [B,H,T_max,d]."""
+    lib = load_library()
+    _require_cuda(k, v, w, beta, k_cache, v_cache, workspace)
+    B, H, L, d = k.shape
+    T_max = k_cache.shape[2]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_kcache_from_prefill(_p(k), _p(v), _p(w), _p(beta), _p(k_cache),
+                                      _p(v_cache), B, H, L, T_max, d, _dt(k),
+                                      _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_kcache_from_prefill")
+
+
+def path_decode_workspace_bytes(B, H, T_max, d, dtype) -> int:
+    return load_library().path_decode_workspace_bytes(B, H, T_max, d, dtype)
+
+
+def path_decode_step(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t, t,
+                     scale, workspace=None, stream=None):
+    """caches [B,H,T_max,d]; q_t,k_t,v_t,w_t,out_t [B,H,d]; beta_t, lse_t [B,H]."""
+    lib = load_library()
+    _require_cuda(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t, workspace)
+    B, H, T_max, d = k_cache.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_decode_step(_p(k_cache), _p(v_cache), _p(q_t), _p(k_t), _p(v_t), _p(w_t),
+                              _p(beta_t), _p(out_t), _p(lse_t), B, H, int(t), T_max, d,
+                              float(scale), _dt(k_cache), _p(workspace), ws_bytes,
+                              _stream(stream))
+    _check(st, "path_decode_step")
+
+
+# ---------------------------------------------------------------------------
+# conveniences (allocate with torch, then call the C ABI)
+# ---------------------------------------------------------------------------
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def attention(q, k, v, w, beta, log_f=None, scale=None, chunk=0, want_lse=True,
+              stream=None):
+    """PaTH attention forward; returns (out, lse)."""
+    B, H, L, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    n = path_attn_fwd_workspace_bytes(B, H, L, d, _dt(q), chunk)
+    if n == 0:
+        raise PathError(-2, "path_attn_fwd_workspace_bytes")
+    ws = _workspace(n, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device) if want_lse else None
+    path_attn_fwd(q, k, v, w, beta, log_f, out, lse, scale, chunk, ws, stream)
+    return out, lse
+
+
+def kcache_from_prefill(k, v, w, beta, T_max, stream=None):
+    B, H, L, d = k.shape
+    n = path_kcache_workspace_bytes(B, H, L, d, _dt(k))
+    if n == 0:
+        raise PathError(-2, "path_kcache_workspace_bytes")
+    ws = _workspace(n, k.device)
+    kc = torch.zeros(B, H, T_max, d, dtype=k.dtype, device=k.device)
+    vc = torch.zeros(B, H, T_max, d, dtype=k.dtype, device=k.device)
+    path_kcache_from_prefill(k, v, w, beta, kc, vc, ws, stream)
+    return kc, vc
+
+
+def decode_workspace(B, H, T_max, d, dtype, device):
+    n = path_decode_workspace_bytes(B, H, T_max, d, dtype)
+    if n == 0:
+        raise PathError(-2, "path_decode_workspace_bytes")
+    return _workspace(n, device)

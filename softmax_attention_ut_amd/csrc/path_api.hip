@@ -1,0 +1,222 @@
+// C ABI of libpath_attn.so: argument checks, workspace planning, launches.
+// Declarations and contracts: include/path_attn.h.
+#include "path_attn.h"
+#include "path_internal.h"
+
+using namespace path;
+
+namespace {
+
+constexpr int kBf16Chunk = 64;
+
+bool valid_dtype(int dt) { return dt == PATH_F32 || dt == PATH_BF16; }
+
+int default_chunk(int d, int dt) {
+    if (dt == PATH_BF16) return kBf16Chunk;
+    return d <= 32 ? 16 : 32;
+}
+
+// 0 = ok, else a path_status_t
+int check_fwd_shape(int B, int H, int L, int d, int dt, int& chunk) {
+    if (B < 1 || H < 1 || L < 1 || !valid_dtype(dt)) return PATH_ERR_INVALID;
+    if ((long long)B * H * L > (1LL << 31) / 4) return PATH_ERR_UNSUPPORTED;
+    if (chunk == 0) chunk = default_chunk(d, dt);
+    if (dt == PATH_BF16) {
+        if (d != 64 && d != 128) return PATH_ERR_UNSUPPORTED;
+        if (chunk != kBf16Chunk) return PATH_ERR_UNSUPPORTED;
+    } else {
+        if (d != 16 && d != 32 && d != 64 && d != 128) return PATH_ERR_UNSUPPORTED;
+        if (chunk != 16 && chunk != 32 && chunk != 64) return PATH_ERR_UNSUPPORTED;
+        if (d == 128 && chunk > 32) return PATH_ERR_UNSUPPORTED;
+    }
+    return PATH_OK;
+}
+
+Workspace fwd_plan(int B, int H, int L, int d, int dt, int chunk, bool gate, bool with_z) {
+    return plan_workspace((size_t)B * H, (size_t)L, (size_t)d, (size_t)chunk, dt == PATH_BF16,
+                          gate, with_z);
+}
+
+char* at(void* base, size_t off) { return static_cast<char*>(base) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* path_status_string(int status) {
+    switch (status) {
+        case PATH_OK: return "ok";
+        case PATH_ERR_INVALID: return "invalid argument";
+        case PATH_ERR_UNSUPPORTED: return "unsupported size or chunk";
+        case PATH_ERR_HIP: return "HIP runtime or launch error";
+        case PATH_ERR_WORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+const char* path_version(void) { return "path_attn 0.1 (gfx950)"; }
+
+size_t path_attn_fwd_workspace_bytes(int B, int H, int L, int d, int dtype, int chunk) {
+    if (check_fwd_shape(B, H, L, d, dtype, chunk) != PATH_OK) return 0;
+    // the gate sections are always reserved so one size fits both variants
+    return fwd_plan(B, H, L, d, dtype, chunk, true, false).total;
+}
+
+}  // extern "C"
+
+namespace {
+
+struct FwdPlan {
+    Workspace ws;
+    int BH, N;
+    bool gate, bf;
+};
+
+int plan_fwd(int B, int H, int L, int d, int dtype, int& chunk, bool gate, const void* workspace,
+             size_t ws_bytes, FwdPlan& p) {
+    int st = check_fwd_shape(B, H, L, d, dtype, chunk);
+    if (st != PATH_OK) return st;
+    p.ws = fwd_plan(B, H, L, d, dtype, chunk, gate, false);
+    if (!workspace || ws_bytes < p.ws.total) return PATH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return PATH_ERR_WORKSPACE;
+    p.BH = B * H;
+    p.N = (L + chunk - 1) / chunk;
+    p.gate = gate;
+    p.bf = dtype == PATH_BF16;
+    return PATH_OK;
+}
+
+UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, const float* beta,
+               const float* log_f, int L, int d, int chunk, void* workspace, bool with_z) {
+    UtArgs u{};
+    u.k = k; u.v = v; u.w = w; u.beta = beta; u.log_f = log_f;
+    u.BH = p.BH; u.L = L; u.N = p.N; u.C = chunk; u.D = d;
+    u.kt = at(workspace, p.ws.kt);
+    u.ut = at(workspace, p.ws.ut);
+    u.yt = at(workspace, p.ws.yt);
+    u.zt = with_z ? at(workspace, p.ws.zt) : nullptr;
+    u.loc = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.loc)) : nullptr;
+    u.csum = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.csum)) : nullptr;
+    return u;
+}
+
+}  // namespace
+
+extern "C" {
+
+int path_attn_fwd_prepare(const void* k, const void* v, const void* w, const float* beta,
+                          const float* log_f, int B, int H, int L, int d, int dtype, int chunk,
+                          void* workspace, size_t ws_bytes, void* stream) {
+    FwdPlan p;
+    int st = plan_fwd(B, H, L, d, dtype, chunk, log_f != nullptr, workspace, ws_bytes, p);
+    if (st != PATH_OK) return st;
+    if (!k || !v || !w || !beta) return PATH_ERR_INVALID;
+    const UtArgs u = ut_args(p, k, v, w, beta, log_f, L, d, chunk, workspace, false);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = p.bf ? launch_path_ut_bf16(u, s) : launch_path_ut_f32(u, s);
+    return e == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
+int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* w,
+                       const float* log_f, void* out, float* lse, int B, int H, int L, int d,
+                       float scale, int dtype, int chunk, const void* workspace, size_t ws_bytes,
+                       void* stream) {
+    FwdPlan p;
+    void* wsp = const_cast<void*>(workspace);
+    int st = plan_fwd(B, H, L, d, dtype, chunk, log_f != nullptr, wsp, ws_bytes, p);
+    if (st != PATH_OK) return st;
+    if (!q || !k || !v || !w || !out) return PATH_ERR_INVALID;
+    if (!(scale == scale)) return PATH_ERR_INVALID;
+    const UtArgs u = ut_args(p, k, v, w, nullptr, log_f, L, d, chunk, wsp, false);
+    FwdArgs f{};
+    f.q = q; f.k = k; f.v = v; f.w = w;
+    f.kt = u.kt; f.ut = u.ut; f.yt = u.yt;
+    f.loc = u.loc; f.csum = u.csum;
+    f.out = out; f.lse = lse;
+    f.BH = p.BH; f.L = L; f.N = p.N; f.C = chunk; f.D = d;
+    f.nqb = (p.N + 1) / 2;
+    f.scale2 = scale * kLog2e;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = p.bf ? launch_path_fwd_bf16(f, p.gate, s) : launch_path_fwd_f32(f, p.gate, s);
+    return e == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
+int path_attn_fwd(const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_f, void* out, float* lse,
+                  int B, int H, int L, int d, float scale, int dtype, int chunk,
+                  void* workspace, size_t ws_bytes, void* stream) {
+    if (!q || !out) return PATH_ERR_INVALID;
+    int st = path_attn_fwd_prepare(k, v, w, beta, log_f, B, H, L, d, dtype, chunk, workspace,
+                                   ws_bytes, stream);
+    if (st != PATH_OK) return st;
+    return path_attn_fwd_scan(q, k, v, w, log_f, out, lse, B, H, L, d, scale, dtype, chunk,
+                              workspace, ws_bytes, stream);
+}
+
+size_t path_kcache_workspace_bytes(int B, int H, int L, int d, int dtype) {
+    int chunk = kBf16Chunk;
+    if (dtype != PATH_BF16 || check_fwd_shape(B, H, L, d, dtype, chunk) != PATH_OK) return 0;
+    return fwd_plan(B, H, L, d, dtype, chunk, false, true).total;
+}
+
+int path_kcache_from_prefill(const void* k, const void* v, const void* w, const float* beta,
+                             void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                             int d, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    int chunk = kBf16Chunk;
+    if (!valid_dtype(dtype)) return PATH_ERR_INVALID;
+    if (dtype != PATH_BF16) return PATH_ERR_UNSUPPORTED;
+    int st = check_fwd_shape(B, H, L, d, dtype, chunk);
+    if (st != PATH_OK) return st;
+    if (T_max < L) return PATH_ERR_INVALID;
+    if (!k || !v || !w || !beta || !k_cache || !v_cache) return PATH_ERR_INVALID;
+    const Workspace ws = fwd_plan(B, H, L, d, dtype, chunk, false, true);
+    if (!workspace || ws_bytes < ws.total) return PATH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return PATH_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = B * H, N = (L + chunk - 1) / chunk;
+    UtArgs u{};
+    u.k = k; u.v = v; u.w = w; u.beta = beta; u.log_f = nullptr;
+    u.BH = BH; u.L = L; u.N = N; u.C = chunk; u.D = d;
+    u.kt = at(workspace, ws.kt);
+    u.ut = at(workspace, ws.ut);
+    u.yt = at(workspace, ws.yt); u.zt = at(workspace, ws.zt);
+    if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
+    KcacheArgs c{};
+    c.kt = u.kt; c.w = w; c.zt = u.zt; c.v = v;
+    c.k_cache = k_cache; c.v_cache = v_cache;
+    c.BH = BH; c.L = L; c.N = N; c.T_max = T_max;
+    return launch_path_kcache(c, d, s) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
+size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype) {
+    if (B < 1 || H < 1 || T_max < 1 || dtype != PATH_BF16 || (d != 64 && d != 128)) return 0;
+    const size_t nsplit_max = ((size_t)T_max + 255) / 256;
+    return align256((size_t)B * H * nsplit_max * (d + 2) * sizeof(float));
+}
+
+int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
+                     const void* v_t, const void* w_t, const float* beta_t, void* out_t,
+                     float* lse_t, int B, int H, int t, int T_max, int d, float scale,
+                     int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    if (B < 1 || H < 1 || T_max < 1 || t < 0 || t >= T_max || !valid_dtype(dtype))
+        return PATH_ERR_INVALID;
+    if (dtype != PATH_BF16 || (d != 64 && d != 128)) return PATH_ERR_UNSUPPORTED;
+    if (!k_cache || !v_cache || !q_t || !k_t || !v_t || !w_t || !beta_t || !out_t)
+        return PATH_ERR_INVALID;
+    if (!(scale == scale)) return PATH_ERR_INVALID;
+    const size_t need = path_decode_workspace_bytes(B, H, T_max, d, dtype);
+    if (!workspace || ws_bytes < need) return PATH_ERR_WORKSPACE;
+    DecodeArgs a{};
+    a.k_cache = k_cache; a.v_cache = v_cache;
+    a.q = q_t; a.k = k_t; a.v = v_t; a.w = w_t; a.beta = beta_t;
+    a.out = out_t; a.lse = lse_t;
+    a.part = static_cast<float*>(workspace);
+    a.BH = B * H; a.t = t; a.T_max = T_max;
+    a.keys_per_split = 256;
+    a.nsplit = (t + 1 + a.keys_per_split - 1) / a.keys_per_split;
+    a.scale2 = scale * kLog2e;
+    return launch_path_decode(a, d, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PATH_OK : PATH_ERR_HIP;
+}
+
+}  // extern "C"

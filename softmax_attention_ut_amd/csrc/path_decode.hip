@@ -1,0 +1,165 @@
+// path_decode: one PaTH decode step with the in-place key-cache update
+// (gfx950).
+//
+// At step t every cached key is multiplied by the new transition,
+//     k_j <- (I - beta_t w_t w_t^T) k_j          (j < t),
+// the new key and value are stored at slot t, and q_t attends over slots
+// 0..t with plain softmax (Dutch summary section 3, "Inferentie"; Chinese
+// notes, inference paragraph: decoding then reduces to standard softmax
+// decoding).  The update, the write-back and the score are one pass over
+// the cache: per key, w.k and q.k are reduced together, the updated key is
+// stored, and the score is q.k - beta (w.k)(q.w).
+//
+// Split-sequence layout: block (split, head) owns 256 consecutive slots and
+// writes a partial (m, l, o) in log2 units; path_decode_combine merges the
+// splits of a head.  Each group of G = D/8 lanes owns one key (16 bytes per
+// lane), so a wave streams 64/G keys per pass with 16-byte accesses.
+#include "path_internal.h"
+
+namespace path {
+
+template <int D>
+__global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs a) {
+    constexpr int G = D / 8;              // lanes per key
+    constexpr int KPW = 64 / G;           // keys per wave pass
+    constexpr int KPB = 4 * KPW;          // keys per block pass
+    __shared__ float sPart[4 * KPW][D + 2];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / G, gl = lane % G;
+    const int split = blockIdx.x, head = blockIdx.y;
+    const int t = a.t;
+    const int j0 = split * a.keys_per_split;
+    const int j1 = min(j0 + a.keys_per_split, t + 1);
+
+    const bf16* qh = static_cast<const bf16*>(a.q) + (size_t)head * D;
+    const bf16* wh = static_cast<const bf16*>(a.w) + (size_t)head * D;
+    const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)head * D;
+    const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)head * D;
+    bf16* kc = static_cast<bf16*>(a.k_cache) + (size_t)head * a.T_max * D;
+    bf16* vc = static_cast<bf16*>(a.v_cache) + (size_t)head * a.T_max * D;
+    const float beta = a.beta[head];
+
+    float qf[8], wf[8];
+    {
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qh + 8 * gl);
+        const bf16x8 w8 = *reinterpret_cast<const bf16x8*>(wh + 8 * gl);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qf[e] = static_cast<float>(q8[e]); wf[e] = static_cast<float>(w8[e]); }
+    }
+    float qw = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qw += qf[e] * wf[e];
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) qw += __shfl_xor(qw, off, G);
+
+    float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+    for (int jb = j0; jb < j1; jb += KPB) {
+        const int j = jb + wave * KPW + g;
+        const bool ok = j < j1;
+        float kf[8], vf[8];
+        if (ok) {
+            const bf16x8 k8 = (j < t) ? *reinterpret_cast<const bf16x8*>(kc + (size_t)j * D + 8 * gl)
+                                      : *reinterpret_cast<const bf16x8*>(kh + 8 * gl);
+            const bf16x8 v8 = (j < t) ? *reinterpret_cast<const bf16x8*>(vc + (size_t)j * D + 8 * gl)
+                                      : *reinterpret_cast<const bf16x8*>(vh + 8 * gl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { kf[e] = static_cast<float>(k8[e]); vf[e] = static_cast<float>(v8[e]); }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { kf[e] = 0.f; vf[e] = 0.f; }
+        }
+        float pw = 0.f, pq = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { pw += wf[e] * kf[e]; pq += qf[e] * kf[e]; }
+#pragma unroll
+        for (int off = G / 2; off > 0; off >>= 1) {
+            pw += __shfl_xor(pw, off, G);
+            pq += __shfl_xor(pq, off, G);
+        }
+        if (ok) {
+            float s;
+            if (j < t) {
+                const float ba = beta * pw;
+                bf16x8 k8n;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) k8n[e] = static_cast<bf16>(kf[e] - ba * wf[e]);
+                *reinterpret_cast<bf16x8*>(kc + (size_t)j * D + 8 * gl) = k8n;
+                s = pq - ba * qw;
+            } else {   // j == t: the new key enters unchanged
+                bf16x8 k8n, v8n;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { k8n[e] = static_cast<bf16>(kf[e]); v8n[e] = static_cast<bf16>(vf[e]); }
+                *reinterpret_cast<bf16x8*>(kc + (size_t)j * D + 8 * gl) = k8n;
+                *reinterpret_cast<bf16x8*>(vc + (size_t)j * D + 8 * gl) = v8n;
+                s = pq;
+            }
+            s *= a.scale2;
+            const float mn = fmaxf(m, s);
+            const float sc = exp2f(m - mn);
+            const float p = exp2f(s - mn);
+            l = l * sc + p;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = o[e] * sc + p * vf[e];
+            m = mn;
+        }
+    }
+    // merge the 4*KPW key groups of the block
+    const int grp = wave * KPW + g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sPart[grp][8 * gl + e] = o[e];
+    if (gl == 0) { sPart[grp][D] = m; sPart[grp][D + 1] = l; }
+    __syncthreads();
+    if (tid < D) {
+        float mm = -INFINITY;
+        for (int r = 0; r < 4 * KPW; ++r) mm = fmaxf(mm, sPart[r][D]);
+        float ll = 0.f, oo = 0.f;
+        for (int r = 0; r < 4 * KPW; ++r) {
+            const float mr = sPart[r][D];
+            if (mr == -INFINITY) continue;
+            const float sc = exp2f(mr - mm);
+            ll += sPart[r][D + 1] * sc;
+            oo += sPart[r][tid] * sc;
+        }
+        float* part = a.part + ((size_t)head * a.nsplit + split) * (D + 2);
+        part[tid] = oo;
+        if (tid == 0) { part[D] = mm; part[D + 1] = ll; }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void path_decode_combine_kernel(const DecodeArgs a) {
+    const int head = blockIdx.x, e = threadIdx.x;
+    const float* part = a.part + (size_t)head * a.nsplit * (D + 2);
+    float mm = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, part[s * (D + 2) + D]);
+    float ll = 0.f, oo = 0.f;
+    for (int s = 0; s < a.nsplit; ++s) {
+        const float ms = part[s * (D + 2) + D];
+        if (ms == -INFINITY) continue;
+        const float sc = exp2f(ms - mm);
+        ll += part[s * (D + 2) + D + 1] * sc;
+        oo += part[s * (D + 2) + e] * sc;
+    }
+    static_cast<bf16*>(a.out)[(size_t)head * D + e] = static_cast<bf16>(oo / ll);
+    if (e == 0 && a.lse) a.lse[head] = (mm + log2f(ll)) * kLn2;
+}
+
+hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s) {
+    const dim3 grid(a.nsplit, a.BH), block(256);
+    if (D == 64) {
+        hipLaunchKernelGGL(path_decode_split_kernel<64>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(64), 0, s, a);
+    } else if (D == 128) {
+        hipLaunchKernelGGL(path_decode_split_kernel<128>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(128), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace path

@@ -1,0 +1,145 @@
+// Internal declarations shared by the PaTH HIP kernels and the C-ABI layer.
+// gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace path {
+
+using bf16 = __bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Operand-slot permutation.
+//
+// In the 32x32x16 bf16 MFMA the fp32 accumulator of a 32x32 tile gives lane l
+// the rows 8*(v/4) + 4*(l/32) + (v%4), v = 0..15, of column l%32.  The
+// B operand of the same instruction wants lane l to hold 8 consecutive
+// k-slots 8*(l/32)..+7 of column l%32.  Handing accumulator registers
+// v = 8*s .. 8*s+7 straight to the next MFMA as the B operand of k-step s
+// therefore assigns k-slot 16*s + p to row 16*s + perm16(p), where perm16
+// swaps the middle two groups of four: 0-3, 8-11, 4-7, 12-15.  Every operand
+// that meets such a chained accumulator along k is stored with its k axis
+// permuted the same way, so no register shuffles are needed between the
+// chained products.  perm16 is an involution.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int perm16(int p) {
+    return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1);
+}
+__host__ __device__ constexpr int permk(int s) {  // applied inside each group of 16
+    return (s & ~15) | perm16(s & 15);
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout of the forward pass (byte offsets, 256-aligned sections).
+// N = number of chunks, Lp = N * C.
+//   bf16 mode (C = 64):
+//     kt  [BH][Lp][D]   bf16  keys carried to their chunk end, d permuted
+//     ut  [BH][N][D][C] bf16  -U^T (U = T^{-1} W), key axis permuted
+//     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)), m permuted
+//     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), key axis permuted (cache only)
+//   f32 mode:
+//     kt  [BH][Lp][D] f32, u [BH][Lp][D] f32, y [BH][N][C][C] f32 (natural)
+//   both (forget gate only):
+//     loc  [BH][Lp] f32  -sum_{s=j+1}^{chunk end} log2 f_s
+//     csum [BH][N]  f32  sum over the chunk of log2 f_s
+// ---------------------------------------------------------------------------
+struct Workspace {
+    size_t kt, ut, yt, zt, loc, csum, total;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
+                                bool bf16_mode, bool gate, bool with_z) {
+    Workspace w{};
+    const size_t N = (L + C - 1) / C, Lp = N * C;
+    const size_t es = bf16_mode ? 2 : 4;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    w.kt = take(BH * Lp * D * es);
+    w.ut = take(BH * Lp * D * es);
+    w.yt = take(BH * N * C * C * es);
+    w.zt = with_z ? take(BH * Lp * D * es) : 0;
+    w.loc = gate ? take(BH * Lp * 4) : 0;
+    w.csum = gate ? take(BH * N * 4) : 0;
+    w.total = off;
+    return w;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel argument blocks.
+// ---------------------------------------------------------------------------
+struct UtArgs {
+    const void* k;
+    const void* v;
+    const void* w;
+    const float* beta;
+    const float* log_f;    // may be null
+    int BH, L, N, C, D;
+    void* kt;              // outputs (see Workspace)
+    void* ut;
+    void* yt;
+    void* zt;              // may be null
+    float* loc;            // null without gate
+    float* csum;
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;         // values and w are read straight from the inputs
+    const void* w;
+    const void* kt;
+    const void* ut;
+    const void* yt;
+    const float* loc;
+    const float* csum;
+    void* out;
+    float* lse;
+    int BH, L, N, C, D, nqb;
+    float scale2;          // scale * log2(e)
+};
+
+struct KcacheArgs {
+    const void* kt;        // keys carried to their chunk end (bf16, d permuted)
+    const void* w;         // input w [BH][L][D]
+    const void* zt;
+    const void* v;         // input values [BH][L][D]
+    void* k_cache;         // [BH][T_max][D]
+    void* v_cache;
+    int BH, L, N, T_max;
+};
+
+struct DecodeArgs {
+    void* k_cache;
+    void* v_cache;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* w;
+    const float* beta;
+    void* out;
+    float* lse;
+    float* part;           // [BH][nsplit][D + 2] partial (o, m, l)
+    int BH, t, T_max, nsplit, keys_per_split;
+    float scale2;
+};
+
+// Host-side launchers (return hipError_t of the launch).
+hipError_t launch_path_ut_f32(const UtArgs& a, hipStream_t s);
+hipError_t launch_path_ut_bf16(const UtArgs& a, hipStream_t s);
+hipError_t launch_path_fwd_f32(const FwdArgs& a, bool gate, hipStream_t s);
+hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s);
+hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s);
+hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s);
+
+}  // namespace path

@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol include/path_attn.h declares, and rejects bad arguments before
+any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import softmax_attention_ut_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_symbols():
+    txt = open(os.path.join(ROOT, "include", "path_attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return set(re.findall(r"\b(path_[a-z_0-9]+)\s*\(", txt))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pa.load_library()
+    syms = _header_symbols()
+    assert syms == set(pa.EXPORTS)
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert b"gfx950" in lib.path_version()
+
+
+def test_status_strings():
+    lib = pa.load_library()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.path_status_string(code).decode() == pa.STATUS[code]
+
+
+def test_workspace_sizes():
+    f = pa.path_attn_fwd_workspace_bytes
+    assert f(2, 8, 1024, 64, pa.PATH_BF16, 0) > 0
+    assert f(2, 8, 1000, 64, pa.PATH_BF16, 0) == f(2, 8, 1024, 64, pa.PATH_BF16, 0)
+    assert f(1, 1, 64, 16, pa.PATH_F32, 16) > 0
+    assert f(1, 1, 0, 64, pa.PATH_BF16, 0) == 0          # empty sequence
+    assert f(1, 1, 64, 48, pa.PATH_BF16, 0) == 0         # unsupported d
+    assert f(1, 1, 64, 64, pa.PATH_BF16, 32) == 0        # bf16 chunk is 64
+    assert f(1, 1, 64, 128, pa.PATH_F32, 64) == 0        # f32 d=128 needs chunk <= 32
+    assert f(1, 1, 64, 64, 7, 0) == 0                    # bad dtype
+    assert pa.path_kcache_workspace_bytes(2, 32, 8192, 128, pa.PATH_BF16) > 0
+    assert pa.path_kcache_workspace_bytes(2, 32, 8192, 128, pa.PATH_F32) == 0
+    assert pa.path_decode_workspace_bytes(2, 32, 8448, 128, pa.PATH_BF16) > 0
+    assert pa.path_decode_workspace_bytes(2, 32, 8448, 96, pa.PATH_BF16) == 0
+
+
+def _fwd_raw(ptr=1, L=64, d=64, dt=pa.PATH_BF16, chunk=0, ws=None, ws_bytes=None,
+             log_f=None, B=1, H=1):
+    lib = pa.load_library()
+    p = ctypes.c_void_p(ptr) if ptr else None
+    need = lib.path_attn_fwd_workspace_bytes(B, H, L, d, dt, chunk)
+    if ws is None:
+        ws = ctypes.c_void_p(4096)              # 256-aligned fake address, never touched
+    if ws_bytes is None:
+        ws_bytes = need
+    return lib.path_attn_fwd(p, p, p, p, p, log_f, p, None, B, H, L, d, 0.125, dt, chunk,
+                             ws, ws_bytes, None)
+
+
+def test_fwd_argument_errors_before_launch():
+    assert _fwd_raw(ptr=0) == -1                 # null inputs
+    assert _fwd_raw(L=0) == -1                   # empty sequence
+    assert _fwd_raw(B=0) == -1
+    assert _fwd_raw(dt=3) == -1
+    assert _fwd_raw(d=80) == -2
+    assert _fwd_raw(chunk=32) == -2              # bf16 supports chunk 64 only
+    assert _fwd_raw(d=128, dt=pa.PATH_F32, chunk=64) == -2
+    assert _fwd_raw(ws=None, ws_bytes=0) == -4   # no room
+    assert _fwd_raw(ws_bytes=100) == -4
+    assert _fwd_raw(ws=ctypes.c_void_p(4096 + 8)) == -4    # misaligned workspace
+
+
+def test_decode_argument_errors_before_launch():
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = lib.path_decode_workspace_bytes(1, 1, 16, 64, pa.PATH_BF16)
+    args = lambda t, T, d, dt, wsb: (p, p, p, p, p, p, p, p, None, 1, 1, t, T, d, 0.1, dt, p, wsb, None)
+    assert lib.path_decode_step(*args(16, 16, 64, pa.PATH_BF16, ws)) == -1   # t >= T_max
+    assert lib.path_decode_step(*args(-1, 16, 64, pa.PATH_BF16, ws)) == -1
+    assert lib.path_decode_step(*args(3, 16, 96, pa.PATH_BF16, ws)) == -2
+    assert lib.path_decode_step(*args(3, 16, 64, pa.PATH_F32, ws)) == -2
+    assert lib.path_decode_step(*args(3, 16, 64, pa.PATH_BF16, 8)) == -4
+
+
+def test_kcache_argument_errors_before_launch():
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = lib.path_kcache_workspace_bytes(1, 1, 128, 64, pa.PATH_BF16)
+    assert lib.path_kcache_from_prefill(p, p, p, p, p, p, 1, 1, 128, 100, 64, pa.PATH_BF16,
+                                        p, ws, None) == -1          # T_max < L
+    assert lib.path_kcache_from_prefill(p, p, p, p, p, p, 1, 1, 128, 200, 64, pa.PATH_F32,
+                                        p, ws, None) == -2
+    assert lib.path_kcache_from_prefill(None, p, p, p, p, p, 1, 1, 128, 200, 64,
+                                        pa.PATH_BF16, p, ws, None) == -1
+    assert lib.path_kcache_from_prefill(p, p, p, p, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16,
+                                        p, ws - 1, None) == -4
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        pa._lib_backup = pa._lib
+        try:
+            pa._lib = None
+            pa.load_library(str(tmp_path / "nope.so"))
+        finally:
+            pa._lib = pa._lib_backup
