@@ -93,6 +93,7 @@ UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, co
     u.BH = p.BH; u.L = L; u.N = p.N; u.C = chunk; u.D = d;
     u.kt = at(workspace, p.ws.kt);
     u.ut = at(workspace, p.ws.ut);
+    u.vt = p.bf ? at(workspace, p.ws.vt) : nullptr;
     u.yt = at(workspace, p.ws.yt);
     u.zt = with_z ? at(workspace, p.ws.zt) : nullptr;
     u.loc = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.loc)) : nullptr;
@@ -130,7 +131,7 @@ int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* 
     const UtArgs u = ut_args(p, k, v, w, nullptr, log_f, L, d, chunk, wsp, false);
     FwdArgs f{};
     f.q = q; f.k = k; f.v = v; f.w = w;
-    f.kt = u.kt; f.ut = u.ut; f.yt = u.yt;
+    f.kt = u.kt; f.ut = u.ut; f.vt = u.vt; f.yt = u.yt;
     f.loc = u.loc; f.csum = u.csum;
     f.out = out; f.lse = lse;
     f.BH = p.BH; f.L = L; f.N = p.N; f.C = chunk; f.D = d;
@@ -179,6 +180,7 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w, const 
     u.BH = BH; u.L = L; u.N = N; u.C = chunk; u.D = d;
     u.kt = at(workspace, ws.kt);
     u.ut = at(workspace, ws.ut);
+    u.vt = at(workspace, ws.vt);
     u.yt = at(workspace, ws.yt); u.zt = at(workspace, ws.zt);
     if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
     KcacheArgs c{};

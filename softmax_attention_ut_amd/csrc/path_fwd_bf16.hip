@@ -16,18 +16,22 @@
 // Orientation.  All products are formed transposed (S^T = K~ Q^T,
 // X^T = W Q^T, O^T += V^T P^T, Q^T -= U^T X^T), so every accumulator that
 // feeds a later product (S^T -> P^T, X^T, Q^T) is already in B-operand
-// position: accumulator registers 8s..8s+7 are the B operand of k-step s,
-// under the k-slot permutation perm16 (see path_internal.h).  The A operands
-// (K~, W along d; V^T, U^T, Y^T along keys) sit in LDS with that permutation
-// applied, so they are plain 16-byte LDS reads: K~, U^T and Y^T are written
-// pre-permuted by path_ut; W is permuted (groups of four d) and V transposed
-// while they are staged from the inputs.
+// position: accumulator registers 8s..8s+7 are the B operand of k-step s
+// under the k-slot permutation perm16 (path_internal.h).  V^T, U^T and Y^T
+// are written by path_ut with their key axis in that slot order and the d
+// rows of V^T, U^T permuted too, so the carried query and the output come
+// out with d in natural order: K~ and W are used as they are, and every LDS
+// operand read is one 16-byte ds_read.
 //
-// Workgroup: 4 waves = 128 queries = query chunks 2qb and 2qb+1.  Key chunks
-// are staged once per workgroup in LDS and shared by the 4 waves.  Block
-// order: heaviest query blocks first; when BH is a multiple of 8 all blocks
-// of one head land on one XCD (blocks are dealt to the 8 XCDs round-robin),
-// so a head's K~/W/U/V chunks are reused out of that XCD's L2.
+// Pipeline.  A workgroup (4 waves = 128 queries = query chunks 2qb, 2qb+1)
+// stages key chunks in LDS in two alternating buffer sets.  While the waves
+// compute on one set, the next chunk is copied into the other with
+// global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through VGPRs).
+// LDS tiles are unpadded; the 16-byte units of row r are XOR-swizzled by
+// (r & 7), which keeps the 32-row MFMA operand reads free of bank conflicts.
+// Block order: heaviest query blocks first; when BH is a multiple of 8 all
+// blocks of one head land on one XCD (blocks are dealt to the 8 XCDs
+// round-robin), so a head's chunks are reused out of that XCD's L2.
 #include "path_internal.h"
 
 namespace path {
@@ -48,57 +52,46 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// copy a [rows][cols] bf16 tile (contiguous in global) to LDS with row pitch
-template <int ROWS, int COLS, int PITCH>
-__device__ __forceinline__ void stage_tile(bf16* dst, const bf16* src, int tid) {
-    constexpr int UPR = COLS / 8;              // 16-byte units per row
-    constexpr int UNITS = ROWS * UPR;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_void;
+
+// Swizzled tile: 16-byte unit u of row r sits at unit u ^ (r & 7).
+template <int COLS>
+__device__ __forceinline__ int swz(int r, int u) { return r * COLS + ((u ^ (r & 7)) << 3); }
+
+// Asynchronous copy of a [ROWS][COLS] bf16 tile, contiguous in global memory,
+// into a swizzled LDS tile.  Each wave instruction fills one contiguous 1 KB
+// block of LDS (lane i -> bytes 16i..16i+15); the lane picks the global unit
+// that belongs there.
+template <int ROWS, int COLS>
+__device__ __forceinline__ void copy_async(bf16* lds, const bf16* g, int wave, int lane) {
+    constexpr int UPR = COLS / 8;
+    constexpr int RPB = 64 / UPR;             // rows per 1 KB block
+    constexpr int NBLK = ROWS / RPB;
 #pragma unroll
-    for (int u = tid; u < UNITS; u += 256) {
-        const int r = u / UPR, c8 = u % UPR;
-        const uint4 val = *reinterpret_cast<const uint4*>(src + (size_t)u * 8);
-        *reinterpret_cast<uint4*>(dst + r * PITCH + c8 * 8) = val;
+    for (int b = wave; b < NBLK; b += 4) {
+        const int r = b * RPB + lane / UPR;
+        const int u = (lane % UPR) ^ (r & 7);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(g + (size_t)r * COLS + u * 8),
+                                         (lds_void*)(lds + b * 512), 16, 0, 0);
     }
 }
 
-// W rows [C][D] (input, rows >= nvalid are padding) -> LDS [C][PITCH] with
-// the d axis permuted: d-quad q of each group of 16 goes to slot quad perm(q)
-template <int C, int D, int PITCH>
-__device__ __forceinline__ void stage_w_perm(bf16* dst, const bf16* src, int nvalid, int tid) {
-    constexpr int UPR = D / 8;
+// Synchronous guarded copy (rows >= nvalid are zero) into a swizzled tile.
+template <int ROWS, int COLS>
+__device__ __forceinline__ void copy_guarded(bf16* lds, const bf16* g, int nvalid, int tid) {
+    constexpr int UPR = COLS / 8;
 #pragma unroll
-    for (int u = tid; u < C * UPR; u += 256) {
-        const int r = u / UPR, d0 = (u % UPR) * 8;
+    for (int i = tid; i < ROWS * UPR; i += 256) {
+        const int r = i / UPR, u = i % UPR;
         uint4 val = {0u, 0u, 0u, 0u};
-        if (r < nvalid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * D + d0);
-        const int s0 = permk(d0), s1 = permk(d0 + 4);
-        *reinterpret_cast<uint2*>(dst + r * PITCH + s0) = make_uint2(val.x, val.y);
-        *reinterpret_cast<uint2*>(dst + r * PITCH + s1) = make_uint2(val.z, val.w);
+        if (r < nvalid) val = *reinterpret_cast<const uint4*>(g + (size_t)r * COLS + u * 8);
+        *reinterpret_cast<uint4*>(lds + swz<COLS>(r, u)) = val;
     }
 }
 
-// V rows [C][D] (input) -> LDS V^T [D][PITCH] with the key axis permuted.
-// Each work item moves a quad of keys x 8 values of d.
-template <int C, int D, int PITCH>
-__device__ __forceinline__ void stage_v_trans(bf16* dst, const bf16* src, int nvalid, int tid) {
-    constexpr int ITEMS = (C / 4) * (D / 8);
-#pragma unroll
-    for (int it = tid; it < ITEMS; it += 256) {
-        const int kq = it / (D / 8), d0 = (it % (D / 8)) * 8;
-        bf16x8 rows[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int j = 4 * kq + r;
-            rows[r] = bf16x8{};
-            if (j < nvalid) rows[r] = *reinterpret_cast<const bf16x8*>(src + (size_t)j * D + d0);
-        }
-        const int slot = permk(4 * kq);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            bf16x4 col = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
-            *reinterpret_cast<bf16x4*>(dst + (d0 + e) * PITCH + slot) = col;
-        }
-    }
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
 }
 
 __device__ __forceinline__ void decode_block(int bid, int BH, int nqb, int& head, int& qb) {
@@ -112,21 +105,178 @@ __device__ __forceinline__ void decode_block(int bid, int BH, int nqb, int& head
     }
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of a value with the lane 32 positions away (the two lane halves
+// hold the two key halves of the same query column)
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The running maximum is raised (and O, l rescaled) only when some lane's
+// candidate exceeds it by more than this many log2 units, so probabilities
+// stay <= 2^kRescaleSlack before the final normalisation.
+constexpr float kRescaleSlack = 8.f;
+
+template <int D, bool GATE>
+struct WaveState {
+    static constexpr int DT = D / 32, KSD = D / 16;
+    f32x16 qacc[DT];   // carried query Q^T (fp32); register 8s+t = d 32dt+16s+8hh+t
+    bf16x8 qB[KSD];    // its bf16 B operand
+    f32x16 oacc[DT];   // O^T (unnormalised), same d mapping
+    float m_run, l_run, loc_i;
+    double dab;        // gate: sum of chunk sums between the query chunk and the key chunk
+    int offD[KSD];     // swizzled element offsets of unit 2ks+hh in a row (row & 7 = lane & 7)
+};
+
+template <int D>
+struct Stage {
+    bf16* k;           // K~  [C][D]
+    bf16* w;           // W   [C][D]
+    bf16* u;           // -U^T [D][C]
+    bf16* v;           // V^T  [D][C]
+    float* loc;        // -local log2 gate prefix [C]
+};
+
+// One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
+template <int D, bool GATE, bool DIAG>
+__device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>& sg,
+                                          const bf16* sY, int l32, int hh, int iloc,
+                                          bool carry, float c2) {
+    constexpr int C = 64;
+    constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
+
+    // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys)
+    f32x16 s[2], x[2];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) { s[kt2][v] = 0.f; x[kt2][v] = 0.f; }
+        const bf16* ak = sg.k + (32 * kt2 + l32) * D;
+        const bf16* aw = sg.w + (32 * kt2 + l32) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
+            x[kt2] = mfma32(lds8(aw + st.offD[ks]), st.qB[ks], x[kt2]);
+        }
+    }
+    if (DIAG) {
+        // S^T += Y^T strictUpper(X)^T ;  X^T <- lower part (m <= i)
+        bf16x8 xu[KSC];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int v = 8 * (ks & 1) + t;
+                const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const float xv = x[ks >> 1][v];
+                xu[ks][t] = static_cast<bf16>(m > iloc ? xv : 0.f);
+                x[ks >> 1][v] = (m <= iloc) ? xv : 0.f;
+            }
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+            const bf16* ay = sY + (32 * kt2 + l32) * C;
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) s[kt2] = mfma32(lds8(ay + st.offD[ks]), xu[ks], s[kt2]);
+        }
+    }
+    // carry the query through this chunk:  Q^T += (-U^T) X^T   (independent of
+    // the softmax below, so its MFMAs overlap with the vector work)
+    if (carry) {
+        bf16x8 xB[KSC];
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) xB[ks] = pack8(x[ks >> 1], ks & 1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16* au = sg.u + (32 * dt + l32) * C;
+#pragma unroll
+            for (int ks = 0; ks < KSC; ++ks) st.qacc[dt] = mfma32(lds8(au + st.offD[ks]), xB[ks], st.qacc[dt]);
+        }
+    }
+
+    // online softmax in log2 units.  Lane holds keys
+    // j = 32*kt2 + 8*(v/4) + 4*hh + v%4 of query iloc; lane^32 holds the rest.
+    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 lj = {0.f, 0.f, 0.f, 0.f};
+            if (GATE) lj = *reinterpret_cast<const f32x4*>(sg.loc + 32 * kt2 + 8 * r4 + 4 * hh);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int v = 4 * r4 + t;
+                float z = GATE ? fmaf(s[kt2][v], c2, -lj[t]) : s[kt2][v];
+                if (DIAG && (32 * kt2 + 8 * r4 + 4 * hh + t) > iloc) z = -INFINITY;
+                s[kt2][v] = z;
+                mx = fmaxf(mx, z);
+            }
+        }
+    mx = pair_max(mx);
+    const float cand = GATE ? mx + a_i : mx * c2;
+    if (__any(cand > st.m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m_run, cand);
+        const float alpha = fast_exp2(st.m_run - m_new);
+        st.m_run = m_new;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
+    }
+    const float msub = GATE ? st.m_run - a_i : st.m_run;
+    bf16x8 pB[KSC];
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float z = s[ks >> 1][8 * (ks & 1) + t];
+            const float p = GATE ? fast_exp2(z - msub) : fast_exp2(fmaf(z, c2, -msub));
+            psum += p;
+            pB[ks][t] = static_cast<bf16>(p);
+        }
+    st.l_run += psum;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const bf16* av = sg.v + (32 * dt + l32) * C;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offD[ks]), pB[ks], st.oacc[dt]);
+    }
+    if (carry) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    }
+}
+
 template <int D, bool GATE>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(const FwdArgs a) {
     constexpr int C = 64;
-    constexpr int PK = D + 8;     // pitch of [key][d] tiles
-    constexpr int PC = C + 8;     // pitch of [d][key] and [key][key] tiles
+    constexpr int TILE = C * D;   // elements of every staged tile
     constexpr int DT = D / 32;    // 32-row tiles along d
     constexpr int KSD = D / 16;   // k-steps along d
-    constexpr int KSC = C / 16;   // k-steps along keys (4)
 
-    __shared__ __attribute__((aligned(16))) bf16 sK[C * PK];
-    __shared__ __attribute__((aligned(16))) bf16 sW[C * PK];
-    __shared__ __attribute__((aligned(16))) bf16 sU[D * PC];
-    __shared__ __attribute__((aligned(16))) bf16 sV[D * PC];
-    __shared__ __attribute__((aligned(16))) bf16 sY[C * PC];
-    __shared__ __attribute__((aligned(16))) float sLoc[C];
+    // two stage sets (distinct objects so the DMA target and the tiles being
+    // read are known not to alias), the diagonal-chunk Y^T tile, gate terms
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sU0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sU1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sY[C * C];
+    __shared__ __attribute__((aligned(256))) float sLoc0[C];
+    __shared__ __attribute__((aligned(256))) float sLoc1[C];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -140,170 +290,105 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
     const int qi = qc * C + iloc;
     const bool qvalid = active && qi < L;
 
-    const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)head * L + (qvalid ? qi : 0)) * D;
     const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
     const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
-    const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
     const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
+    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
     const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
+    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
 
-    // carried query (fp32, accumulator layout) and its bf16 B operand
-    f32x16 qacc[DT];
+    const Stage<D> stage0{sK0, sW0, sU0, sV0, sLoc0};
+    const Stage<D> stage1{sK1, sW1, sU1, sV1, sLoc1};
+
+    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
+        copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
+        copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
+        copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
+        copy_async<D, C>(sg.v, vt + (size_t)kc * D * C, wave, lane);
+        if (GATE && wave == 0)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
+                                             (lds_void*)sg.loc, 4, 0, 0);
+    };
+
+    WaveState<D, GATE> st;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int ks = 0; ks < KSD; ++ks) st.offD[ks] = (((2 * ks + hh) ^ (l32 & 7)) << 3);
+    {
+        const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)head * L + (qvalid ? qi : 0)) * D;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 q4 = {};
-            if (qvalid) q4 = *reinterpret_cast<const bf16x4*>(qrow + 32 * dt + 8 * r4 + 4 * hh);
+        for (int ks = 0; ks < KSD; ++ks) {
+            bf16x8 q8 = {};
+            if (qvalid) q8 = lds8(qrow + 16 * ks + 8 * hh);
+            st.qB[ks] = q8;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) qacc[dt][4 * r4 + t] = static_cast<float>(q4[t]);
+            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
         }
-    bf16x8 qB[KSD];
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) qB[ks] = pack8(qacc[ks >> 1], ks & 1);
-
-    f32x16 oacc[DT];
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
-    float loc_i = 0.f;
-    double dab = 0.0;
-    if (GATE && qvalid) loc_i = a.loc[(size_t)head * Lp + qi];
+        for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+    st.loc_i = (GATE && qvalid) ? locg[qi] : 0.f;
+    st.dab = 0.0;
     const float c2 = a.scale2;
 
-    const int top = min(2 * qb + 1, N - 1);
-    for (int kc = top; kc >= 0; --kc) {
+    // prologue: the top chunk (possibly the ragged last one) and its Y^T
+    int kc = min(2 * qb + 1, N - 1);
+    copy_async<C, D>(sK0, kt + (size_t)kc * C * D, wave, lane);
+    copy_async<D, C>(sU0, ut + (size_t)kc * D * C, wave, lane);
+    copy_async<D, C>(sV0, vt + (size_t)kc * D * C, wave, lane);
+    copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
+    if (GATE && wave == 0)
+        __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sLoc0, 4, 0, 0);
+    copy_guarded<C, D>(sW0, win + (size_t)kc * C * D, min(C, L - kc * C), tid);
+    wait_vmem();
+    __syncthreads();
+
+    auto compute = [&](const Stage<D>& sg, int kcur) {
+        if (!active || kcur > qc) return;
+        const bool carry = kcur > 0;
+        if (kcur == qc)
+            scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
+        else
+            scan_step<D, GATE, false>(st, sg, sY, l32, hh, iloc, carry, c2);
+        if (GATE && carry) st.dab += static_cast<double>(a.csum[(size_t)head * N + kcur]);
+    };
+
+    for (;;) {
+        if (kc > 0) issue(stage1, kc - 1);
+        compute(stage0, kc);
+        wait_vmem();
         __syncthreads();
-        const int nvalid = min(C, L - kc * C);
-        stage_tile<C, D, PK>(sK, kt + (size_t)kc * C * D, tid);
-        stage_w_perm<C, D, PK>(sW, win + (size_t)kc * C * D, nvalid, tid);
-        stage_tile<D, C, PC>(sU, ut + (size_t)kc * D * C, tid);
-        stage_v_trans<C, D, PC>(sV, vin + (size_t)kc * C * D, nvalid, tid);
-        if (kc >= 2 * qb) stage_tile<C, C, PC>(sY, yt + (size_t)kc * C * C, tid);
-        if (GATE && tid < C) sLoc[tid] = a.loc[(size_t)head * Lp + kc * C + tid];
+        if (kc == 0) break;
+        --kc;
+        if (kc >= 2 * qb) {           // second diagonal chunk of this block: its Y^T
+            copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
+            wait_vmem();
+            __syncthreads();
+        }
+        if (kc > 0) issue(stage0, kc - 1);
+        compute(stage1, kc);
+        wait_vmem();
         __syncthreads();
-        if (!active || kc > qc) continue;
-        const bool diag = (kc == qc);
-
-        // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys)
-        f32x16 s[2], x[2];
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) { s[kt2][v] = 0.f; x[kt2][v] = 0.f; }
-            const bf16* ak = sK + (32 * kt2 + l32) * PK + 8 * hh;
-            const bf16* aw = sW + (32 * kt2 + l32) * PK + 8 * hh;
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) {
-                s[kt2] = mfma32(lds8(ak + 16 * ks), qB[ks], s[kt2]);
-                x[kt2] = mfma32(lds8(aw + 16 * ks), qB[ks], x[kt2]);
-            }
-        }
-        if (diag) {
-            // S^T += Y^T strictUpper(X)^T ; X^T <- lower part (m <= i)
-            bf16x8 xu[KSC];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const int v = 8 * (ks & 1) + t;
-                    const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
-                    const float xv = x[ks >> 1][v];
-                    xu[ks][t] = static_cast<bf16>(m > iloc ? xv : 0.f);
-                    x[ks >> 1][v] = (m <= iloc) ? xv : 0.f;
-                }
-#pragma unroll
-            for (int kt2 = 0; kt2 < 2; ++kt2) {
-                const bf16* ay = sY + (32 * kt2 + l32) * PC + 8 * hh;
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) s[kt2] = mfma32(lds8(ay + 16 * ks), xu[ks], s[kt2]);
-            }
-        }
-
-        // online softmax (log2 units).  Lane holds keys
-        // j = 32*kt2 + 8*(v/4) + 4*hh + v%4 of query iloc; lane^32 holds the rest.
-        const float a_i = GATE ? loc_i + static_cast<float>(dab) : 0.f;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                f32x4 lj = {0.f, 0.f, 0.f, 0.f};
-                if (GATE) lj = *reinterpret_cast<const f32x4*>(sLoc + 32 * kt2 + 8 * r4 + 4 * hh);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int v = 4 * r4 + t;
-                    const int j = 32 * kt2 + 8 * r4 + 4 * hh + t;
-                    float z = GATE ? fmaf(s[kt2][v], c2, -lj[t]) : s[kt2][v];
-                    if (diag && j > iloc) z = -INFINITY;
-                    s[kt2][v] = z;
-                    mx = fmaxf(mx, z);
-                }
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = GATE ? fmaxf(m_run, mx + a_i) : fmaxf(m_run, mx * c2);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
-        const float msub = GATE ? m_new - a_i : m_new;
-        bf16x8 pB[KSC];
-        float psum = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float z = s[ks >> 1][8 * (ks & 1) + t];
-                const float p = GATE ? exp2f(z - msub) : exp2f(fmaf(z, c2, -msub));
-                psum += p;
-                pB[ks][t] = static_cast<bf16>(p);
-            }
-        l_run += psum;
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16* av = sV + (32 * dt + l32) * PC + 8 * hh;
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) oacc[dt] = mfma32(lds8(av + 16 * ks), pB[ks], oacc[dt]);
-        }
-        // carry the query through chunk kc:  Q^T += (-U^T) X^T
-        if (kc > 0) {
-            bf16x8 xB[KSC];
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) xB[ks] = pack8(x[ks >> 1], ks & 1);
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const bf16* au = sU + (32 * dt + l32) * PC + 8 * hh;
-#pragma unroll
-                for (int ks = 0; ks < KSC; ++ks) qacc[dt] = mfma32(lds8(au + 16 * ks), xB[ks], qacc[dt]);
-            }
-#pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) qB[ks] = pack8(qacc[ks >> 1], ks & 1);
-            if (GATE) dab += static_cast<double>(a.csum[(size_t)head * N + kc]);
-        }
+        if (kc == 0) break;
+        --kc;
     }
 
     if (!active) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = pair_sum(st.l_run);
     if (!qvalid) return;
     const float inv = 1.f / l_tot;
     bf16* orow = static_cast<bf16*>(a.out) + ((size_t)head * L + qi) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int ks = 0; ks < KSD; ++ks) {
+        bf16x8 o8;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 o4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) o4[t] = static_cast<bf16>(oacc[dt][4 * r4 + t] * inv);
-            *reinterpret_cast<bf16x4*>(orow + 32 * dt + 8 * r4 + 4 * hh) = o4;
-        }
-    if (a.lse && hh == 0) a.lse[(size_t)head * L + qi] = (m_run + log2f(l_tot)) * kLn2;
+        for (int t = 0; t < 8; ++t) o8[t] = static_cast<bf16>(st.oacc[ks >> 1][8 * (ks & 1) + t] * inv);
+        *reinterpret_cast<bf16x8*>(orow + 16 * ks + 8 * hh) = o8;
+    }
+    if (a.lse && hh == 0) a.lse[(size_t)head * L + qi] = (st.m_run + log2f(l_tot)) * kLn2;
 }
 
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s) {

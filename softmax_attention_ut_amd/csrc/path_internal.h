@@ -42,10 +42,14 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 // Workspace layout of the forward pass (byte offsets, 256-aligned sections).
 // N = number of chunks, Lp = N * C.
 //   bf16 mode (C = 64):
-//     kt  [BH][Lp][D]   bf16  keys carried to their chunk end, d permuted
-//     ut  [BH][N][D][C] bf16  -U^T (U = T^{-1} W), key axis permuted
-//     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)), m permuted
-//     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), key axis permuted (cache only)
+//     kt  [BH][Lp][D]   bf16  keys carried to their chunk end (natural rows)
+//     ut  [BH][N][D][C] bf16  -U^T (U = T^{-1} W): [rho][sigma] = -U[permk(sigma)][permk(rho)]
+//     vt  [BH][N][D][C] bf16  V^T, laid out like ut
+//     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)): [j][sigma] = Y[permk(sigma)][j]
+//     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), laid out like ut (cache only)
+//   Permuting the d rows of the transposed tiles makes the fp32 accumulators
+//   they multiply into (carried query, output) come out with register 8s+t
+//   holding d = 16s + 8*(lane/32) + t, i.e. in natural B-operand order.
 //   f32 mode:
 //     kt  [BH][Lp][D] f32, u [BH][Lp][D] f32, y [BH][N][C][C] f32 (natural)
 //   both (forget gate only):
@@ -53,7 +57,7 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     csum [BH][N]  f32  sum over the chunk of log2 f_s
 // ---------------------------------------------------------------------------
 struct Workspace {
-    size_t kt, ut, yt, zt, loc, csum, total;
+    size_t kt, ut, vt, yt, zt, loc, csum, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -67,6 +71,7 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     w.kt = take(BH * Lp * D * es);
     w.ut = take(BH * Lp * D * es);
+    w.vt = bf16_mode ? take(BH * Lp * D * es) : 0;
     w.yt = take(BH * N * C * C * es);
     w.zt = with_z ? take(BH * Lp * D * es) : 0;
     w.loc = gate ? take(BH * Lp * 4) : 0;
@@ -87,6 +92,7 @@ struct UtArgs {
     int BH, L, N, C, D;
     void* kt;              // outputs (see Workspace)
     void* ut;
+    void* vt;              // bf16 mode only
     void* yt;
     void* zt;              // may be null
     float* loc;            // null without gate
@@ -96,10 +102,11 @@ struct UtArgs {
 struct FwdArgs {
     const void* q;
     const void* k;
-    const void* v;         // values and w are read straight from the inputs
+    const void* v;         // w (and v in f32 mode) are read from the inputs
     const void* w;
     const void* kt;
     const void* ut;
+    const void* vt;        // bf16 mode: V^T tiles (f32 mode reads v)
     const void* yt;
     const float* loc;
     const float* csum;

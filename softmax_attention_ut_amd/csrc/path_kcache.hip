@@ -9,7 +9,9 @@
 //     k^T <- k^T - (k^T W_c^T) Z_c,    Z_c = T_c^{-T} W_c,
 // which is (H_{end(c)} ... H_{start(c)}) k.  Layout and MFMA orientation are
 // those of the query transport in path_fwd (the key rides in fp32
-// accumulators, K^T -= Z^T X^T with X^T = W K^T).
+// accumulators, K^T -= Z^T X^T with X^T = W K^T; -Z^T comes from path_ut with
+// its token axis in k-slot order and its d rows permuted, so the key's
+// registers hold d in natural order).
 #include "path_internal.h"
 
 namespace path {
@@ -28,15 +30,14 @@ __device__ __forceinline__ bf16x8 pack8k(const f32x16& acc, int half) {
 }
 
 template <int C, int D, int PITCH>
-__device__ __forceinline__ void stage_w_perm_k(bf16* dst, const bf16* src, int nvalid, int tid) {
+__device__ __forceinline__ void stage_rows_k(bf16* dst, const bf16* src, int nvalid, int tid) {
     constexpr int UPR = D / 8;
 #pragma unroll
     for (int u = tid; u < C * UPR; u += 256) {
         const int r = u / UPR, d0 = (u % UPR) * 8;
         uint4 val = {0u, 0u, 0u, 0u};
         if (r < nvalid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * D + d0);
-        *reinterpret_cast<uint2*>(dst + r * PITCH + permk(d0)) = make_uint2(val.x, val.y);
-        *reinterpret_cast<uint2*>(dst + r * PITCH + permk(d0 + 4)) = make_uint2(val.z, val.w);
+        *reinterpret_cast<uint4*>(dst + r * PITCH + d0) = val;
     }
 }
 
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
     }
     for (int c = 2 * kb + 1; c < N; ++c) {
         __syncthreads();
-        stage_w_perm_k<C, D, PK>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
+        stage_rows_k<C, D, PK>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
         stage_tile_k<D, C, PC>(sZ, zt + (size_t)c * D * C, tid);
         __syncthreads();
         if (!active || c <= kc_own) continue;
@@ -128,16 +129,12 @@ __global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
         for (int ks = 0; ks < KSD; ++ks) kB[ks] = pack8k(kacc[ks >> 1], ks & 1);
     }
     if (!active || j >= L) return;
+    // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t (the d rows
+    // of -Z^T are stored permuted for this)
     bf16* kout = static_cast<bf16*>(a.k_cache) + ((size_t)head * a.T_max + j) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 o4;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) o4[t] = static_cast<bf16>(kacc[dt][4 * r4 + t]);
-            *reinterpret_cast<bf16x4*>(kout + 32 * dt + 8 * r4 + 4 * hh) = o4;
-        }
+    for (int ks = 0; ks < KSD; ++ks)
+        *reinterpret_cast<bf16x8*>(kout + 16 * ks + 8 * hh) = pack8k(kacc[ks >> 1], ks & 1);
     // values are copied unchanged, 4 bf16 per lane half
     const bf16* vin = static_cast<const bf16*>(a.v) + ((size_t)head * L + j) * D;
     bf16* vout = static_cast<bf16*>(a.v_cache) + ((size_t)head * a.T_max + j) * D;

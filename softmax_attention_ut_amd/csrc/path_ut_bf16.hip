@@ -7,11 +7,14 @@
 // C = 64 tokens and d in {64, 128}:
 //     U  = T^{-1} W,   Y = T^{-1} strictLower(W K^T),   K~ = K - Y^T W,
 //     Z  = T^{-T} W   (key-cache hand-off only)
-// written in the operand layouts the scan kernel reads (see path_internal.h):
-//     kt [Lp][D]   K~ rows, d axis permuted
-//     ut [N][D][C] -U^T, token axis permuted
-//     yt [N][C][C] Y^T,  token (m) axis permuted
-//     zt [N][D][C] -Z^T, token axis permuted
+// written in the operand layouts the scan kernel reads (see path_internal.h;
+// permk = the k-slot permutation, applied to token axes and to the d rows of
+// the transposed tiles):
+//     kt [Lp][D]   K~ rows, natural
+//     ut [N][D][C] -U^T:  ut[rho][sigma] = -U[permk(sigma)][permk(rho)]
+//     vt [N][D][C]  V^T:  vt[rho][sigma] =  V[permk(sigma)][permk(rho)]
+//     yt [N][C][C]  Y^T:  yt[j][sigma]   =  Y[permk(sigma)][j]
+//     zt [N][D][C] -Z^T, laid out like ut (key-cache hand-off only)
 // plus the chunk-local forget-gate sums.
 //
 // Arithmetic.  G = W W^T and R = W K^T are bf16 MFMAs with fp32
@@ -71,7 +74,8 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
 
     __shared__ __attribute__((aligned(16))) bf16 sW[C * PW];     // W rows, d natural
     __shared__ __attribute__((aligned(16))) bf16 sK[C * PW];     // K rows
-    __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T, token slots
+    __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T: [rho][sigma] = W[permk(sigma)][permk(rho)]
+    __shared__ __attribute__((aligned(16))) bf16 sV[C * PW];     // V rows
     __shared__ __attribute__((aligned(16))) float sG[C * GP];    // G rows (p < m used)
     __shared__ __attribute__((aligned(16))) bf16 sTh[C * PT];    // T^{-1} rows, n in slots (hi)
     __shared__ __attribute__((aligned(16))) bf16 sTl[C * PT];    //                          (lo)
@@ -92,19 +96,22 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     {
         const bf16* w = static_cast<const bf16*>(a.w) + ((size_t)head * L + p0) * D;
         const bf16* k = static_cast<const bf16*>(a.k) + ((size_t)head * L + p0) * D;
+        const bf16* v = static_cast<const bf16*>(a.v) + ((size_t)head * L + p0) * D;
         constexpr int UPR = D / 8;
         for (int u = tid; u < C * UPR; u += 256) {
             const int r = u / UPR, d0 = (u % UPR) * 8;
-            bf16x8 wv = {}, kv = {};
+            bf16x8 wv = {}, kv = {}, vv = {};
             if (r < nvalid) {
                 wv = ld8(w + (size_t)r * D + d0);
                 kv = ld8(k + (size_t)r * D + d0);
+                vv = ld8(v + (size_t)r * D + d0);
             }
             *reinterpret_cast<bf16x8*>(sW + r * PW + d0) = wv;
             *reinterpret_cast<bf16x8*>(sK + r * PW + d0) = kv;
+            *reinterpret_cast<bf16x8*>(sV + r * PW + d0) = vv;
             const int slot = permk(r);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sWt[(d0 + e) * PT + slot] = wv[e];
+            for (int e = 0; e < 8; ++e) sWt[permk(d0 + e) * PT + slot] = wv[e];
         }
         if (tid < C) sB[tid] = tid < nvalid ? a.beta[(size_t)head * L + p0 + tid] : 0.f;
     }
@@ -167,15 +174,27 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
                 *reinterpret_cast<bf16x8*>(sZl + n * PT + s8) = lo;
             }
         }
-    } else if (tid == 64 && a.loc) {
-        // forget gate: chunk-local suffix sums in log2 units (fp64)
-        double acc = 0.0;
-        for (int s = C - 1; s >= 0; --s) {
-            a.loc[rowbase + s] = static_cast<float>(-acc);
-            const double lf = s < nvalid ? (double)a.log_f[(size_t)head * L + p0 + s] : 0.0;
-            acc += lf * 1.4426950408889634;
+    } else {
+        // waves 1-3: V^T tile, 8 token slots per 16-byte store
+        bf16* vt = static_cast<bf16*>(a.vt) + chunkbase * D * C;
+        for (int u = tid - 64; u < D * (C / 8); u += 192) {
+            const int rho = u / (C / 8), s0 = (u % (C / 8)) * 8;
+            const int e = permk(rho);
+            bf16x8 col;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) col[t] = sV[permk(s0 + t) * PW + e];
+            *reinterpret_cast<bf16x8*>(vt + (size_t)rho * C + s0) = col;
         }
-        a.csum[chunkbase] = static_cast<float>(acc);
+        if (tid == 64 && a.loc) {
+            // forget gate: chunk-local suffix sums in log2 units (fp64)
+            double acc = 0.0;
+            for (int s = C - 1; s >= 0; --s) {
+                a.loc[rowbase + s] = static_cast<float>(-acc);
+                const double lf = s < nvalid ? (double)a.log_f[(size_t)head * L + p0 + s] : 0.0;
+                acc += lf * 1.4426950408889634;
+            }
+            a.csum[chunkbase] = static_cast<float>(acc);
+        }
     }
     __syncthreads();
 
@@ -223,19 +242,21 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
-        // K~^T[e][j] = K^T[e][j] - sum_m W^T[e][m] Y[m][j]
+        // K~^T[d][j] = K^T[d][j] - sum_m W^T[d][m] Y[m][j]
         bf16x8 yh[4], yl[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) split8(yacc[ks >> 1], ks & 1, -1.f, yh[ks], yl[ks]);
         bf16* krow = static_cast<bf16*>(a.kt) + (rowbase + j) * D;
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
+            // accumulator rows are sWt rows rho, i.e. d = permk(rho): register
+            // 8s+t holds d = 32 et + 16 s + 8 hh + t
             f32x16 kacc;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const bf16x4 k4 = *reinterpret_cast<const bf16x4*>(sK + j * PW + 32 * et + 8 * r4 + 4 * hh);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 k8 = ld8(sK + j * PW + 32 * et + 16 * s2 + 8 * hh);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) kacc[4 * r4 + t] = static_cast<float>(k4[t]);
+                for (int t = 0; t < 8; ++t) kacc[8 * s2 + t] = static_cast<float>(k8[t]);
             }
             const bf16* aw = sWt + (32 * et + l32) * PT + 8 * hh;
 #pragma unroll
@@ -252,7 +273,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
         const int mt = wave - 2;             // token tile m (for U) / n (for Z)
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
-            const int e = 32 * et + l32;
+            const int e = 32 * et + l32;         // sWt row rho: d = permk(rho)
             const bf16* bw = sWt + e * PT + 8 * hh;
             // U[m][e] = sum_n T^{-1}[m][n] W[n][e]
             f32x16 uacc;
