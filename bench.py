@@ -199,6 +199,26 @@ def bench_decode(args, cfg, torch, pa, inputs):
     return res, None
 
 
+def copy_calibration(mib, torch):
+    """A plain device-to-device copy of a known size: its FETCH_SIZE /
+    WRITE_SIZE counters calibrate the HBM-traffic figures of the kernels."""
+    n = mib * 2 ** 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "GB_per_s": 2 * n / (ms * 1e-3) / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +227,8 @@ def main():
     ap.add_argument("--workload", default="fox_L4k")
     ap.add_argument("--cpu-threads", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (traffic-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the PaTH hot path is data-parallel over "
@@ -220,6 +242,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, torch)
+        return
     cfg = inputs.CONFIGS[args.workload]
     if args.workload == "d128_L8k_decode":
         res, inp = bench_decode(args, cfg, torch, pa, inputs)

@@ -55,9 +55,18 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_void;
 
-// Swizzled tile: 16-byte unit u of row r sits at unit u ^ (r & 7).
+// Swizzled tile: 16-byte unit u of row r sits at unit u ^ g(r).  g keeps the
+// 32-row MFMA operand reads (16-byte per lane, consecutive lanes on
+// consecutive rows) on distinct banks whether the LDS serves 8 or 16 lanes
+// per cycle: rows of 128 bytes use g(r) = (r ^ ((r >> 3) & 3)) & 7, rows of
+// 256 bytes use g(r) = r & 15.  Both repeat every 32 rows, so a lane reading
+// rows 32t + lane%32 uses one offset for every t.
 template <int COLS>
-__device__ __forceinline__ int swz(int r, int u) { return r * COLS + ((u ^ (r & 7)) << 3); }
+__device__ __forceinline__ int swz_g(int r) {
+    return COLS == 64 ? ((r ^ ((r >> 3) & 3)) & 7) : (r & 15);
+}
+template <int COLS>
+__device__ __forceinline__ int swz(int r, int u) { return r * COLS + ((u ^ swz_g<COLS>(r)) << 3); }
 
 // Asynchronous copy of a [ROWS][COLS] bf16 tile, contiguous in global memory,
 // into a swizzled LDS tile.  Each wave instruction fills one contiguous 1 KB
@@ -71,7 +80,7 @@ __device__ __forceinline__ void copy_async(bf16* lds, const bf16* g, int wave, i
 #pragma unroll
     for (int b = wave; b < NBLK; b += 4) {
         const int r = b * RPB + lane / UPR;
-        const int u = (lane % UPR) ^ (r & 7);
+        const int u = (lane % UPR) ^ swz_g<COLS>(r);
         __builtin_amdgcn_global_load_lds((gbl_void*)(g + (size_t)r * COLS + u * 8),
                                          (lds_void*)(lds + b * 512), 16, 0, 0);
     }
@@ -92,6 +101,13 @@ __device__ __forceinline__ void copy_guarded(bf16* lds, const bf16* g, int nvali
 
 __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
+}
+// vmcnt(N): every vector-memory load but the N most recent ones has landed
+// (loads complete in issue order)
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
 
 __device__ __forceinline__ void decode_block(int bid, int BH, int nqb, int& head, int& qb) {
@@ -131,7 +147,9 @@ struct WaveState {
     f32x16 oacc[DT];   // O^T (unnormalised), same d mapping
     float m_run, l_run, loc_i;
     double dab;        // gate: sum of chunk sums between the query chunk and the key chunk
-    int offD[KSD];     // swizzled element offsets of unit 2ks+hh in a row (row & 7 = lane & 7)
+    int offD[KSD];     // swizzled offsets of unit 2ks+hh in a D-wide row  (row = 32x + lane%32)
+    int offC_[D == 64 ? 1 : 4];   // same in a 64-wide row (d = 64: equal to offD)
+    __device__ __forceinline__ int offC(int ks) const { return D == 64 ? offD[ks] : offC_[ks]; }
 };
 
 template <int D>
@@ -151,7 +169,10 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
     constexpr int C = 64;
     constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
 
-    // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys)
+    // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys).  With the forget
+    // gate, one more k-step adds -loc_j / c2 to every logit of key j (the key
+    // part of the bias, split into two bf16 terms), so that c2 * S holds
+    // scale*log2(e)*(k~_j . q) + log2 prod f over the key's chunk tail.
     f32x16 s[2], x[2];
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
@@ -160,9 +181,22 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
         const bf16* ak = sg.k + (32 * kt2 + l32) * D;
         const bf16* aw = sg.w + (32 * kt2 + l32) * D;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
-            x[kt2] = mfma32(lds8(aw + st.offD[ks]), st.qB[ks], x[kt2]);
+        for (int ks = 0; ks < KSD; ++ks) x[kt2] = mfma32(lds8(aw + st.offD[ks]), st.qB[ks], x[kt2]);
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
+        if (GATE) {
+            const float g = -sg.loc[32 * kt2 + l32] * (1.f / c2);
+            const bf16 gh = static_cast<bf16>(g);
+            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
+            bf16x8 ag = {};
+            bf16x8 ones = {};
+            if (hh == 0) {
+                ag[0] = gh;
+                ag[1] = gl;
+                ones[0] = static_cast<bf16>(1.f);
+                ones[1] = static_cast<bf16>(1.f);
+            }
+            s[kt2] = mfma32(ag, ones, s[kt2]);
         }
     }
     if (DIAG) {
@@ -182,7 +216,7 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
         for (int kt2 = 0; kt2 < 2; ++kt2) {
             const bf16* ay = sY + (32 * kt2 + l32) * C;
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) s[kt2] = mfma32(lds8(ay + st.offD[ks]), xu[ks], s[kt2]);
+            for (int ks = 0; ks < KSC; ++ks) s[kt2] = mfma32(lds8(ay + st.offC(ks)), xu[ks], s[kt2]);
         }
     }
     // carry the query through this chunk:  Q^T += (-U^T) X^T   (independent of
@@ -195,31 +229,23 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
         for (int dt = 0; dt < DT; ++dt) {
             const bf16* au = sg.u + (32 * dt + l32) * C;
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) st.qacc[dt] = mfma32(lds8(au + st.offD[ks]), xB[ks], st.qacc[dt]);
+            for (int ks = 0; ks < KSC; ++ks) st.qacc[dt] = mfma32(lds8(au + st.offC(ks)), xB[ks], st.qacc[dt]);
         }
     }
 
-    // online softmax in log2 units.  Lane holds keys
+    // online softmax in log2 units: z = c2 * S + a_i.  Lane holds keys
     // j = 32*kt2 + 8*(v/4) + 4*hh + v%4 of query iloc; lane^32 holds the rest.
     const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
     float mx = -INFINITY;
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            f32x4 lj = {0.f, 0.f, 0.f, 0.f};
-            if (GATE) lj = *reinterpret_cast<const f32x4*>(sg.loc + 32 * kt2 + 8 * r4 + 4 * hh);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int v = 4 * r4 + t;
-                float z = GATE ? fmaf(s[kt2][v], c2, -lj[t]) : s[kt2][v];
-                if (DIAG && (32 * kt2 + 8 * r4 + 4 * hh + t) > iloc) z = -INFINITY;
-                s[kt2][v] = z;
-                mx = fmaxf(mx, z);
-            }
+        for (int v = 0; v < 16; ++v) {
+            if (DIAG && (32 * kt2 + 8 * (v >> 2) + 4 * hh + (v & 3)) > iloc) s[kt2][v] = -INFINITY;
+            mx = fmaxf(mx, s[kt2][v]);
         }
     mx = pair_max(mx);
-    const float cand = GATE ? mx + a_i : mx * c2;
+    const float cand = fmaf(mx, c2, a_i);
     if (__any(cand > st.m_run + kRescaleSlack)) {
         const float m_new = fmaxf(st.m_run, cand);
         const float alpha = fast_exp2(st.m_run - m_new);
@@ -230,18 +256,21 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
 #pragma unroll
             for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
     }
-    const float msub = GATE ? st.m_run - a_i : st.m_run;
+    const float msub = st.m_run - a_i;
     bf16x8 pB[KSC];
     float psum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSC; ++ks)
+    for (int ks = 0; ks < KSC; ++ks) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float z = s[ks >> 1][8 * (ks & 1) + t];
-            const float p = GATE ? fast_exp2(z - msub) : fast_exp2(fmaf(z, c2, -msub));
-            psum += p;
-            pB[ks][t] = static_cast<bf16>(p);
+        for (int t = 0; t < 8; ++t)
+            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
+        // row sum of the rounded probabilities (the values the PV product uses)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
         }
+    }
     st.l_run += psum;
 
     // O^T += V^T P^T
@@ -249,7 +278,7 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
     for (int dt = 0; dt < DT; ++dt) {
         const bf16* av = sg.v + (32 * dt + l32) * C;
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offD[ks]), pB[ks], st.oacc[dt]);
+        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offC(ks)), pB[ks], st.oacc[dt]);
     }
     if (carry) {
 #pragma unroll
@@ -312,7 +341,11 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
 
     WaveState<D, GATE> st;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) st.offD[ks] = (((2 * ks + hh) ^ (l32 & 7)) << 3);
+    for (int ks = 0; ks < KSD; ++ks) st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
+    if (D != 64) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) st.offC_[ks & (D == 64 ? 0 : 3)] = ((2 * ks + hh) ^ swz_g<C>(l32)) << 3;
+    }
     {
         const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)head * L + (qvalid ? qi : 0)) * D;
 #pragma unroll
