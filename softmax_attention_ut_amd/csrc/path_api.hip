@@ -96,6 +96,7 @@ UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, co
     u.vt = p.bf ? at(workspace, p.ws.vt) : nullptr;
     u.yt = at(workspace, p.ws.yt);
     u.zt = with_z ? at(workspace, p.ws.zt) : nullptr;
+    u.mt = p.ws.mt ? at(workspace, p.ws.mt) : nullptr;
     u.loc = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.loc)) : nullptr;
     u.csum = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.csum)) : nullptr;
     return u;
@@ -131,7 +132,7 @@ int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* 
     const UtArgs u = ut_args(p, k, v, w, nullptr, log_f, L, d, chunk, wsp, false);
     FwdArgs f{};
     f.q = q; f.k = k; f.v = v; f.w = w;
-    f.kt = u.kt; f.ut = u.ut; f.vt = u.vt; f.yt = u.yt;
+    f.kt = u.kt; f.ut = u.ut; f.vt = u.vt; f.yt = u.yt; f.mt = u.mt;
     f.loc = u.loc; f.csum = u.csum;
     f.out = out; f.lse = lse;
     f.BH = p.BH; f.L = L; f.N = p.N; f.C = chunk; f.D = d;

@@ -155,11 +155,16 @@ struct WaveState {
 template <int D>
 struct Stage {
     bf16* k;           // K~  [C][D]
-    bf16* w;           // W   [C][D]
-    bf16* u;           // -U^T [D][C]
+    bf16* w;           // W   [C][D]      (d = 64: the diagonal chunk's, shared)
+    bf16* u;           // -U^T [D][C]     (d = 64: the diagonal chunk's, shared)
     bf16* v;           // V^T  [D][C]
+    bf16* mt;          // -M^T [D][D]     (d = 64 only)
     float* loc;        // -local log2 gate prefix [C]
 };
+
+// d = 64 scan carries the query with the d x d product of the chunk
+template <int D>
+constexpr bool kDense = D == 64;
 
 // One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
 template <int D, bool GATE, bool DIAG>
@@ -286,6 +291,91 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
     }
 }
 
+// One key chunk strictly left of the wave's query chunk, d = 64: the query
+// is carried through the whole chunk with its d x d product,
+// Q^T += (-M^T) Q^T (M = W^T U), which needs only the query operand the
+// logits use, so the carry, the logits and the softmax are independent.
+template <int D, bool GATE>
+__device__ __forceinline__ void scan_step_dense(WaveState<D, GATE>& st, const Stage<D>& sg,
+                                                int l32, int hh, bool carry, float c2) {
+    constexpr int C = 64;
+    constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
+    if (carry) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const bf16* am = sg.mt + (32 * dt + l32) * D;
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) st.qacc[dt] = mfma32(lds8(am + st.offD[ks]), st.qB[ks], st.qacc[dt]);
+        }
+    }
+    f32x16 s[2];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
+        const bf16* ak = sg.k + (32 * kt2 + l32) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
+        if (GATE) {
+            const float g = -sg.loc[32 * kt2 + l32] * (1.f / c2);
+            const bf16 gh = static_cast<bf16>(g);
+            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
+            bf16x8 ag = {};
+            bf16x8 ones = {};
+            if (hh == 0) {
+                ag[0] = gh;
+                ag[1] = gl;
+                ones[0] = static_cast<bf16>(1.f);
+                ones[1] = static_cast<bf16>(1.f);
+            }
+            s[kt2] = mfma32(ag, ones, s[kt2]);
+        }
+    }
+    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
+    mx = pair_max(mx);
+    const float cand = fmaf(mx, c2, a_i);
+    if (__any(cand > st.m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m_run, cand);
+        const float alpha = fast_exp2(st.m_run - m_new);
+        st.m_run = m_new;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
+    }
+    const float msub = st.m_run - a_i;
+    bf16x8 pB[KSC];
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSC; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
+        }
+    }
+    st.l_run += psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+        const bf16* av = sg.v + (32 * dt + l32) * C;
+#pragma unroll
+        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offC(ks)), pB[ks], st.oacc[dt]);
+    }
+    if (carry) {
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    }
+}
+
 template <int D, bool GATE>
 __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(const FwdArgs a) {
     constexpr int C = 64;
@@ -295,14 +385,22 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
 
     // two stage sets (distinct objects so the DMA target and the tiles being
     // read are known not to alias), the diagonal-chunk Y^T tile, gate terms
+    constexpr bool DENSE = kDense<D>;
+    constexpr int WU = DENSE ? 8 : TILE;    // per-stage W, U (rank-C carry only)
+    constexpr int MM = DENSE ? D * D : 8;   // per-stage -M^T (d x d carry only)
+    constexpr int WUD = DENSE ? TILE : 8;   // diagonal chunk's W, U (d x d carry)
     __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sU0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW0[WU];
+    __shared__ __attribute__((aligned(1024))) bf16 sU0[WU];
     __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sM0[MM];
     __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sU1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW1[WU];
+    __shared__ __attribute__((aligned(1024))) bf16 sU1[WU];
     __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sM1[MM];
+    __shared__ __attribute__((aligned(1024))) bf16 sWd[WUD];
+    __shared__ __attribute__((aligned(1024))) bf16 sUd[WUD];
     __shared__ __attribute__((aligned(1024))) bf16 sY[C * C];
     __shared__ __attribute__((aligned(256))) float sLoc0[C];
     __shared__ __attribute__((aligned(256))) float sLoc1[C];
@@ -324,15 +422,20 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
     const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
     const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
     const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
+    const bf16* mtg = DENSE ? static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D : nullptr;
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
 
-    const Stage<D> stage0{sK0, sW0, sU0, sV0, sLoc0};
-    const Stage<D> stage1{sK1, sW1, sU1, sV1, sLoc1};
+    const Stage<D> stage0{sK0, DENSE ? sWd : sW0, DENSE ? sUd : sU0, sV0, sM0, sLoc0};
+    const Stage<D> stage1{sK1, DENSE ? sWd : sW1, DENSE ? sUd : sU1, sV1, sM1, sLoc1};
 
     auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
         copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
-        copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
-        copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
+        if constexpr (DENSE) {
+            copy_async<D, D>(sg.mt, mtg + (size_t)kc * D * D, wave, lane);
+        } else {
+            copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
+            copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
+        }
         copy_async<D, C>(sg.v, vt + (size_t)kc * D * C, wave, lane);
         if (GATE && wave == 0)
             __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
@@ -368,14 +471,19 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
     const float c2 = a.scale2;
 
     // prologue: the top chunk (possibly the ragged last one) and its Y^T
+    // the diagonal chunk's W, -U^T (d x d carry: own buffers) and Y^T
+    auto load_diag = [&](int kcd) {
+        copy_guarded<C, D>(DENSE ? sWd : sW0, win + (size_t)kcd * C * D, min(C, L - kcd * C), tid);
+        copy_async<D, C>(DENSE ? sUd : sU0, ut + (size_t)kcd * D * C, wave, lane);
+        copy_async<C, C>(sY, yt + (size_t)kcd * C * C, wave, lane);
+    };
     int kc = min(2 * qb + 1, N - 1);
     copy_async<C, D>(sK0, kt + (size_t)kc * C * D, wave, lane);
-    copy_async<D, C>(sU0, ut + (size_t)kc * D * C, wave, lane);
+    if constexpr (DENSE) copy_async<D, D>(sM0, mtg + (size_t)kc * D * D, wave, lane);
     copy_async<D, C>(sV0, vt + (size_t)kc * D * C, wave, lane);
-    copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
     if (GATE && wave == 0)
         __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sLoc0, 4, 0, 0);
-    copy_guarded<C, D>(sW0, win + (size_t)kc * C * D, min(C, L - kc * C), tid);
+    load_diag(kc);
     wait_vmem();
     __syncthreads();
 
@@ -384,6 +492,8 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         const bool carry = kcur > 0;
         if (kcur == qc)
             scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
+        else if constexpr (DENSE)
+            scan_step_dense<D, GATE>(st, sg, l32, hh, carry, c2);
         else
             scan_step<D, GATE, false>(st, sg, sY, l32, hh, iloc, carry, c2);
         if (GATE && carry) st.dab += static_cast<double>(a.csum[(size_t)head * N + kcur]);
@@ -396,8 +506,9 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         __syncthreads();
         if (kc == 0) break;
         --kc;
-        if (kc >= 2 * qb) {           // second diagonal chunk of this block: its Y^T
-            copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
+        if (kc >= 2 * qb) {           // second diagonal chunk of this block
+            if constexpr (DENSE) load_diag(kc);
+            else copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
             wait_vmem();
             __syncthreads();
         }

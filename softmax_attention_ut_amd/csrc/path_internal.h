@@ -48,6 +48,8 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     vt  [BH][N][D][C] bf16  V^T, laid out like ut
 //     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)): [j][sigma] = Y[permk(sigma)][j]
 //     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), laid out like ut (cache only)
+//     mt  [BH][N][D][D] bf16  -M^T, M = W^T U: [rho][d'] = -M[d'][permk(rho)]
+//                             (d = 64 forward only: dense d x d transport)
 //   Permuting the d rows of the transposed tiles makes the fp32 accumulators
 //   they multiply into (carried query, output) come out with register 8s+t
 //   holding d = 16s + 8*(lane/32) + t, i.e. in natural B-operand order.
@@ -58,10 +60,16 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     csum [BH][N]  f32  sum over the chunk of log2 f_s
 // ---------------------------------------------------------------------------
 struct Workspace {
-    size_t kt, ut, vt, yt, zt, loc, csum, total;
+    size_t kt, ut, vt, yt, zt, mt, loc, csum, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The d = 64 bf16 forward carries queries through whole chunks with the
+// d x d product (2 d^2 flops per query and chunk, against 4 C d for the
+// rank-C form); at d = 128 (= 2C) both cost the same and the rank-C form,
+// which needs no extra tile, is kept.
+inline bool dense_transport(size_t D, bool bf16_mode) { return bf16_mode && D == 64; }
 
 inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
                                 bool bf16_mode, bool gate, bool with_z) {
@@ -75,6 +83,7 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     w.vt = bf16_mode ? take(BH * Lp * D * es) : 0;
     w.yt = take(BH * N * C * C * es);
     w.zt = with_z ? take(BH * Lp * D * es) : 0;
+    w.mt = (!with_z && dense_transport(D, bf16_mode)) ? take(BH * N * D * D * es) : 0;
     w.loc = gate ? take(BH * Lp * 4) : 0;
     w.csum = gate ? take(BH * N * 4) : 0;
     w.total = off;
@@ -96,6 +105,7 @@ struct UtArgs {
     void* vt;              // bf16 mode only
     void* yt;
     void* zt;              // may be null
+    void* mt;              // may be null (dense d x d transport tiles)
     float* loc;            // null without gate
     float* csum;
 };
@@ -109,6 +119,7 @@ struct FwdArgs {
     const void* ut;
     const void* vt;        // bf16 mode: V^T tiles (f32 mode reads v)
     const void* yt;
+    const void* mt;        // d = 64: -M^T tiles
     const float* loc;
     const float* csum;
     void* out;

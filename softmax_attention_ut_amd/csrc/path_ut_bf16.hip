@@ -15,6 +15,9 @@
 //     vt [N][D][C]  V^T:  vt[rho][sigma] =  V[permk(sigma)][permk(rho)]
 //     yt [N][C][C]  Y^T:  yt[j][sigma]   =  Y[permk(sigma)][j]
 //     zt [N][D][C] -Z^T, laid out like ut (key-cache hand-off only)
+//     mt [N][D][D] -M^T with M = W^T U (the chunk's product is I - M in
+//                  row-vector form): mt[rho][d'] = -M[d'][permk(rho)]
+//                  (optional; the d = 64 scan carries queries with it)
 // plus the chunk-local forget-gate sums.
 //
 // Arithmetic.  G = W W^T and R = W K^T are bf16 MFMAs with fp32
@@ -270,42 +273,74 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
                 *reinterpret_cast<bf16x8*>(krow + 32 * et + 16 * s2 + 8 * hh) = cvt8(kacc, s2, 1.f);
         }
     } else {
-        const int mt = wave - 2;             // token tile m (for U) / n (for Z)
-#pragma unroll
-        for (int et = 0; et < ET; ++et) {
+        // waves 2, 3: U (and Z) for every token, a subset of the d columns
+        for (int et = wave - 2; et < ET; et += 2) {
             const int e = 32 * et + l32;         // sWt row rho: d = permk(rho)
             const bf16* bw = sWt + e * PT + 8 * hh;
             // U[m][e] = sum_n T^{-1}[m][n] W[n][e]
-            f32x16 uacc;
-            zero(uacc);
-            const bf16* th = sTh + (32 * mt + l32) * PT + 8 * hh;
-            const bf16* tl = sTl + (32 * mt + l32) * PT + 8 * hh;
+            f32x16 uacc[2];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 w8 = ld8(bw + 16 * ks);
-                uacc = mfma(ld8(th + 16 * ks), w8, uacc);
-                uacc = mfma(ld8(tl + 16 * ks), w8, uacc);
-            }
-            bf16* urow = static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc, s2, -1.f);
-            if (WITH_Z) {
-                // Z[n][e] = sum_m T^{-1}[m][n] W[m][e]
-                f32x16 zacc;
-                zero(zacc);
-                const bf16* zh = sZh + (32 * mt + l32) * PT + 8 * hh;
-                const bf16* zl = sZl + (32 * mt + l32) * PT + 8 * hh;
+            for (int mt = 0; mt < 2; ++mt) {
+                zero(uacc[mt]);
+                const bf16* th = sTh + (32 * mt + l32) * PT + 8 * hh;
+                const bf16* tl = sTl + (32 * mt + l32) * PT + 8 * hh;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const bf16x8 w8 = ld8(bw + 16 * ks);
-                    zacc = mfma(ld8(zh + 16 * ks), w8, zacc);
-                    zacc = mfma(ld8(zl + 16 * ks), w8, zacc);
+                    uacc[mt] = mfma(ld8(th + 16 * ks), w8, uacc[mt]);
+                    uacc[mt] = mfma(ld8(tl + 16 * ks), w8, uacc[mt]);
                 }
-                bf16* zrow = static_cast<bf16*>(a.zt) + (chunkbase * D + e) * C;
+            }
+            bf16* urow = static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
-                    *reinterpret_cast<bf16x8*>(zrow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(zacc, s2, -1.f);
+                    *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc[mt], s2, -1.f);
+            if (a.mt) {
+                // M = W^T U (d x d): the whole chunk's transition product is
+                // I - M in row-vector form.  The U accumulator's column is
+                // d = permk(e), which is row e of -M^T in the stored layout
+                // (row rho holds d = permk(rho)); columns d' come out natural.
+                bf16x8 uh[4], ul[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) split8(uacc[ks >> 1], ks & 1, 1.f, uh[ks], ul[ks]);
+                bf16* mrow = static_cast<bf16*>(a.mt) + (chunkbase * D + e) * D;
+#pragma unroll
+                for (int ot = 0; ot < ET; ++ot) {
+                    f32x16 macc;
+                    zero(macc);
+                    const bf16* aw = sWt + (32 * ot + l32) * PT + 8 * hh;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 w8 = ld8(aw + 16 * ks);
+                        macc = mfma(w8, uh[ks], macc);
+                        macc = mfma(w8, ul[ks], macc);
+                    }
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        *reinterpret_cast<bf16x8*>(mrow + 32 * ot + 16 * s2 + 8 * hh) = cvt8(macc, s2, -1.f);
+                }
+            }
+            if (WITH_Z) {
+                // Z[n][e] = sum_m T^{-1}[m][n] W[m][e]
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x16 zacc;
+                    zero(zacc);
+                    const bf16* zh = sZh + (32 * nt + l32) * PT + 8 * hh;
+                    const bf16* zl = sZl + (32 * nt + l32) * PT + 8 * hh;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const bf16x8 w8 = ld8(bw + 16 * ks);
+                        zacc = mfma(ld8(zh + 16 * ks), w8, zacc);
+                        zacc = mfma(ld8(zl + 16 * ks), w8, zacc);
+                    }
+                    bf16* zrow = static_cast<bf16*>(a.zt) + (chunkbase * D + e) * C;
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        *reinterpret_cast<bf16x8*>(zrow + 32 * nt + 16 * s2 + 8 * hh) = cvt8(zacc, s2, -1.f);
+                }
             }
         }
     }
