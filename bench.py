@@ -31,18 +31,28 @@ HBM_PEAK_GBS = 8000.0                # MI355X HBM3E
 
 
 def flop_model(B, H, L, d, C=64):
-    """Algorithmic FLOPs of one forward (per the blockwise method with chunk C):
-    attention over the causal triangle, the low-rank query transport through
-    every full chunk strictly between query and key chunk, the diagonal-chunk
-    extras done by the scan kernel, and the per-chunk UT work of prepare."""
+    """Algorithmic FLOPs of one forward with chunk C, as the library computes it:
+      eff   2 L^2 d per head: QK^T and PV over the causal triangle, the count
+            behind "effective TFLOP/s" (independent of the carry form)
+      carry the query carried through every full chunk strictly between its
+            own chunk and the key chunk: 2 d^2 C per (query chunk, chunk) pair
+            with the d x d product (d = 64), 4 C^2 d with the rank-C form
+            Q - (Q W^T) U (d = 128)
+      diag  the diagonal-chunk extras done by the scan kernel: Q W^T, the
+            carry to the chunk start and the strictUpper(Q W^T) Y correction
+      prep  the per-chunk UT work of the prepare stage (G, R, T^{-1}, U, Y, K~,
+            and M = W^T U for the d x d carry)
+    "scan" is what the scan kernel must compute; "alg" the whole forward."""
     N = (L + C - 1) // C
+    dense = d == 64
+    pairs = (N - 1) * (N - 2) / 2.0
     f_eff = 2.0 * L * L * d
-    f_transport = 4.0 * C * C * d * (N - 1) * (N - 2) / 2.0
+    f_carry = pairs * (2.0 * d * d * C if dense else 4.0 * C * C * d)
     f_diag = N * (4.0 * C * C * d + 2.0 * C ** 3)
-    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3)
+    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3 + (2.0 * C * d * d if dense else 0.0))
     BH = B * H
-    return {"eff": BH * f_eff, "scan": BH * (f_eff + f_transport + f_diag),
-            "alg": BH * (f_eff + f_transport + f_prep)}
+    return {"eff": BH * f_eff, "scan": BH * (f_eff + f_carry + f_diag),
+            "alg": BH * (f_eff + f_carry + f_prep)}
 
 
 def _kernel_sha(name):
@@ -137,7 +147,8 @@ def bench_fwd(args, cfg, torch, pa, inputs):
         "tflops_algorithmic": f["alg"] / (ms * 1e-3) / 1e12,
         "mfma_peak_frac_algorithmic": f["alg"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "stage_ms": {"prepare(path_ut)": prep_ms, "scan(path_fwd)": scan_ms},
-        "roofline": {"kernel": "path_fwd_bf16_kernel<64,gate>", "bound": "mfma",
+        "roofline": {"kernel": f"path_fwd_bf16_kernel<{d},{'true' if cfg.gate else 'false'}>",
+                     "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic,

@@ -277,3 +277,18 @@ def test_decode_continuation_and_cache():
         o2, l2, _, _ = oracle.rows(q, k, v, w, beta, None, s, [h] * extra, rr)
         np.testing.assert_allclose(out[h, L:], o2, atol=1e-12)
         np.testing.assert_allclose(lse[h, L:], l2, atol=1e-12)
+
+
+def test_oracle_regression_fixture():
+    """The oracle's outputs on the tiny fp32 workload have not drifted
+    (fixture written by tests/golden/make_golden.py from the oracle)."""
+    import json
+    import os
+    from softmax_attention_ut_amd.inputs import CONFIGS, generate_config
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_f32_oracle.json")
+    rec = json.load(open(path))
+    cfg = CONFIGS["tiny_f32"]
+    inp = generate_config(cfg)
+    out, lse, _, _ = oracle.recurrent(inp.q, inp.k, inp.v, inp.w, inp.beta, None, cfg.scale)
+    np.testing.assert_allclose(out[0, 0], np.array(rec["out"]), atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.array(rec["lse"]), atol=1e-12)
