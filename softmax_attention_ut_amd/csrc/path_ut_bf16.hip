@@ -38,6 +38,10 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x4 mfma16f(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ void split8(const f32x16& acc, int half, float sign, bf16x8& hi,
                                        bf16x8& lo) {
 #pragma unroll
@@ -138,45 +142,33 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     }
     __syncthreads();
 
-    // ---- phase 2: T^{-1} by forward substitution (wave 0, lane n = column n) ----
+    // ---- phase 2: X = T^{-1}, blocked by 16 ----
+    // X is lower triangular.  X^T is written over the upper triangle of sG
+    // (row n, columns m >= n hold X[m][n]); G below the diagonal stays where
+    // the off-diagonal products need it.  The diagonal 16-blocks are stored
+    // whole, zeros above their diagonal.
+    //   (a) diagonal blocks X_bb = (I + strictLower(D_b G_bb))^{-1} D_b by
+    //       forward substitution, four blocks at once on wave 0;
+    //   (b) X_10, X_32 = -X_ii G_{i,i-1} X_{i-1,i-1};
+    //   (c) the lower-left 32-block, -X'_11 G'_10 X'_00 over 32-blocks;
+    // (I + A)^{-1} for the 2 x 2 block lower triangular I + A is
+    // [[X0, 0], [-X1 A10 X0, X1]], and D A10 = D G10 puts the right-hand
+    // diagonal into X1.
     if (wave == 0) {
-        const int n = lane;
-        const int sn = permk(n);
-        float t[C];
+        const int base = 16 * (lane >> 4), n = lane & 15;
+        float t[16];
 #pragma unroll
-        for (int m = 0; m < C; ++m) {
-            float s = 0.f;
+        for (int m = 0; m < 16; ++m) {
+            const float* grow = sG + (base + m) * GP + base;
+            float acc = 0.f;
 #pragma unroll
-            for (int p = 0; p < (m & ~3); p += 4) {
-                const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + m * GP + p);
-                s = fmaf(g4[0], t[p], s);
-                s = fmaf(g4[1], t[p + 1], s);
-                s = fmaf(g4[2], t[p + 2], s);
-                s = fmaf(g4[3], t[p + 3], s);
-            }
-#pragma unroll
-            for (int p = (m & ~3); p < m; ++p) s = fmaf(sG[m * GP + p], t[p], s);
-            const float tm = sB[m] * ((n == m ? 1.f : 0.f) - s);
-            t[m] = tm;
-            const bf16 h = static_cast<bf16>(tm);
-            sTh[m * PT + sn] = h;
-            sTl[m * PT + sn] = static_cast<bf16>(tm - static_cast<float>(h));
+            for (int p = 0; p < m; ++p) acc = fmaf(grow[p], t[p], acc);
+            t[m] = sB[base + m] * ((n == m ? 1.f : 0.f) - acc);
         }
-        if (WITH_Z) {
-            // row n of T^{-T} = column n of T^{-1}, token axis in slot order
+        float* xrow = sG + (base + n) * GP + base;
 #pragma unroll
-            for (int s8 = 0; s8 < C; s8 += 8) {
-                bf16x8 hi, lo;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = t[permk(s8 + e)];
-                    hi[e] = static_cast<bf16>(x);
-                    lo[e] = static_cast<bf16>(x - static_cast<float>(hi[e]));
-                }
-                *reinterpret_cast<bf16x8*>(sZh + n * PT + s8) = hi;
-                *reinterpret_cast<bf16x8*>(sZl + n * PT + s8) = lo;
-            }
-        }
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4*>(xrow + 4 * q) = f32x4{t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
     } else {
         // waves 1-3: V^T tile, 8 token slots per 16-byte store
         bf16* vt = static_cast<bf16*>(a.vt) + chunkbase * D * C;
@@ -188,15 +180,96 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
             for (int t = 0; t < 8; ++t) col[t] = sV[permk(s0 + t) * PW + e];
             *reinterpret_cast<bf16x8*>(vt + (size_t)rho * C + s0) = col;
         }
-        if (tid == 64 && a.loc) {
-            // forget gate: chunk-local suffix sums in log2 units (fp64)
-            double acc = 0.0;
-            for (int s = C - 1; s >= 0; --s) {
-                a.loc[rowbase + s] = static_cast<float>(-acc);
-                const double lf = s < nvalid ? (double)a.log_f[(size_t)head * L + p0 + s] : 0.0;
-                acc += lf * 1.4426950408889634;
+        if (wave == 1 && a.loc) {
+            // forget gate: chunk-local suffix sums in log2 units, fp64.  Lane s
+            // holds log2 f_s; an inclusive suffix scan over the 64 lanes gives
+            // x_s = sum_{s' >= s}, so loc_s = -(x_s - log2 f_s), csum = x_0.
+            const double lf = lane < nvalid ? (double)a.log_f[(size_t)head * L + p0 + lane] * 1.4426950408889634
+                                            : 0.0;
+            double x = lf;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double y = __shfl_down(x, off, 64);
+                if (lane + off < 64) x += y;
             }
-            a.csum[chunkbase] = static_cast<float>(acc);
+            a.loc[rowbase + lane] = static_cast<float>(-(x - lf));
+            if (lane == 0) a.csum[chunkbase] = static_cast<float>(x);
+        }
+    }
+    __syncthreads();
+
+    // (b), (c): 16 x 16 x 4 fp32 MFMAs.  Lane l = 16 g + r; A supplies
+    // A[r][k], B supplies B[k][r], and accumulator register v holds
+    // row 4 g + v, column r.  The k index of step s is taken as 4 g + s, so an
+    // accumulator feeds the next product's B operand register by register.
+    {
+        const int r = lane & 15, g = lane >> 4;
+        if (wave < 2) {
+            const int i = 2 * wave + 1, j = i - 1;
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(sG + (16 * i + r) * GP + 16 * j + 4 * g);
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(sG + (16 * j + r) * GP + 16 * j + 4 * g);
+            f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pacc = mfma16f(a4[q], b4[q], pacc);
+            f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) xacc = mfma16f(sG[(16 * i + 4 * g + q) * GP + 16 * i + r], pacc[q], xacc);
+            *reinterpret_cast<f32x4*>(sG + (16 * j + r) * GP + 16 * i + 4 * g) = -xacc;
+        }
+        __syncthreads();
+        // (c): wave (rb, cb) forms the output 16-tile rows 32 + 16 rb, columns
+        // 16 cb; it needs the 16-tiles (pb, cb), pb <= rb, of P = G'_10 X'_00.
+        {
+            const int rb = wave >> 1, cb = wave & 1;
+            f32x4 pt[2];
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb) {
+                pt[pb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (pb > rb) continue;
+                for (int kb = cb; kb < 2; ++kb) {  // X'_00[k][n] = 0 for k < n
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(sG + (32 + 16 * pb + r) * GP + 16 * kb + 4 * g);
+                    const f32x4 b4 = *reinterpret_cast<const f32x4*>(sG + (16 * cb + r) * GP + 16 * kb + 4 * g);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pt[pb] = mfma16f(a4[q], b4[q], pt[pb]);
+                }
+            }
+            f32x4 xacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pb = 0; pb < 2; ++pb) {
+                if (pb > rb) continue;  // X'_11[r][c] = 0 for c > r
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    xacc = mfma16f(sG[(32 + 16 * pb + 4 * g + q) * GP + 32 + 16 * rb + r], pt[pb][q], xacc);
+            }
+            *reinterpret_cast<f32x4*>(sG + (16 * cb + r) * GP + 32 + 16 * rb + 4 * g) = -xacc;
+        }
+    }
+    __syncthreads();
+
+    // T^{-1} rows with the n axis in k-slot order, split hi/lo; for the key
+    // cache also T^{-T} rows with the m axis in slot order.
+    for (int u = tid; u < C * (C / 8); u += 256) {
+        const int row = u >> 3, s0 = (u & 7) * 8;
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = permk(s0 + e);
+            const float x = col <= row ? sG[col * GP + row] : 0.f;
+            hi[e] = static_cast<bf16>(x);
+            lo[e] = static_cast<bf16>(x - static_cast<float>(hi[e]));
+        }
+        *reinterpret_cast<bf16x8*>(sTh + row * PT + s0) = hi;
+        *reinterpret_cast<bf16x8*>(sTl + row * PT + s0) = lo;
+        if (WITH_Z) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int col = permk(s0 + e);
+                const float x = col >= row ? sG[row * GP + col] : 0.f;
+                hi[e] = static_cast<bf16>(x);
+                lo[e] = static_cast<bf16>(x - static_cast<float>(hi[e]));
+            }
+            *reinterpret_cast<bf16x8*>(sZh + row * PT + s0) = hi;
+            *reinterpret_cast<bf16x8*>(sZl + row * PT + s0) = lo;
         }
     }
     __syncthreads();
