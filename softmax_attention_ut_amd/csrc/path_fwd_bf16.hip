@@ -162,10 +162,6 @@ struct Stage {
     float* loc;        // -local log2 gate prefix [C]
 };
 
-// d = 64 scan carries the query with the d x d product of the chunk
-template <int D>
-constexpr bool kDense = D == 64;
-
 // One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
 template <int D, bool GATE, bool DIAG>
 __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>& sg,
@@ -291,174 +287,174 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
     }
 }
 
-// One key chunk strictly left of the wave's query chunk, d = 64: the query
-// is carried through the whole chunk with its d x d product,
-// Q^T += (-M^T) Q^T (M = W^T U), which needs only the query operand the
-// logits use, so the carry, the logits and the softmax are independent.
-template <int D, bool GATE>
-__device__ __forceinline__ void scan_step_dense(WaveState<D, GATE>& st, const Stage<D>& sg,
-                                                int l32, int hh, bool carry, float c2) {
-    constexpr int C = 64;
-    constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
-    if (carry) {
+// Three-term bf16 split, x = h + m + l to about 24 bits.
+__device__ __forceinline__ void split3(float x, bf16& h, bf16& m, bf16& l) {
+    h = static_cast<bf16>(x);
+    const float r = x - static_cast<float>(h);
+    m = static_cast<bf16>(r);
+    l = static_cast<bf16>(r - static_cast<float>(m));
+}
+
+// x with every 32-bit lane word ANDed with msk (0 or ~0)
+__device__ __forceinline__ bf16x8 mask8(bf16x8 x, unsigned msk) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 w = __builtin_bit_cast(u32x4, x);
+    w &= msk;
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// Row sums above this trigger a rescale in the d = 64 key-chunk step (the
+// probabilities are then bounded by it before the final normalisation).
+constexpr float kRescaleTrigger = 4096.f;
+
+// One key chunk strictly left of the wave's query chunk, d = 64.
+//
+// The carried query is held pre-scaled by c2 = scale*log2(e) (the transport
+// is linear, so this is the same as scaling the logits).  One extra k-step of
+// the logit product adds the key's gate term -loc_j and the query's offset
+// a_i - m_run, each as three bf16 terms:
+//     A row j    = (g_h, g_m, g_l, 1, 1, 1, 0, 0 | 0 ... 0),   g = -loc_j
+//     B column i = (1, 1, 1, o_h, o_m, o_l, 0, 0 | 0 ... 0),   o = a_i - m_run
+// so the accumulator holds z_ij - m_run and the probabilities are exp2 of it.
+// The running maximum is raised only when a row sum exceeds kRescaleTrigger.
+// The query is carried through the whole chunk with the chunk's d x d
+// product, Q^T += (-M^T) Q^T (M = W^T U); the carry, the logits and the
+// softmax only share the query operand.
+template <bool GATE>
+__device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<64>& sg, int l32, int hh) {
+    constexpr int C = 64, D = 64, KS = 4;
+    const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
+    const unsigned lower = hh ? 0u : ~0u;   // bias terms live on the lower lane half
+    // every LDS operand of the logit and carry products, issued together
+    float gk[2] = {0.f, 0.f};
+    if (GATE) {
+        gk[0] = sg.loc[l32];
+        gk[1] = sg.loc[32 + l32];
+    }
+    bf16x8 opk[2 * KS], opm[2 * KS];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16* am = sg.mt + (32 * dt + l32) * D;
+    for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) st.qacc[dt] = mfma32(lds8(am + st.offD[ks]), st.qB[ks], st.qacc[dt]);
-        }
+        for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opm[KS * dt + ks] = lds8(sg.mt + (32 * dt + l32) * D + st.offD[ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 bq;
+    {
+        const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+        bf16 h, m, l;
+        split3(a_i - st.m_run, h, m, l);
+        bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
     }
     f32x16 s[2];
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
+        bf16 h = nil, m = nil, l = nil;
+        if (GATE) split3(-gk[kt2], h, m, l);
+        const bf16x8 ag = mask8(bf16x8{h, m, l, one, one, one, nil, nil}, lower);
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
-        const bf16* ak = sg.k + (32 * kt2 + l32) * D;
+        s[kt2] = mfma32(ag, bq, s[kt2]);
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
-        if (GATE) {
-            const float g = -sg.loc[32 * kt2 + l32] * (1.f / c2);
-            const bf16 gh = static_cast<bf16>(g);
-            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
-            bf16x8 ag = {};
-            bf16x8 ones = {};
-            if (hh == 0) {
-                ag[0] = gh;
-                ag[1] = gl;
-                ones[0] = static_cast<bf16>(1.f);
-                ones[1] = static_cast<bf16>(1.f);
-            }
-            s[kt2] = mfma32(ag, ones, s[kt2]);
-        }
+        for (int ks = 0; ks < KS; ++ks) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
     }
-    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
-    float mx = -INFINITY;
+    // carry:  Q^T += (-M^T) Q^T  (also formed, unused, for key chunk 0)
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
-    mx = pair_max(mx);
-    const float cand = fmaf(mx, c2, a_i);
-    if (__any(cand > st.m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(st.m_run, cand);
-        const float alpha = fast_exp2(st.m_run - m_new);
-        st.m_run = m_new;
-        st.l_run *= alpha;
+        for (int ks = 0; ks < KS; ++ks) st.qacc[dt] = mfma32(opm[KS * dt + ks], st.qB[ks], st.qacc[dt]);
+    // V^T operands, read while the softmax runs
+    bf16x8 opv[2 * KS];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
-    }
-    const float msub = st.m_run - a_i;
-    bf16x8 pB[KSC];
+        for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = lds8(sg.v + (32 * dt + l32) * D + st.offD[ks]);
+    __builtin_amdgcn_sched_barrier(0);
+    // probabilities and their row sum (of the rounded values the PV product uses)
+    bf16x8 pB[KS];
     float psum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
+        for (int t = 0; t < 8; ++t) pB[ks][t] = static_cast<bf16>(fast_exp2(s[ks >> 1][8 * (ks & 1) + t]));
 #pragma unroll
         for (int t = 0; t < 8; t += 2) {
             const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{one, one}, psum, false);
+        }
+    }
+    if (__any(!(psum <= kRescaleTrigger))) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
+        const float shift = fmaxf(pair_max(mx), 0.f);
+        const float alpha = fast_exp2(-shift);
+        st.m_run += shift;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
+        psum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                pB[ks][t] = static_cast<bf16>(fast_exp2(s[ks >> 1][8 * (ks & 1) + t] - shift));
+#pragma unroll
+            for (int t = 0; t < 8; t += 2) {
+                const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
+                psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{one, one}, psum, false);
+            }
         }
     }
     st.l_run += psum;
+    // O^T += V^T P^T
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const bf16* av = sg.v + (32 * dt + l32) * C;
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offC(ks)), pB[ks], st.oacc[dt]);
-    }
-    if (carry) {
+        for (int ks = 0; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-    }
+    for (int ks = 0; ks < KS; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    if (GATE) st.dab += static_cast<double>(sg.loc[C]);
 }
 
+// Per-lane setup shared by both kernels: block decode, query load, state.
 template <int D, bool GATE>
-__global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(const FwdArgs a) {
-    constexpr int C = 64;
-    constexpr int TILE = C * D;   // elements of every staged tile
-    constexpr int DT = D / 32;    // 32-row tiles along d
-    constexpr int KSD = D / 16;   // k-steps along d
+struct ScanSetup {
+    int head, qb, qc, iloc, qi;
+    bool active, qvalid;
+};
 
-    // two stage sets (distinct objects so the DMA target and the tiles being
-    // read are known not to alias), the diagonal-chunk Y^T tile, gate terms
-    constexpr bool DENSE = kDense<D>;
-    constexpr int WU = DENSE ? 8 : TILE;    // per-stage W, U (rank-C carry only)
-    constexpr int MM = DENSE ? D * D : 8;   // per-stage -M^T (d x d carry only)
-    constexpr int WUD = DENSE ? TILE : 8;   // diagonal chunk's W, U (d x d carry)
-    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW0[WU];
-    __shared__ __attribute__((aligned(1024))) bf16 sU0[WU];
-    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sM0[MM];
-    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW1[WU];
-    __shared__ __attribute__((aligned(1024))) bf16 sU1[WU];
-    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sM1[MM];
-    __shared__ __attribute__((aligned(1024))) bf16 sWd[WUD];
-    __shared__ __attribute__((aligned(1024))) bf16 sUd[WUD];
-    __shared__ __attribute__((aligned(1024))) bf16 sY[C * C];
-    __shared__ __attribute__((aligned(256))) float sLoc0[C];
-    __shared__ __attribute__((aligned(256))) float sLoc1[C];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int L = a.L, N = a.N, Lp = N * C;
-    int head, qb;
-    decode_block(blockIdx.x, a.BH, a.nqb, head, qb);
-
-    const int qc = 2 * qb + (wave >> 1);      // this wave's query chunk
-    const bool active = qc < N;
-    const int iloc = (wave & 1) * 32 + l32;   // query row within its chunk
-    const int qi = qc * C + iloc;
-    const bool qvalid = active && qi < L;
-
-    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
-    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
-    const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
-    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
-    const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
-    const bf16* mtg = DENSE ? static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D : nullptr;
-    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
-
-    const Stage<D> stage0{sK0, DENSE ? sWd : sW0, DENSE ? sUd : sU0, sV0, sM0, sLoc0};
-    const Stage<D> stage1{sK1, DENSE ? sWd : sW1, DENSE ? sUd : sU1, sV1, sM1, sLoc1};
-
-    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
-        copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
-        if constexpr (DENSE) {
-            copy_async<D, D>(sg.mt, mtg + (size_t)kc * D * D, wave, lane);
-        } else {
-            copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
-            copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
-        }
-        copy_async<D, C>(sg.v, vt + (size_t)kc * D * C, wave, lane);
-        if (GATE && wave == 0)
-            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
-                                             (lds_void*)sg.loc, 4, 0, 0);
-    };
-
-    WaveState<D, GATE> st;
+template <int D, bool GATE>
+__device__ __forceinline__ ScanSetup<D, GATE> scan_setup(const FwdArgs& a, WaveState<D, GATE>& st, int wave,
+                                                          int l32, int hh) {
+    constexpr int C = 64, DT = D / 32, KSD = D / 16;
+    ScanSetup<D, GATE> u;
+    decode_block(blockIdx.x, a.BH, a.nqb, u.head, u.qb);
+    u.qc = 2 * u.qb + (wave >> 1);           // this wave's query chunk
+    u.active = u.qc < a.N;
+    u.iloc = (wave & 1) * 32 + l32;          // query row within its chunk
+    u.qi = u.qc * C + u.iloc;
+    u.qvalid = u.active && u.qi < a.L;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks) st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
     if (D != 64) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) st.offC_[ks & (D == 64 ? 0 : 3)] = ((2 * ks + hh) ^ swz_g<C>(l32)) << 3;
     }
-    {
-        const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)head * L + (qvalid ? qi : 0)) * D;
+    const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)u.head * a.L + (u.qvalid ? u.qi : 0)) * D;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
-            bf16x8 q8 = {};
-            if (qvalid) q8 = lds8(qrow + 16 * ks + 8 * hh);
-            st.qB[ks] = q8;
+    for (int ks = 0; ks < KSD; ++ks) {
+        bf16x8 q8 = {};
+        if (u.qvalid) q8 = lds8(qrow + 16 * ks + 8 * hh);
+        st.qB[ks] = q8;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
-        }
+        for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -466,24 +462,91 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
     st.m_run = -INFINITY;
     st.l_run = 0.f;
-    st.loc_i = (GATE && qvalid) ? locg[qi] : 0.f;
+    st.loc_i = (GATE && u.qvalid) ? a.loc[(size_t)u.head * a.N * C + u.qi] : 0.f;
     st.dab = 0.0;
+    return u;
+}
+
+// Normalised output row and log-sum-exp (natural log).
+template <int D, bool GATE>
+__device__ __forceinline__ void scan_store(const FwdArgs& a, const WaveState<D, GATE>& st,
+                                           const ScanSetup<D, GATE>& u, int hh) {
+    constexpr int KSD = D / 16;
+    if (!u.active) return;
+    const float l_tot = pair_sum(st.l_run);
+    if (!u.qvalid) return;
+    const float inv = 1.f / l_tot;
+    bf16* orow = static_cast<bf16*>(a.out) + ((size_t)u.head * a.L + u.qi) * D;
+#pragma unroll
+    for (int ks = 0; ks < KSD; ++ks) {
+        bf16x8 o8;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) o8[t] = static_cast<bf16>(st.oacc[ks >> 1][8 * (ks & 1) + t] * inv);
+        *reinterpret_cast<bf16x8*>(orow + 16 * ks + 8 * hh) = o8;
+    }
+    if (a.lse && hh == 0) a.lse[(size_t)u.head * a.L + u.qi] = (st.m_run + log2f(l_tot)) * kLn2;
+}
+
+// d = 128: every key chunk carries the query with the rank-C form
+// Q <- Q - (Q W^T) U.
+template <int D, bool GATE>
+__global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) {
+    constexpr int C = 64;
+    constexpr int TILE = C * D;   // elements of every staged tile
+
+    // two stage sets (distinct objects so the DMA target and the tiles being
+    // read are known not to alias), the diagonal-chunk Y^T tile, gate terms
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sU0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sW1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sU1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sY[C * C];
+    __shared__ __attribute__((aligned(256))) float sLoc0[C];
+    __shared__ __attribute__((aligned(256))) float sLoc1[C];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = a.L, N = a.N, Lp = N * C;
+    WaveState<D, GATE> st;
+    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, wave, l32, hh);
+    const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
+    const bool active = u.active;
+
+    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
+    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
+    const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
+    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
+    const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
+    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
+
+    const Stage<D> stage0{sK0, sW0, sU0, sV0, nullptr, sLoc0};
+    const Stage<D> stage1{sK1, sW1, sU1, sV1, nullptr, sLoc1};
+
+    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
+        copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
+        copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
+        copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
+        copy_async<D, C>(sg.v, vt + (size_t)kc * D * C, wave, lane);
+        if (GATE && wave == 0)
+            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
+                                             (lds_void*)sg.loc, 4, 0, 0);
+    };
     const float c2 = a.scale2;
 
-    // prologue: the top chunk (possibly the ragged last one) and its Y^T
-    // the diagonal chunk's W, -U^T (d x d carry: own buffers) and Y^T
-    auto load_diag = [&](int kcd) {
-        copy_guarded<C, D>(DENSE ? sWd : sW0, win + (size_t)kcd * C * D, min(C, L - kcd * C), tid);
-        copy_async<D, C>(DENSE ? sUd : sU0, ut + (size_t)kcd * D * C, wave, lane);
-        copy_async<C, C>(sY, yt + (size_t)kcd * C * C, wave, lane);
-    };
+    // prologue: the top chunk (possibly the ragged last one: its W rows past
+    // L are zero-filled) and its Y^T
     int kc = min(2 * qb + 1, N - 1);
     copy_async<C, D>(sK0, kt + (size_t)kc * C * D, wave, lane);
-    if constexpr (DENSE) copy_async<D, D>(sM0, mtg + (size_t)kc * D * D, wave, lane);
+    copy_guarded<C, D>(sW0, win + (size_t)kc * C * D, min(C, L - kc * C), tid);
+    copy_async<D, C>(sU0, ut + (size_t)kc * D * C, wave, lane);
     copy_async<D, C>(sV0, vt + (size_t)kc * D * C, wave, lane);
     if (GATE && wave == 0)
         __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sLoc0, 4, 0, 0);
-    load_diag(kc);
+    copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
     wait_vmem();
     __syncthreads();
 
@@ -492,8 +555,6 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         const bool carry = kcur > 0;
         if (kcur == qc)
             scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
-        else if constexpr (DENSE)
-            scan_step_dense<D, GATE>(st, sg, l32, hh, carry, c2);
         else
             scan_step<D, GATE, false>(st, sg, sY, l32, hh, iloc, carry, c2);
         if (GATE && carry) st.dab += static_cast<double>(a.csum[(size_t)head * N + kcur]);
@@ -507,8 +568,7 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         if (kc == 0) break;
         --kc;
         if (kc >= 2 * qb) {           // second diagonal chunk of this block
-            if constexpr (DENSE) load_diag(kc);
-            else copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
+            copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
             wait_vmem();
             __syncthreads();
         }
@@ -519,27 +579,135 @@ __global__ __launch_bounds__(256, (D == 64 ? 2 : 1)) void path_fwd_bf16_kernel(c
         if (kc == 0) break;
         --kc;
     }
+    scan_store<D, GATE>(a, st, u, hh);
+}
 
-    if (!active) return;
-    const float l_tot = pair_sum(st.l_run);
-    if (!qvalid) return;
-    const float inv = 1.f / l_tot;
-    bf16* orow = static_cast<bf16*>(a.out) + ((size_t)head * L + qi) * D;
+// d = 64: the query's own chunk with the rank-C form (scan_step), every chunk
+// to its left with the d x d carry (dense_step).  The two diagonal key chunks
+// of a block are the first two iterations and are peeled off the loop, so
+// the loop body holds only dense steps.
+template <bool GATE>
+__global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs a) {
+    constexpr int C = 64, D = 64;
+    constexpr int TILE = C * D;
+    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sM0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sM1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
+    __shared__ __attribute__((aligned(1024))) bf16 sWd[TILE];   // diagonal chunk: W
+    __shared__ __attribute__((aligned(1024))) bf16 sUd[TILE];   //                 -U^T
+    __shared__ __attribute__((aligned(1024))) bf16 sY[TILE];    //                 Y^T
+    // gate terms of the staged chunk: -loc_j for its 64 keys, then its chunk sum
+    __shared__ __attribute__((aligned(256))) float sLoc0[C + 4];
+    __shared__ __attribute__((aligned(256))) float sLoc1[C + 4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = a.L, N = a.N, Lp = N * C;
+    WaveState<D, GATE> st;
+    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, wave, l32, hh);
+    const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
+    const bool active = u.active;
+
+    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
+    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
+    const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
+    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
+    const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
+    const bf16* mtg = static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D;
+    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
+    const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
+
+    const Stage<D> stage0{sK0, sWd, sUd, sV0, sM0, sLoc0};
+    const Stage<D> stage1{sK1, sWd, sUd, sV1, sM1, sLoc1};
+
+    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
+        copy_async<C, D>(sg.k, kt + (size_t)kc * TILE, wave, lane);
+        copy_async<D, D>(sg.mt, mtg + (size_t)kc * TILE, wave, lane);
+        copy_async<D, C>(sg.v, vt + (size_t)kc * TILE, wave, lane);
+        if (GATE && wave == 0) {
+            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
+                                             (lds_void*)sg.loc, 4, 0, 0);
+            if (lane == 0)
+                __builtin_amdgcn_global_load_lds((gbl_void*)(csg + kc), (lds_void*)(sg.loc + C), 4, 0, 0);
+        }
+    };
+    // the diagonal chunk's W (rows past L zero-filled), -U^T and Y^T
+    auto load_diag = [&](int kcd) {
+        copy_guarded<C, D>(sWd, win + (size_t)kcd * TILE, min(C, L - kcd * C), tid);
+        copy_async<D, C>(sUd, ut + (size_t)kcd * TILE, wave, lane);
+        copy_async<C, C>(sY, yt + (size_t)kcd * TILE, wave, lane);
+    };
+    const float c2 = a.scale2;
+    // the wave's own chunk; afterwards the carried query is held scaled by c2
+    auto diag = [&](const Stage<D>& sg, int kcur) {
+        const bool carry = kcur > 0;
+        scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
+        if (carry) {
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        bf16x8 o8;
+            for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) o8[t] = static_cast<bf16>(st.oacc[ks >> 1][8 * (ks & 1) + t] * inv);
-        *reinterpret_cast<bf16x8*>(orow + 16 * ks + 8 * hh) = o8;
+                for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+            if (GATE) st.dab += static_cast<double>(sg.loc[C]);
+        }
+    };
+    auto dense = [&](const Stage<D>& sg) { dense_step<GATE>(st, sg, l32, hh); };
+
+    // top chunk kc0: diagonal for the waves of query chunk kc0.  When the
+    // block has both query chunks, the next chunk (2qb) is diagonal for waves
+    // 0, 1; the stage sets are chosen so that the loop starts on set 0.
+    const int kc0 = min(2 * qb + 1, N - 1);
+    const bool both = kc0 == 2 * qb + 1;
+    auto top = [&](const Stage<D>& cur, const Stage<D>& nxt) {
+        issue(cur, kc0);
+        load_diag(kc0);
+        wait_vmem();
+        __syncthreads();
+        if (kc0 > 0) issue(nxt, kc0 - 1);
+        if (active && qc == kc0) diag(cur, kc0);
+        wait_vmem();
+        __syncthreads();
+    };
+    if (both) top(stage0, stage1);
+    else top(stage1, stage0);
+    int kc = kc0 - 1;
+    if (both && kc >= 0) {
+        load_diag(kc);
+        wait_vmem();
+        __syncthreads();
+        if (kc > 0) issue(stage0, kc - 1);
+        if (active) {
+            if (qc == kc) diag(stage1, kc);
+            else dense(stage1);
+        }
+        wait_vmem();
+        __syncthreads();
+        --kc;
     }
-    if (a.lse && hh == 0) a.lse[(size_t)head * L + qi] = (st.m_run + log2f(l_tot)) * kLn2;
+    while (kc >= 0) {
+        if (kc > 0) issue(stage1, kc - 1);
+        if (active) dense(stage0);
+        wait_vmem();
+        __syncthreads();
+        if (--kc < 0) break;
+        if (kc > 0) issue(stage0, kc - 1);
+        if (active) dense(stage1);
+        wait_vmem();
+        __syncthreads();
+        --kc;
+    }
+    scan_store<D, GATE>(a, st, u, hh);
 }
 
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s) {
     const dim3 grid(a.BH * a.nqb), block(256);
     if (a.D == 64) {
-        if (gate) hipLaunchKernelGGL((path_fwd_bf16_kernel<64, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_fwd_bf16_kernel<64, false>), grid, block, 0, s, a);
+        if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64_kernel<true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((path_fwd_bf16_d64_kernel<false>), grid, block, 0, s, a);
     } else if (a.D == 128) {
         if (gate) hipLaunchKernelGGL((path_fwd_bf16_kernel<128, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((path_fwd_bf16_kernel<128, false>), grid, block, 0, s, a);
