@@ -99,6 +99,23 @@ __device__ __forceinline__ void copy_guarded(bf16* lds, const bf16* g, int nvali
     }
 }
 
+// Asynchronous copy of one contiguous [64][64] bf16 tile (8 KB) into a
+// swizzled LDS tile, laid out as copy_async<64, 64> does: wave w fills the
+// 1 KB blocks w and w + 4.  The swizzle repeats every 32 rows, so one
+// per-lane source offset (tile64_lane_offset) serves both blocks and every
+// such tile; wave_u must be wave-uniform.
+__device__ __forceinline__ unsigned tile64_lane_offset(int wave, int lane) {
+    const int r = 8 * wave + (lane >> 3);
+    const int u = (lane & 7) ^ swz_g<64>(r);
+    return static_cast<unsigned>((r * 64 + u * 8) * 2);
+}
+__device__ __forceinline__ void copy_tile64(bf16* lds, const bf16* g, int wave_u, unsigned lane_off) {
+    const char* src = reinterpret_cast<const char*>(g);
+    char* dst = reinterpret_cast<char*>(lds) + wave_u * 1024;
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane_off), (lds_void*)dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void*)(src + 4096 + lane_off), (lds_void*)(dst + 4096), 16, 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
 }
@@ -307,6 +324,41 @@ __device__ __forceinline__ bf16x8 mask8(bf16x8 x, unsigned msk) {
 // probabilities are then bounded by it before the final normalisation).
 constexpr float kRescaleTrigger = 4096.f;
 
+// Probabilities of one 32-key tile (accumulator registers 0..15 = two PV
+// k-steps), summed as the rounded values the PV product uses.
+__device__ __forceinline__ float tile_probs(const f32x16& s, bf16x8& p0, bf16x8& p1, float shift) {
+    const bf16 one = static_cast<bf16>(1.f);
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p0[t] = static_cast<bf16>(fast_exp2(s[t] - shift));
+#pragma unroll
+    for (int t = 0; t < 8; ++t) p1[t] = static_cast<bf16>(fast_exp2(s[8 + t] - shift));
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[t], p0[t + 1]}, bf16x2{one, one}, sum, false);
+#pragma unroll
+    for (int t = 0; t < 8; t += 2) sum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[t], p1[t + 1]}, bf16x2{one, one}, sum, false);
+    return sum;
+}
+
+__device__ __forceinline__ float tile_max(const f32x16& s) {
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    return mx;
+}
+
+// Raise the running maximum by shift >= 0: rescale O and l.
+template <bool GATE>
+__device__ __forceinline__ void raise_max(WaveState<64, GATE>& st, float shift) {
+    const float alpha = fast_exp2(-shift);
+    st.m_run += shift;
+    st.l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
+}
+
 // One key chunk strictly left of the wave's query chunk, d = 64.
 //
 // The carried query is held pre-scaled by c2 = scale*log2(e) (the transport
@@ -320,27 +372,27 @@ constexpr float kRescaleTrigger = 4096.f;
 // The query is carried through the whole chunk with the chunk's d x d
 // product, Q^T += (-M^T) Q^T (M = W^T U); the carry, the logits and the
 // softmax only share the query operand.
+//
+// Issue order (a wave issues in program order, and an MFMA occupies the
+// matrix pipe for 8 passes while independent vector instructions issue):
+// logits of keys 0..31, logits of keys 32..63, the carry interleaved with
+// the probabilities of keys 0..31, the PV product of keys 0..31 interleaved
+// with the probabilities of keys 32..63, the PV product of keys 32..63.
 template <bool GATE>
 __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<64>& sg, int l32, int hh) {
     constexpr int C = 64, D = 64, KS = 4;
     const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
     const unsigned lower = hh ? 0u : ~0u;   // bias terms live on the lower lane half
-    // every LDS operand of the logit and carry products, issued together
     float gk[2] = {0.f, 0.f};
     if (GATE) {
         gk[0] = sg.loc[l32];
         gk[1] = sg.loc[32 + l32];
     }
-    bf16x8 opk[2 * KS], opm[2 * KS];
+    bf16x8 opk[2 * KS];
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opm[KS * dt + ks] = lds8(sg.mt + (32 * dt + l32) * D + st.offD[ks]);
-    __builtin_amdgcn_sched_barrier(0);
     bf16x8 bq;
     {
         const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
@@ -349,6 +401,7 @@ __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<
         bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
     }
     f32x16 s[2];
+    bf16x8 opm[2 * KS];
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
         bf16 h = nil, m = nil, l = nil;
@@ -359,65 +412,65 @@ __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<
         s[kt2] = mfma32(ag, bq, s[kt2]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
+        if (kt2 == 0) {
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    opm[KS * dt + ks] = lds8(sg.mt + (32 * dt + l32) * D + st.offD[ks]);
+        }
     }
-    // carry:  Q^T += (-M^T) Q^T  (also formed, unused, for key chunk 0)
+    __builtin_amdgcn_sched_barrier(0);
+    // carry Q^T += (-M^T) Q^T (also formed, unused, for key chunk 0), with the
+    // probabilities of keys 0..31
+    bf16x8 pB[KS];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) st.qacc[dt] = mfma32(opm[KS * dt + ks], st.qB[ks], st.qacc[dt]);
-    // V^T operands, read while the softmax runs
+    float psum = tile_probs(s[0], pB[0], pB[1], 0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__any(!(psum <= kRescaleTrigger))) {
+        const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
+        raise_max(st, shift);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[1][v] -= shift;
+        psum = tile_probs(s[0], pB[0], pB[1], shift);
+    }
+    st.l_run += psum;
     bf16x8 opv[2 * KS];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = lds8(sg.v + (32 * dt + l32) * D + st.offD[ks]);
-    __builtin_amdgcn_sched_barrier(0);
-    // probabilities and their row sum (of the rounded values the PV product uses)
-    bf16x8 pB[KS];
-    float psum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) pB[ks][t] = static_cast<bf16>(fast_exp2(s[ks >> 1][8 * (ks & 1) + t]));
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{one, one}, psum, false);
-        }
-    }
-    if (__any(!(psum <= kRescaleTrigger))) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt2][v]);
-        const float shift = fmaxf(pair_max(mx), 0.f);
-        const float alpha = fast_exp2(-shift);
-        st.m_run += shift;
-        st.l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
-        psum = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                pB[ks][t] = static_cast<bf16>(fast_exp2(s[ks >> 1][8 * (ks & 1) + t] - shift));
-#pragma unroll
-            for (int t = 0; t < 8; t += 2) {
-                const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
-                psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{one, one}, psum, false);
-            }
-        }
-    }
-    st.l_run += psum;
-    // O^T += V^T P^T
+    // O^T += V^T P^T for keys 0..31, with the probabilities of keys 32..63
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
+        for (int ks = 0; ks < 2; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
+    psum = tile_probs(s[1], pB[2], pB[3], 0.f);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__any(!(psum <= kRescaleTrigger))) {
+        const float shift = fmaxf(pair_max(tile_max(s[1])), 0.f);
+        raise_max(st, shift);
+        psum = tile_probs(s[1], pB[2], pB[3], shift);
+    }
+    st.l_run += psum;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 2; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
     if (GATE) st.dab += static_cast<double>(sg.loc[C]);
@@ -623,11 +676,13 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     const Stage<D> stage0{sK0, sWd, sUd, sV0, sM0, sLoc0};
     const Stage<D> stage1{sK1, sWd, sUd, sV1, sM1, sLoc1};
 
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const unsigned loff = tile64_lane_offset(wave_u, lane);
     auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
-        copy_async<C, D>(sg.k, kt + (size_t)kc * TILE, wave, lane);
-        copy_async<D, D>(sg.mt, mtg + (size_t)kc * TILE, wave, lane);
-        copy_async<D, C>(sg.v, vt + (size_t)kc * TILE, wave, lane);
-        if (GATE && wave == 0) {
+        copy_tile64(sg.k, kt + (size_t)kc * TILE, wave_u, loff);
+        copy_tile64(sg.mt, mtg + (size_t)kc * TILE, wave_u, loff);
+        copy_tile64(sg.v, vt + (size_t)kc * TILE, wave_u, loff);
+        if (GATE && wave_u == 0) {
             __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
                                              (lds_void*)sg.loc, 4, 0, 0);
             if (lane == 0)
@@ -637,8 +692,8 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     // the diagonal chunk's W (rows past L zero-filled), -U^T and Y^T
     auto load_diag = [&](int kcd) {
         copy_guarded<C, D>(sWd, win + (size_t)kcd * TILE, min(C, L - kcd * C), tid);
-        copy_async<D, C>(sUd, ut + (size_t)kcd * TILE, wave, lane);
-        copy_async<C, C>(sY, yt + (size_t)kcd * TILE, wave, lane);
+        copy_tile64(sUd, ut + (size_t)kcd * TILE, wave_u, loff);
+        copy_tile64(sY, yt + (size_t)kcd * TILE, wave_u, loff);
     };
     const float c2 = a.scale2;
     // the wave's own chunk; afterwards the carried query is held scaled by c2
