@@ -99,6 +99,7 @@ UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, co
     u.mt = p.ws.mt ? at(workspace, p.ws.mt) : nullptr;
     u.loc = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.loc)) : nullptr;
     u.csum = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.csum)) : nullptr;
+    u.gb = p.ws.gb ? at(workspace, p.ws.gb) : nullptr;
     return u;
 }
 
@@ -133,7 +134,7 @@ int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* 
     FwdArgs f{};
     f.q = q; f.k = k; f.v = v; f.w = w;
     f.kt = u.kt; f.ut = u.ut; f.vt = u.vt; f.yt = u.yt; f.mt = u.mt;
-    f.loc = u.loc; f.csum = u.csum;
+    f.loc = u.loc; f.csum = u.csum; f.gb = u.gb;
     f.out = out; f.lse = lse;
     f.BH = p.BH; f.L = L; f.N = p.N; f.C = chunk; f.D = d;
     f.nqb = (p.N + 1) / 2;

@@ -176,7 +176,8 @@ struct Stage {
     bf16* u;           // -U^T [D][C]     (d = 64: the diagonal chunk's, shared)
     bf16* v;           // V^T  [D][C]
     bf16* mt;          // -M^T [D][D]     (d = 64 only)
-    float* loc;        // -local log2 gate prefix [C]
+    float* loc;        // -local log2 gate prefix [C], then the chunk's gate sum
+    bf16* gb;          // d = 64 with gate: bias k-step A rows [C][16]
 };
 
 // One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
@@ -368,6 +369,7 @@ __device__ __forceinline__ void raise_max(WaveState<64, GATE>& st, float shift) 
 //     A row j    = (g_h, g_m, g_l, 1, 1, 1, 0, 0 | 0 ... 0),   g = -loc_j
 //     B column i = (1, 1, 1, o_h, o_m, o_l, 0, 0 | 0 ... 0),   o = a_i - m_run
 // so the accumulator holds z_ij - m_run and the probabilities are exp2 of it.
+// The A rows are written per key by path_ut (gate) or constant (no gate).
 // The running maximum is raised only when a row sum exceeds kRescaleTrigger.
 // The query is carried through the whole chunk with the chunk's d x d
 // product, Q^T += (-M^T) Q^T (M = W^T U); the carry, the logits and the
@@ -383,10 +385,12 @@ __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<
     constexpr int C = 64, D = 64, KS = 4;
     const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
     const unsigned lower = hh ? 0u : ~0u;   // bias terms live on the lower lane half
-    float gk[2] = {0.f, 0.f};
+    bf16x8 opg[2];
     if (GATE) {
-        gk[0] = sg.loc[l32];
-        gk[1] = sg.loc[32 + l32];
+        opg[0] = lds8(sg.gb + l32 * 16 + 8 * hh);
+        opg[1] = lds8(sg.gb + (32 + l32) * 16 + 8 * hh);
+    } else {
+        opg[0] = opg[1] = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
     }
     bf16x8 opk[2 * KS];
 #pragma unroll
@@ -404,12 +408,9 @@ __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<
     bf16x8 opm[2 * KS];
 #pragma unroll
     for (int kt2 = 0; kt2 < 2; ++kt2) {
-        bf16 h = nil, m = nil, l = nil;
-        if (GATE) split3(-gk[kt2], h, m, l);
-        const bf16x8 ag = mask8(bf16x8{h, m, l, one, one, one, nil, nil}, lower);
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
-        s[kt2] = mfma32(ag, bq, s[kt2]);
+        s[kt2] = mfma32(opg[kt2], bq, s[kt2]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
         if (kt2 == 0) {
@@ -576,8 +577,8 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
     const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
 
-    const Stage<D> stage0{sK0, sW0, sU0, sV0, nullptr, sLoc0};
-    const Stage<D> stage1{sK1, sW1, sU1, sV1, nullptr, sLoc1};
+    const Stage<D> stage0{sK0, sW0, sU0, sV0, nullptr, sLoc0, nullptr};
+    const Stage<D> stage1{sK1, sW1, sU1, sV1, nullptr, sLoc1, nullptr};
 
     auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
         copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
@@ -652,9 +653,12 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     __shared__ __attribute__((aligned(1024))) bf16 sWd[TILE];   // diagonal chunk: W
     __shared__ __attribute__((aligned(1024))) bf16 sUd[TILE];   //                 -U^T
     __shared__ __attribute__((aligned(1024))) bf16 sY[TILE];    //                 Y^T
-    // gate terms of the staged chunk: -loc_j for its 64 keys, then its chunk sum
+    // gate terms of the staged chunk: -loc_j for its 64 keys, then its chunk
+    // sum; the bias k-step rows of its keys
     __shared__ __attribute__((aligned(256))) float sLoc0[C + 4];
     __shared__ __attribute__((aligned(256))) float sLoc1[C + 4];
+    __shared__ __attribute__((aligned(1024))) bf16 sG0[GATE ? C * 16 : 8];
+    __shared__ __attribute__((aligned(1024))) bf16 sG1[GATE ? C * 16 : 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -673,8 +677,9 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
     const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
 
-    const Stage<D> stage0{sK0, sWd, sUd, sV0, sM0, sLoc0};
-    const Stage<D> stage1{sK1, sWd, sUd, sV1, sM1, sLoc1};
+    const Stage<D> stage0{sK0, sWd, sUd, sV0, sM0, sLoc0, sG0};
+    const Stage<D> stage1{sK1, sWd, sUd, sV1, sM1, sLoc1, sG1};
+    const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const unsigned loff = tile64_lane_offset(wave_u, lane);
@@ -682,6 +687,9 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
         copy_tile64(sg.k, kt + (size_t)kc * TILE, wave_u, loff);
         copy_tile64(sg.mt, mtg + (size_t)kc * TILE, wave_u, loff);
         copy_tile64(sg.v, vt + (size_t)kc * TILE, wave_u, loff);
+        if (GATE && wave_u < 2)      // bias rows: 2 KB, one 1 KB block per wave
+            __builtin_amdgcn_global_load_lds((gbl_void*)(gbg + (size_t)kc * C * 16 + wave_u * 512 + lane * 8),
+                                             (lds_void*)(sg.gb + wave_u * 512), 16, 0, 0);
         if (GATE && wave_u == 0) {
             __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
                                              (lds_void*)sg.loc, 4, 0, 0);

@@ -60,7 +60,7 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     csum [BH][N]  f32  sum over the chunk of log2 f_s
 // ---------------------------------------------------------------------------
 struct Workspace {
-    size_t kt, ut, vt, yt, zt, mt, loc, csum, total;
+    size_t kt, ut, vt, yt, zt, mt, loc, csum, gb, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -86,6 +86,9 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     w.mt = (!with_z && dense_transport(D, bf16_mode)) ? take(BH * N * D * D * es) : 0;
     w.loc = gate ? take(BH * Lp * 4) : 0;
     w.csum = gate ? take(BH * N * 4) : 0;
+    // d x d transport with the gate: each key's gate term as the A row of the
+    // logit product's bias k-step, 16 bf16 per key
+    w.gb = (gate && w.mt) ? take(BH * Lp * 16 * es) : 0;
     w.total = off;
     return w;
 }
@@ -108,6 +111,7 @@ struct UtArgs {
     void* mt;              // may be null (dense d x d transport tiles)
     float* loc;            // null without gate
     float* csum;
+    void* gb;              // may be null (gate bias rows, d x d transport)
 };
 
 struct FwdArgs {
@@ -122,6 +126,7 @@ struct FwdArgs {
     const void* mt;        // d = 64: -M^T tiles
     const float* loc;
     const float* csum;
+    const void* gb;        // d = 64 with gate: bias rows of the key chunks
     void* out;
     float* lse;
     int BH, L, N, C, D, nqb;

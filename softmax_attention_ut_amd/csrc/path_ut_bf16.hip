@@ -192,8 +192,22 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
                 const double y = __shfl_down(x, off, 64);
                 if (lane + off < 64) x += y;
             }
-            a.loc[rowbase + lane] = static_cast<float>(-(x - lf));
+            const float loc = static_cast<float>(-(x - lf));
+            a.loc[rowbase + lane] = loc;
             if (lane == 0) a.csum[chunkbase] = static_cast<float>(x);
+            if (a.gb) {
+                // the key's gate term -loc as the A row of the scan's bias
+                // k-step: three bf16 terms, three ones, zeros
+                const float g = -loc;
+                const bf16 h = static_cast<bf16>(g);
+                const float r = g - static_cast<float>(h);
+                const bf16 m = static_cast<bf16>(r);
+                const bf16 l = static_cast<bf16>(r - static_cast<float>(m));
+                const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
+                bf16x8* row = reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.gb) + (rowbase + lane) * 16);
+                row[0] = bf16x8{h, m, l, one, one, one, nil, nil};
+                row[1] = bf16x8{nil, nil, nil, nil, nil, nil, nil, nil};
+            }
         }
     }
     __syncthreads();
