@@ -74,11 +74,12 @@ def _traffic(profile_md, kernel_src):
     return float(m.group(1))
 
 
-def cpu_baseline(inp, cfg, threads):
-    """The fp64 oracle (recurrent form), unmodified, on the first `threads`
-    heads of the same inputs; extrapolated to the whole job."""
+def cpu_baseline(inp, cfg, threads, heads):
+    """The fp64 oracle (recurrent form), unmodified, on the first `heads`
+    heads of the same inputs with `threads` threads (about 2-3 s wall for 32
+    heads of the 4k workload on 8 threads); extrapolated to the whole job."""
     import oracle
-    n = threads
+    n = max(threads, min(heads, cfg.B * cfg.H))
     sl = lambda t: None if t is None else t.reshape(-1, *t.shape[2:])[:n]
     t0 = time.perf_counter()
     _, _, _, used = oracle.recurrent(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.w), sl(inp.beta),
@@ -238,6 +239,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fox_L4k")
     ap.add_argument("--cpu-threads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=32,
+                    help="heads the oracle baseline runs (the sample it extrapolates from)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (traffic-counter calibration)")
@@ -264,7 +267,7 @@ def main():
         res, inp = bench_fwd(args, cfg, torch, pa, inputs)
     if inp is not None and not args.no_cpu_baseline:
         threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, cfg.B * cfg.H))
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, threads)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, threads, args.cpu_heads)
     print(json.dumps(res), flush=True)
 
 
