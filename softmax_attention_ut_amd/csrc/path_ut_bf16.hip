@@ -30,6 +30,8 @@
 // bf16 rounding of the stored result.
 #include "path_internal.h"
 
+#include <type_traits>
+
 namespace path {
 
 namespace {
@@ -289,14 +291,19 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     __syncthreads();
 
     // ---- phase 3 ----
-    if (wave < 2) {
-        const int jt = wave;                 // key tile: columns j = 32 jt + l32
+    // R, Y and T^{-1} are triangular: tiles and k-steps that only meet their
+    // zero blocks are skipped (key tile jt is wave-uniform, a compile-time
+    // case each).
+    auto keys = [&](auto jtc) {
+        constexpr int jt = decltype(jtc)::value;   // key tile: columns j = 32 jt + l32
         const int j = 32 * jt + l32;
-        // R[n][j] = w_n . k_j for n > j (accumulator rows n, cols j)
+        // R[n][j] = w_n . k_j for n > j (accumulator rows n, cols j); the row
+        // tile above the key tile (n < 32 jt) is zero
         f32x16 racc[2];
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             zero(racc[nb]);
+            if (nb < jt) continue;
             const bf16* ap = sW + (32 * nb + l32) * PW + 8 * hh;
             const bf16* bp = sK + j * PW + 8 * hh;
 #pragma unroll
@@ -309,16 +316,18 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
         }
         bf16x8 rh[4], rl[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) split8(racc[ks >> 1], ks & 1, 1.f, rh[ks], rl[ks]);
-        // Y[m][j] = sum_n T^{-1}[m][n] R[n][j]
+        for (int ks = 2 * jt; ks < 4; ++ks) split8(racc[ks >> 1], ks & 1, 1.f, rh[ks], rl[ks]);
+        // Y[m][j] = sum_{j < n <= m} T^{-1}[m][n] R[n][j]: zero for m < 32 jt,
+        // and k-steps n in [32 jt, 32 mb + 31]
         f32x16 yacc[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             zero(yacc[mb]);
+            if (mb < jt) continue;
             const bf16* th = sTh + (32 * mb + l32) * PT + 8 * hh;
             const bf16* tl = sTl + (32 * mb + l32) * PT + 8 * hh;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 2 * jt; ks < 2 * mb + 2; ++ks) {
                 const bf16x8 ah = ld8(th + 16 * ks), al = ld8(tl + 16 * ks);
                 yacc[mb] = mfma(ah, rh[ks], yacc[mb]);
                 yacc[mb] = mfma(ah, rl[ks], yacc[mb]);
@@ -332,10 +341,10 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
-        // K~^T[d][j] = K^T[d][j] - sum_m W^T[d][m] Y[m][j]
+        // K~^T[d][j] = K^T[d][j] - sum_{m > j} W^T[d][m] Y[m][j]
         bf16x8 yh[4], yl[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) split8(yacc[ks >> 1], ks & 1, -1.f, yh[ks], yl[ks]);
+        for (int ks = 2 * jt; ks < 4; ++ks) split8(yacc[ks >> 1], ks & 1, -1.f, yh[ks], yl[ks]);
         bf16* krow = static_cast<bf16*>(a.kt) + (rowbase + j) * D;
 #pragma unroll
         for (int et = 0; et < ET; ++et) {
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
             }
             const bf16* aw = sWt + (32 * et + l32) * PT + 8 * hh;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int ks = 2 * jt; ks < 4; ++ks) {
                 const bf16x8 w8 = ld8(aw + 16 * ks);
                 kacc = mfma(w8, yh[ks], kacc);
                 kacc = mfma(w8, yl[ks], kacc);
@@ -359,6 +368,10 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
             for (int s2 = 0; s2 < 2; ++s2)
                 *reinterpret_cast<bf16x8*>(krow + 32 * et + 16 * s2 + 8 * hh) = cvt8(kacc, s2, 1.f);
         }
+    };
+    if (wave < 2) {
+        if (__builtin_amdgcn_readfirstlane(wave) == 0) keys(std::integral_constant<int, 0>{});
+        else keys(std::integral_constant<int, 1>{});
     } else {
         // waves 2, 3: U (and Z) for every token, a subset of the d columns
         for (int et = wave - 2; et < ET; et += 2) {
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
                 const bf16* th = sTh + (32 * mt + l32) * PT + 8 * hh;
                 const bf16* tl = sTl + (32 * mt + l32) * PT + 8 * hh;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
+                for (int ks = 0; ks < 2 * mt + 2; ++ks) {   // T^{-1}[m][n] = 0 for n > m
                     const bf16x8 w8 = ld8(bw + 16 * ks);
                     uacc[mt] = mfma(ld8(th + 16 * ks), w8, uacc[mt]);
                     uacc[mt] = mfma(ld8(tl + 16 * ks), w8, uacc[mt]);
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
                     const bf16* zh = sZh + (32 * nt + l32) * PT + 8 * hh;
                     const bf16* zl = sZl + (32 * nt + l32) * PT + 8 * hh;
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
+                    for (int ks = 2 * nt; ks < 4; ++ks) {   // T^{-T}[n][m] = 0 for m < n
                         const bf16x8 w8 = ld8(bw + 16 * ks);
                         zacc = mfma(ld8(zh + 16 * ks), w8, zacc);
                         zacc = mfma(ld8(zl + 16 * ks), w8, zacc);
