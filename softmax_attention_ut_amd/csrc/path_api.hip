@@ -93,7 +93,7 @@ UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, co
     u.BH = p.BH; u.L = L; u.N = p.N; u.C = chunk; u.D = d;
     u.kt = at(workspace, p.ws.kt);
     u.ut = at(workspace, p.ws.ut);
-    u.vt = p.bf ? at(workspace, p.ws.vt) : nullptr;
+    u.vt = p.ws.vt ? at(workspace, p.ws.vt) : nullptr;
     u.yt = at(workspace, p.ws.yt);
     u.zt = with_z ? at(workspace, p.ws.zt) : nullptr;
     u.mt = p.ws.mt ? at(workspace, p.ws.mt) : nullptr;
@@ -182,7 +182,7 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w, const 
     u.BH = BH; u.L = L; u.N = N; u.C = chunk; u.D = d;
     u.kt = at(workspace, ws.kt);
     u.ut = at(workspace, ws.ut);
-    u.vt = at(workspace, ws.vt);
+    u.vt = ws.vt ? at(workspace, ws.vt) : nullptr;
     u.yt = at(workspace, ws.yt); u.zt = at(workspace, ws.zt);
     if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
     KcacheArgs c{};

@@ -53,6 +53,43 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// PV A operands from a V tile kept as it is ([64 tokens][64 d], 16-byte units
+// swizzled like every 64-wide tile) with LDS transpose loads.  Within each
+// group of 16 lanes, ds_read_b64_tr_b16 gives lane i, element t, the element
+// i % 4 of the 8 bytes read by lane 4t + i/4.  So lane 4t + q reads 4
+// consecutive d of one token, and every lane receives one d column of four
+// tokens.  The permutations of the token (k-slot) and d (row) axes act on
+// blocks of four, which this access respects.  The operand of k-step ks, rows
+// dt, takes two loads (slots 0-3 and 4-7); a lane's 8 byte offsets depend
+// on (ks & 1, load, dt), the rows 32 (ks >> 1) further on add 4096 bytes.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+template <int COLS>
+__device__ __forceinline__ int swz_g(int r);
+__device__ __forceinline__ void vtr_offsets(unsigned off[8], int lane) {
+    const int hh = lane >> 5, hp = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int ins = 0; ins < 2; ++ins)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int tok = permk(16 * par + 8 * hh + 4 * ins + (j >> 2));
+                const int d = permk(32 * dt + 16 * hp + 4 * (j & 3));
+                off[(par * 2 + ins) * 2 + dt] =
+                    static_cast<unsigned>((tok * 64 + (((d >> 3) ^ swz_g<64>(tok)) << 3) + (d & 7)) * 2);
+            }
+}
+__device__ __forceinline__ bf16x8 pv_operand(const bf16* sv, const unsigned off[8], int dt, int ks) {
+    const char* base = reinterpret_cast<const char*>(sv) + 4096 * (ks >> 1);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 0) * 2 + dt]));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 1) * 2 + dt]));
+    const v4s both[2] = {lo, hi};
+    bf16x8 r;
+    __builtin_memcpy(&r, both, sizeof(r));
+    return r;
+}
 typedef __attribute__((address_space(1))) const void gbl_void;
 
 // Swizzled tile: 16-byte unit u of row r sits at unit u ^ g(r).  g keeps the
@@ -166,6 +203,7 @@ struct WaveState {
     double dab;        // gate: sum of chunk sums between the query chunk and the key chunk
     int offD[KSD];     // swizzled offsets of unit 2ks+hh in a D-wide row  (row = 32x + lane%32)
     int offC_[D == 64 ? 1 : 4];   // same in a 64-wide row (d = 64: equal to offD)
+    unsigned voff[D == 64 ? 8 : 1]; // d = 64: transpose-load offsets of the PV operands
     __device__ __forceinline__ int offC(int ks) const { return D == 64 ? offD[ks] : offC_[ks]; }
 };
 
@@ -292,12 +330,17 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
     }
     st.l_run += psum;
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T (d = 64: V as it is, through transpose loads)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
         const bf16* av = sg.v + (32 * dt + l32) * C;
 #pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) st.oacc[dt] = mfma32(lds8(av + st.offC(ks)), pB[ks], st.oacc[dt]);
+        for (int ks = 0; ks < KSC; ++ks) {
+            bf16x8 a8;
+            if constexpr (D == 64) a8 = pv_operand(sg.v, st.voff, dt, ks);
+            else a8 = lds8(av + st.offC(ks));
+            st.oacc[dt] = mfma32(a8, pB[ks], st.oacc[dt]);
+        }
     }
     if (carry) {
 #pragma unroll
@@ -448,7 +491,7 @@ __device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = lds8(sg.v + (32 * dt + l32) * D + st.offD[ks]);
+        for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = pv_operand(sg.v, st.voff, dt, ks);
     // O^T += V^T P^T for keys 0..31, with the probabilities of keys 32..63
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
@@ -667,11 +710,12 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, wave, l32, hh);
     const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
     const bool active = u.active;
+    vtr_offsets(st.voff, lane);
 
     const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
     const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
     const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
-    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
+    const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
     const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
     const bf16* mtg = static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D;
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
@@ -686,7 +730,8 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
         copy_tile64(sg.k, kt + (size_t)kc * TILE, wave_u, loff);
         copy_tile64(sg.mt, mtg + (size_t)kc * TILE, wave_u, loff);
-        copy_tile64(sg.v, vt + (size_t)kc * TILE, wave_u, loff);
+        if ((kc + 1) * C <= L) copy_tile64(sg.v, vin + (size_t)kc * TILE, wave_u, loff);
+        else copy_guarded<C, D>(sg.v, vin + (size_t)kc * TILE, L - kc * C, tid);   // ragged: zero rows
         if (GATE && wave_u < 2)      // bias rows: 2 KB, one 1 KB block per wave
             __builtin_amdgcn_global_load_lds((gbl_void*)(gbg + (size_t)kc * C * 16 + wave_u * 512 + lane * 8),
                                              (lds_void*)(sg.gb + wave_u * 512), 16, 0, 0);

@@ -45,7 +45,8 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //   bf16 mode (C = 64):
 //     kt  [BH][Lp][D]   bf16  keys carried to their chunk end (natural rows)
 //     ut  [BH][N][D][C] bf16  -U^T (U = T^{-1} W): [rho][sigma] = -U[permk(sigma)][permk(rho)]
-//     vt  [BH][N][D][C] bf16  V^T, laid out like ut
+//     vt  [BH][N][D][C] bf16  V^T, laid out like ut (d = 128; the d = 64 scan
+//                             reads V as it is with LDS transpose loads)
 //     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)): [j][sigma] = Y[permk(sigma)][j]
 //     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), laid out like ut (cache only)
 //     mt  [BH][N][D][D] bf16  -M^T, M = W^T U: [rho][d'] = -M[d'][permk(rho)]
@@ -80,7 +81,7 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     w.kt = take(BH * Lp * D * es);
     w.ut = take(BH * Lp * D * es);
-    w.vt = bf16_mode ? take(BH * Lp * D * es) : 0;
+    w.vt = (bf16_mode && D != 64) ? take(BH * Lp * D * es) : 0;
     w.yt = take(BH * N * C * C * es);
     w.zt = with_z ? take(BH * Lp * D * es) : 0;
     w.mt = (!with_z && dense_transport(D, bf16_mode)) ? take(BH * N * D * D * es) : 0;
@@ -105,7 +106,7 @@ struct UtArgs {
     int BH, L, N, C, D;
     void* kt;              // outputs (see Workspace)
     void* ut;
-    void* vt;              // bf16 mode only
+    void* vt;              // bf16 mode, d = 128 only (may be null)
     void* yt;
     void* zt;              // may be null
     void* mt;              // may be null (dense d x d transport tiles)
@@ -121,7 +122,7 @@ struct FwdArgs {
     const void* w;
     const void* kt;
     const void* ut;
-    const void* vt;        // bf16 mode: V^T tiles (f32 mode reads v)
+    const void* vt;        // bf16 d = 128: V^T tiles (otherwise v is read)
     const void* yt;
     const void* mt;        // d = 64: -M^T tiles
     const float* loc;

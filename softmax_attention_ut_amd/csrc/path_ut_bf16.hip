@@ -13,6 +13,7 @@
 //     kt [Lp][D]   K~ rows, natural
 //     ut [N][D][C] -U^T:  ut[rho][sigma] = -U[permk(sigma)][permk(rho)]
 //     vt [N][D][C]  V^T:  vt[rho][sigma] =  V[permk(sigma)][permk(rho)]
+//                  (d = 128 only: the d = 64 scan reads V as it is)
 //     yt [N][C][C]  Y^T:  yt[j][sigma]   =  Y[permk(sigma)][j]
 //     zt [N][D][C] -Z^T, laid out like ut (key-cache hand-off only)
 //     mt [N][D][D] -M^T with M = W^T U (the chunk's product is I - M in
@@ -84,7 +85,8 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sW[C * PW];     // W rows, d natural
     __shared__ __attribute__((aligned(16))) bf16 sK[C * PW];     // K rows
     __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T: [rho][sigma] = W[permk(sigma)][permk(rho)]
-    __shared__ __attribute__((aligned(16))) bf16 sV[C * PW];     // V rows
+    constexpr bool VT = D != 64;  // V^T tiles are written (d = 128)
+    __shared__ __attribute__((aligned(16))) bf16 sV[VT ? C * PW : 8];  // V rows
     __shared__ __attribute__((aligned(16))) float sG[C * GP];    // G rows (p < m used)
     __shared__ __attribute__((aligned(16))) bf16 sTh[C * PT];    // T^{-1} rows, n in slots (hi)
     __shared__ __attribute__((aligned(16))) bf16 sTl[C * PT];    //                          (lo)
@@ -113,11 +115,11 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
             if (r < nvalid) {
                 wv = ld8(w + (size_t)r * D + d0);
                 kv = ld8(k + (size_t)r * D + d0);
-                vv = ld8(v + (size_t)r * D + d0);
+                if (VT) vv = ld8(v + (size_t)r * D + d0);
             }
             *reinterpret_cast<bf16x8*>(sW + r * PW + d0) = wv;
             *reinterpret_cast<bf16x8*>(sK + r * PW + d0) = kv;
-            *reinterpret_cast<bf16x8*>(sV + r * PW + d0) = vv;
+            if (VT) *reinterpret_cast<bf16x8*>(sV + r * PW + d0) = vv;
             const int slot = permk(r);
 #pragma unroll
             for (int e = 0; e < 8; ++e) sWt[permk(d0 + e) * PT + slot] = wv[e];
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     } else {
         // waves 1-3: V^T tile, 8 token slots per 16-byte store
         bf16* vt = static_cast<bf16*>(a.vt) + chunkbase * D * C;
-        for (int u = tid - 64; u < D * (C / 8); u += 192) {
+        for (int u = tid - 64; VT && u < D * (C / 8); u += 192) {
             const int rho = u / (C / 8), s0 = (u % (C / 8)) * 8;
             const int e = permk(rho);
             bf16x8 col;
