@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
     constexpr int PT = C + 8;     // pitch of [x][token-slot] bf16 tiles
-    constexpr int GP = C + 4;     // pitch of the fp32 G rows
+    constexpr int GP = C + 8;     // pitch of the fp32 G rows (the T^{-1} hi/lo tiles reuse them)
     constexpr int ET = D / 32;
     constexpr int KSD = D / 16;
 
@@ -87,9 +87,13 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T: [rho][sigma] = W[permk(sigma)][permk(rho)]
     constexpr bool VT = D != 64;  // V^T tiles are written (d = 128)
     __shared__ __attribute__((aligned(16))) bf16 sV[VT ? C * PW : 8];  // V rows
-    __shared__ __attribute__((aligned(16))) float sG[C * GP];    // G rows (p < m used)
-    __shared__ __attribute__((aligned(16))) bf16 sTh[C * PT];    // T^{-1} rows, n in slots (hi)
-    __shared__ __attribute__((aligned(16))) bf16 sTl[C * PT];    //                          (lo)
+    // G rows (p < m used), then X^T over its upper triangle (fp32); once X is
+    // complete the same space holds T^{-1} rows with n in slots, hi and lo
+    // (2 x C x PT bf16 = C x GP fp32)
+    static_assert(2 * PT * 2 == GP * 4, "T^{-1} hi/lo tiles fill the G tile");
+    __shared__ __attribute__((aligned(16))) float sG[C * GP];
+    bf16* const sTh = reinterpret_cast<bf16*>(sG);
+    bf16* const sTl = reinterpret_cast<bf16*>(sG) + C * PT;
     __shared__ __attribute__((aligned(16))) bf16 sZh[WITH_Z ? C * PT : 8];  // T^{-T} rows, m slots
     __shared__ __attribute__((aligned(16))) bf16 sZl[WITH_Z ? C * PT : 8];
     __shared__ float sB[C];
@@ -265,26 +269,37 @@ __global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
     __syncthreads();
 
     // T^{-1} rows with the n axis in k-slot order, split hi/lo; for the key
-    // cache also T^{-T} rows with the m axis in slot order.
-    for (int u = tid; u < C * (C / 8); u += 256) {
-        const int row = u >> 3, s0 = (u & 7) * 8;
-        bf16x8 hi, lo;
+    // cache also T^{-T} rows with the m axis in slot order.  X is read into
+    // registers first: the hi/lo tiles overwrite it.
+    static_assert(C * (C / 8) == 2 * 256, "two 8-slot units per thread");
+    float xs[2][8], zs[2][8];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = tid + 256 * it, row = u >> 3, s0 = (u & 7) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int col = permk(s0 + e);
-            const float x = col <= row ? sG[col * GP + row] : 0.f;
-            hi[e] = static_cast<bf16>(x);
-            lo[e] = static_cast<bf16>(x - static_cast<float>(hi[e]));
+            xs[it][e] = col <= row ? sG[col * GP + row] : 0.f;
+            if (WITH_Z) zs[it][e] = col >= row ? sG[row * GP + col] : 0.f;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = tid + 256 * it, row = u >> 3, s0 = (u & 7) * 8;
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            hi[e] = static_cast<bf16>(xs[it][e]);
+            lo[e] = static_cast<bf16>(xs[it][e] - static_cast<float>(hi[e]));
         }
         *reinterpret_cast<bf16x8*>(sTh + row * PT + s0) = hi;
         *reinterpret_cast<bf16x8*>(sTl + row * PT + s0) = lo;
         if (WITH_Z) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int col = permk(s0 + e);
-                const float x = col >= row ? sG[row * GP + col] : 0.f;
-                hi[e] = static_cast<bf16>(x);
-                lo[e] = static_cast<bf16>(x - static_cast<float>(hi[e]));
+                hi[e] = static_cast<bf16>(zs[it][e]);
+                lo[e] = static_cast<bf16>(zs[it][e] - static_cast<float>(hi[e]));
             }
             *reinterpret_cast<bf16x8*>(sZh + row * PT + s0) = hi;
             *reinterpret_cast<bf16x8*>(sZl + row * PT + s0) = lo;
