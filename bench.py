@@ -148,7 +148,7 @@ def bench_fwd(args, cfg, torch, pa, inputs):
         "tflops_algorithmic": f["alg"] / (ms * 1e-3) / 1e12,
         "mfma_peak_frac_algorithmic": f["alg"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "stage_ms": {"prepare(path_ut)": prep_ms, "scan(path_fwd)": scan_ms},
-        "roofline": {"kernel": (f"path_fwd_bf16_d64_kernel<{'true' if cfg.gate else 'false'}>" if d == 64
+        "roofline": {"kernel": (f"path_fwd_bf16_d64pp_kernel<{'true' if cfg.gate else 'false'}>" if d == 64
                                 else f"path_fwd_bf16_kernel<{d},{'true' if cfg.gate else 'false'}>"),
                      "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,

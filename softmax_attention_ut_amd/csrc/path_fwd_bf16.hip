@@ -32,6 +32,8 @@
 // Block order: heaviest query blocks first; when BH is a multiple of 8 all
 // blocks of one head land on one XCD (blocks are dealt to the 8 XCDs
 // round-robin), so a head's chunks are reused out of that XCD's L2.
+#include <type_traits>
+
 #include "path_internal.h"
 
 namespace path {
@@ -55,7 +57,7 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
 typedef __attribute__((address_space(3))) void lds_void;
 
 // PV A operands from a V tile kept as it is ([64 tokens][64 d], 16-byte units
-// swizzled like every 64-wide tile) with LDS transpose loads.  Within each
+// swizzled by swz_v) with LDS transpose loads.  Within each
 // group of 16 lanes, ds_read_b64_tr_b16 gives lane i, element t, the element
 // i % 4 of the 8 bytes read by lane 4t + i/4.  So lane 4t + q reads 4
 // consecutive d of one token, and every lane receives one d column of four
@@ -63,10 +65,21 @@ typedef __attribute__((address_space(3))) void lds_void;
 // blocks of four, which this access respects.  The operand of k-step ks, rows
 // dt, takes two loads (slots 0-3 and 4-7); a lane's 8 byte offsets depend
 // on (ks & 1, load, dt), the rows 32 (ks >> 1) further on add 4096 bytes.
+//
+// One transpose load reads 8 bytes per lane: lanes 0-31 cover 64 bytes of each
+// of 4 consecutive token rows, lanes 32-63 the next 4 rows (two 256-byte
+// halves; by quarters, 16 lanes cover 32 bytes of each of 4 rows).  The V
+// tile's swizzle gv(r) takes row bits 2, 0, 1 as unit bits 0, 1, 2: rows r
+// and r + 2 then differ in unit bit 2, so the four rows' pieces of either
+// half, or of any quarter, fall on distinct LDS banks (64 banks of 4 bytes
+// for a 32-lane half, 32 for a 16-lane quarter).  The swizzle of the other
+// tiles, made for 16-byte row reads, puts rows r and r + 2 on the same banks
+// here.
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
-template <int COLS>
-__device__ __forceinline__ int swz_g(int r);
+__device__ __forceinline__ int swz_v(int r) {
+    return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2);
+}
 __device__ __forceinline__ void vtr_offsets(unsigned off[8], int lane) {
     const int hh = lane >> 5, hp = (lane >> 4) & 1, j = lane & 15;
 #pragma unroll
@@ -78,7 +91,7 @@ __device__ __forceinline__ void vtr_offsets(unsigned off[8], int lane) {
                 const int tok = permk(16 * par + 8 * hh + 4 * ins + (j >> 2));
                 const int d = permk(32 * dt + 16 * hp + 4 * (j & 3));
                 off[(par * 2 + ins) * 2 + dt] =
-                    static_cast<unsigned>((tok * 64 + (((d >> 3) ^ swz_g<64>(tok)) << 3) + (d & 7)) * 2);
+                    static_cast<unsigned>((tok * 64 + (((d >> 3) ^ swz_v(tok)) << 3) + (d & 7)) * 2);
             }
 }
 __device__ __forceinline__ bf16x8 pv_operand(const bf16* sv, const unsigned off[8], int dt, int ks) {
@@ -102,8 +115,6 @@ template <int COLS>
 __device__ __forceinline__ int swz_g(int r) {
     return COLS == 64 ? ((r ^ ((r >> 3) & 3)) & 7) : (r & 15);
 }
-template <int COLS>
-__device__ __forceinline__ int swz(int r, int u) { return r * COLS + ((u ^ swz_g<COLS>(r)) << 3); }
 
 // Asynchronous copy of a [ROWS][COLS] bf16 tile, contiguous in global memory,
 // into a swizzled LDS tile.  Each wave instruction fills one contiguous 1 KB
@@ -123,45 +134,39 @@ __device__ __forceinline__ void copy_async(bf16* lds, const bf16* g, int wave, i
     }
 }
 
-// Synchronous guarded copy (rows >= nvalid are zero) into a swizzled tile.
-template <int ROWS, int COLS>
+// Synchronous guarded copy (rows >= nvalid are zero) into a swizzled tile by
+// NT threads; VTILE: the V tile's swizzle.
+template <int ROWS, int COLS, int NT = 256, bool VTILE = false>
 __device__ __forceinline__ void copy_guarded(bf16* lds, const bf16* g, int nvalid, int tid) {
     constexpr int UPR = COLS / 8;
 #pragma unroll
-    for (int i = tid; i < ROWS * UPR; i += 256) {
+    for (int i = tid; i < ROWS * UPR; i += NT) {
         const int r = i / UPR, u = i % UPR;
         uint4 val = {0u, 0u, 0u, 0u};
         if (r < nvalid) val = *reinterpret_cast<const uint4*>(g + (size_t)r * COLS + u * 8);
-        *reinterpret_cast<uint4*>(lds + swz<COLS>(r, u)) = val;
+        const int x = VTILE ? swz_v(r) : swz_g<COLS>(r);
+        *reinterpret_cast<uint4*>(lds + r * COLS + ((u ^ x) << 3)) = val;
     }
 }
 
-// Asynchronous copy of one contiguous [64][64] bf16 tile (8 KB) into a
-// swizzled LDS tile, laid out as copy_async<64, 64> does: wave w fills the
-// 1 KB blocks w and w + 4.  The swizzle repeats every 32 rows, so one
-// per-lane source offset (tile64_lane_offset) serves both blocks and every
-// such tile; wave_u must be wave-uniform.
+// Copies of a contiguous [64][64] bf16 tile (8 KB) into a swizzled LDS tile
+// by 8 waves: wave w fills the 1 KB block w (rows 8w .. 8w+7, lane i -> LDS
+// bytes 16i .. 16i+15), its lane reading the global unit that belongs there.
+// Both swizzles depend on the row's low 3 bits only, so the offset is the
+// same for every tile of the kind.
 __device__ __forceinline__ unsigned tile64_lane_offset(int wave, int lane) {
     const int r = 8 * wave + (lane >> 3);
     const int u = (lane & 7) ^ swz_g<64>(r);
     return static_cast<unsigned>((r * 64 + u * 8) * 2);
 }
-__device__ __forceinline__ void copy_tile64(bf16* lds, const bf16* g, int wave_u, unsigned lane_off) {
-    const char* src = reinterpret_cast<const char*>(g);
-    char* dst = reinterpret_cast<char*>(lds) + wave_u * 1024;
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + lane_off), (lds_void*)dst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((gbl_void*)(src + 4096 + lane_off), (lds_void*)(dst + 4096), 16, 0, 0);
+__device__ __forceinline__ unsigned vtile_lane_offset(int wave, int lane) {
+    const int r = 8 * wave + (lane >> 3);
+    const int u = (lane & 7) ^ swz_v(r);
+    return static_cast<unsigned>((r * 64 + u * 8) * 2);
 }
 
 __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
-}
-// vmcnt(N): every vector-memory load but the N most recent ones has landed
-// (loads complete in issue order)
-template <int N>
-__device__ __forceinline__ void wait_vmem_but() {
-    static_assert(N >= 0 && N < 16, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | N);
 }
 
 __device__ __forceinline__ void decode_block(int bid, int BH, int nqb, int& head, int& qb) {
@@ -527,15 +532,17 @@ struct ScanSetup {
     bool active, qvalid;
 };
 
+// The wave's query chunk is qc, its query row within that chunk iloc.
 template <int D, bool GATE>
-__device__ __forceinline__ ScanSetup<D, GATE> scan_setup(const FwdArgs& a, WaveState<D, GATE>& st, int wave,
-                                                          int l32, int hh) {
+__device__ __forceinline__ ScanSetup<D, GATE> scan_setup(const FwdArgs& a, WaveState<D, GATE>& st, int head,
+                                                          int qb, int qc, int iloc, int l32, int hh) {
     constexpr int C = 64, DT = D / 32, KSD = D / 16;
     ScanSetup<D, GATE> u;
-    decode_block(blockIdx.x, a.BH, a.nqb, u.head, u.qb);
-    u.qc = 2 * u.qb + (wave >> 1);           // this wave's query chunk
+    u.head = head;
+    u.qb = qb;
+    u.qc = qc;
     u.active = u.qc < a.N;
-    u.iloc = (wave & 1) * 32 + l32;          // query row within its chunk
+    u.iloc = iloc;
     u.qi = u.qc * C + u.iloc;
     u.qvalid = u.active && u.qi < a.L;
 #pragma unroll
@@ -609,7 +616,10 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
     const int l32 = lane & 31, hh = lane >> 5;
     const int L = a.L, N = a.N, Lp = N * C;
     WaveState<D, GATE> st;
-    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, wave, l32, hh);
+    int head0, qb0;
+    decode_block(blockIdx.x, a.BH, a.nqb, head0, qb0);
+    const ScanSetup<D, GATE> u =
+        scan_setup<D, GATE>(a, st, head0, qb0, 2 * qb0 + (wave >> 1), (wave & 1) * 32 + l32, l32, hh);
     const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
     const bool active = u.active;
 
@@ -679,36 +689,196 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
     scan_store<D, GATE>(a, st, u, hh);
 }
 
-// d = 64: the query's own chunk with the rank-C form (scan_step), every chunk
-// to its left with the d x d carry (dense_step).  The two diagonal key chunks
-// of a block are the first two iterations and are peeled off the loop, so
-// the loop body holds only dense steps.
-template <bool GATE>
-__global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs a) {
-    constexpr int C = 64, D = 64;
-    constexpr int TILE = C * D;
-    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sM0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sM1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sWd[TILE];   // diagonal chunk: W
-    __shared__ __attribute__((aligned(1024))) bf16 sUd[TILE];   //                 -U^T
-    __shared__ __attribute__((aligned(1024))) bf16 sY[TILE];    //                 Y^T
-    // gate terms of the staged chunk: -loc_j for its 64 keys, then its chunk
-    // sum; the bias k-step rows of its keys
-    __shared__ __attribute__((aligned(256))) float sLoc0[C + 4];
-    __shared__ __attribute__((aligned(256))) float sLoc1[C + 4];
-    __shared__ __attribute__((aligned(1024))) bf16 sG0[GATE ? C * 16 : 8];
-    __shared__ __attribute__((aligned(1024))) bf16 sG1[GATE ? C * 16 : 8];
+// ---------------------------------------------------------------------------
+// d = 64, two waves per SIMD in alternating phases.
+//
+// A workgroup of 8 waves holds query chunks 4qb .. 4qb+3; waves w and w+4
+// (which the hardware places on the same SIMD) take the two 32-query halves
+// of chunk 4qb + w%4.  The block's own chunks are walked as in the 4-wave
+// kernel (every wave steps through each chunk, with a barrier per chunk).
+// Every chunk left of them is split per wave into a matrix phase (PV of the
+// previous chunk, logits and carry of this one: 26 MFMAs) and a vector phase
+// (the probabilities: 32 exps).  Waves 4..7 run one phase ahead of waves
+// 0..3 and a workgroup barrier separates the phases, so on every SIMD one
+// wave's MFMAs run while the other wave's vector instructions issue.
+//
+// Staging: the key chunk's K~, -M^T, gate rows and sums (set k % 2) and its
+// V tile (V set k % 2) are copied two phases before their first use; a wave
+// waits for its copies only at the barrier that ends a leader vector phase.
+// ---------------------------------------------------------------------------
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Matrix phase of one wave: O^T += V^T P^T for the pending probabilities pB
+// (V tile sv), then with QK the logits of the staged chunk sg (left in s as
+// z - m_run) and the carry of the query through it.
+//
+// Issue order: the PV operands are read first and the logit operands (K~
+// rows, bias rows) after them, so that the PV MFMAs cover the latency of the
+// latter; the -M^T operands are read in the shadow of the logit MFMAs, and
+// the carry MFMAs come last.
+template <bool GATE, bool QK>
+__device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], const bf16x8 pB[4],
+                                          const Stage<64>& sg, const bf16* sv, int l32, int hh) {
+    constexpr int D = 64, KS = 4;
+    const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
+    const unsigned lower = hh ? 0u : ~0u;
+    bf16x8 opv[2 * KS];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = pv_operand(sv, st.voff, dt, ks);
+    if (!QK) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
+        return;
+    }
+    bf16x8 opg[2], opk[2 * KS];
+    const float csum = GATE ? sg.loc[64] : 0.f;   // the chunk's gate sum, for dab
+    if (GATE) {
+        opg[0] = lds8(sg.gb + l32 * 16 + 8 * hh);
+        opg[1] = lds8(sg.gb + (32 + l32) * 16 + 8 * hh);
+    } else {
+        opg[0] = opg[1] = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
+    }
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);               // PV operand reads
+    __builtin_amdgcn_sched_group_barrier(0x100, GATE ? 11 : 8, 0);    // logit operand reads, csum
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                // PV MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 bq;
+    {
+        const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+        bf16 h, m, l;
+        split3(a_i - st.m_run, h, m, l);
+        bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
+    }
+    bf16x8 opm[2 * KS];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opm[KS * dt + ks] = lds8(sg.mt + (32 * dt + l32) * D + st.offD[ks]);
+    // the two 32-key tiles alternate, so no MFMA waits for the one before it
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
+        s[kt2] = mfma32(opg[kt2], bq, s[kt2]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
+    // logit MFMAs with the -M^T reads between them
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) st.qacc[dt] = mfma32(opm[KS * dt + ks], st.qB[ks], st.qacc[dt]);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if (GATE) st.dab += static_cast<double>(csum);
+}
+
+// Vector phase of one wave: the carried query's new operand, and the logits s
+// turned into probabilities pB (raising the running maximum when a row sum
+// passes kRescaleTrigger).
+template <bool GATE>
+__device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 s[2], bf16x8 pB[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
+    if (__any(!(psum <= kRescaleTrigger))) {
+        const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
+        raise_max(st, shift);
+        psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
+    }
+    st.l_run += psum;
+}
+
+// Workgroup barrier without a memory fence: stage copies stay in flight
+// across it (each wave waits for its own copies explicitly); the clobber keeps
+// the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// global -> LDS copies as global_load_lds does them (lane i: 16 or 4 bytes
+// from gbase + voff to lds + 16i or 4i), but issued as inline assembly: the
+// compiler then neither tracks them nor adds waits for them, so the caller
+// must wait (vmcnt) before the data is read.  gbase and lds are wave-uniform.
+// The copy takes its LDS base from M0: the assembly sets M0, leaves one wait
+// state before the copy, and restores M0 afterwards (the compiler keeps M0
+// for itself).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+__device__ __forceinline__ void dma_lds16(const void* gbase, unsigned voff, const void* lds) {
+    unsigned keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma_lds4(const void* gbase, unsigned voff, const void* lds) {
+    unsigned keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds_addr(lds)) : "memory");
+}
+
+template <bool GATE>
+__global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdArgs a) {
+    constexpr int C = 64, D = 64, NT = 512;
+    constexpr int TILE = C * D;
+    // Two stage sets, each one LDS object for a key chunk's K~, -M^T, V, bias
+    // rows and gate terms and one for an own chunk's W, -U^T, Y^T (the
+    // compiler tells copy targets in flight from tiles being read per object,
+    // and it tracks only a few objects).
+    struct ChunkTiles {
+        bf16 k[TILE];
+        bf16 m[TILE];
+        bf16 v[TILE];
+        bf16 gb[GATE ? C * 16 : 8];
+        float loc[C + 4];
+    };
+    struct OwnTiles {
+        bf16 w[TILE];
+        bf16 u[TILE];
+        bf16 y[TILE];
+    };
+    __shared__ __attribute__((aligned(1024))) ChunkTiles km0;
+    __shared__ __attribute__((aligned(1024))) ChunkTiles km1;
+    __shared__ __attribute__((aligned(1024))) OwnTiles dg0;
+    __shared__ __attribute__((aligned(1024))) OwnTiles dg1;
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const bool leader = wave_u >= 4;
+    const int nqb = (a.N + 3) / 4;
+
+    // One query block (head, qb): query chunks 4qb .. 4qb+3 of one head.  The
+    // arguments and the lane id come in through opaque copies, so that
+    // nothing derived from them is kept live from one block to the next.
+    auto item = [&](const int head, const int qb, const FwdArgs& a, const int lane_in) {
+    const int lane = lane_in & 63;
+    const int tid = wave_u * 64 + lane;
     const int l32 = lane & 31, hh = lane >> 5;
     const int L = a.L, N = a.N, Lp = N * C;
+    const unsigned loff = tile64_lane_offset(wave_u, lane);
+    const unsigned vloff = vtile_lane_offset(wave_u, lane);
+    const float c2 = a.scale2;
     WaveState<D, GATE> st;
-    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, wave, l32, hh);
-    const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
+    const ScanSetup<D, GATE> u =
+        scan_setup<D, GATE>(a, st, head, qb, 4 * qb + (wave_u & 3), (wave_u >> 2) * 32 + l32, l32, hh);
+    const int qc = u.qc, iloc = u.iloc;
     const bool active = u.active;
     vtr_offsets(st.voff, lane);
 
@@ -720,102 +890,198 @@ __global__ __launch_bounds__(256, 2) void path_fwd_bf16_d64_kernel(const FwdArgs
     const bf16* mtg = static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D;
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
     const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
-
-    const Stage<D> stage0{sK0, sWd, sUd, sV0, sM0, sLoc0, sG0};
-    const Stage<D> stage1{sK1, sWd, sUd, sV1, sM1, sLoc1, sG1};
     const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
 
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    const unsigned loff = tile64_lane_offset(wave_u, lane);
-    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
-        copy_tile64(sg.k, kt + (size_t)kc * TILE, wave_u, loff);
-        copy_tile64(sg.mt, mtg + (size_t)kc * TILE, wave_u, loff);
-        if ((kc + 1) * C <= L) copy_tile64(sg.v, vin + (size_t)kc * TILE, wave_u, loff);
-        else copy_guarded<C, D>(sg.v, vin + (size_t)kc * TILE, L - kc * C, tid);   // ragged: zero rows
-        if (GATE && wave_u < 2)      // bias rows: 2 KB, one 1 KB block per wave
+    const Stage<D> set0{km0.k, dg0.w, dg0.u, km0.v, km0.m, km0.loc, km0.gb};
+    const Stage<D> set1{km1.k, dg1.w, dg1.u, km1.v, km1.m, km1.loc, km1.gb};
+
+    // every [64][64] tile: wave w copies its 1 KB block w (rows 8w .. 8w+7)
+    auto tile = [&](bf16* lds, const bf16* g) {
+        __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(g) + loff),
+                                         (lds_void*)(reinterpret_cast<char*>(lds) + wave_u * 1024), 16, 0, 0);
+    };
+    auto issue_km = [&](const Stage<D>& sg, int kc) {   // K~, -M^T, bias rows, gate terms
+        tile(sg.k, kt + (size_t)kc * TILE);
+        tile(sg.mt, mtg + (size_t)kc * TILE);
+        if (GATE && wave_u < 2)
             __builtin_amdgcn_global_load_lds((gbl_void*)(gbg + (size_t)kc * C * 16 + wave_u * 512 + lane * 8),
                                              (lds_void*)(sg.gb + wave_u * 512), 16, 0, 0);
-        if (GATE && wave_u == 0) {
-            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
-                                             (lds_void*)sg.loc, 4, 0, 0);
+        if (GATE && wave_u == 2) {
+            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sg.loc, 4, 0, 0);
             if (lane == 0)
                 __builtin_amdgcn_global_load_lds((gbl_void*)(csg + kc), (lds_void*)(sg.loc + C), 4, 0, 0);
         }
     };
-    // the diagonal chunk's W (rows past L zero-filled), -U^T and Y^T
-    auto load_diag = [&](int kcd) {
-        copy_guarded<C, D>(sWd, win + (size_t)kcd * TILE, min(C, L - kcd * C), tid);
-        copy_tile64(sUd, ut + (size_t)kcd * TILE, wave_u, loff);
-        copy_tile64(sY, yt + (size_t)kcd * TILE, wave_u, loff);
+    auto issue_v = [&](const Stage<D>& sg, int kc) {
+        if ((kc + 1) * C <= L)
+            __builtin_amdgcn_global_load_lds(
+                (gbl_void*)(reinterpret_cast<const char*>(vin + (size_t)kc * TILE) + vloff),
+                (lds_void*)(reinterpret_cast<char*>(sg.v) + wave_u * 1024), 16, 0, 0);
+        else
+            copy_guarded<C, D, NT, true>(sg.v, vin + (size_t)kc * TILE, L - kc * C, tid);   // ragged: zero rows
     };
-    const float c2 = a.scale2;
-    // the wave's own chunk; afterwards the carried query is held scaled by c2
-    auto diag = [&](const Stage<D>& sg, int kcur) {
-        const bool carry = kcur > 0;
-        scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
-        if (carry) {
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-            if (GATE) st.dab += static_cast<double>(sg.loc[C]);
+    // an own chunk's W (rows past L zero-filled), -U^T and Y^T
+    auto issue_own = [&](const Stage<D>& sg, bf16* y, int kcd) {
+        if ((kcd + 1) * C <= L) tile(sg.w, win + (size_t)kcd * TILE);
+        else copy_guarded<C, D, NT>(sg.w, win + (size_t)kcd * TILE, L - kcd * C, tid);
+        tile(sg.u, ut + (size_t)kcd * TILE);
+        tile(y, yt + (size_t)kcd * TILE);
+    };
+    // ---- the block's own chunks ktop .. q0, every wave in step.  Chunk kc
+    // sits in set kc % 2, and the next chunk (with its own-chunk tiles) is
+    // copied while this one is computed; the steps are peeled so that every
+    // set is known at compile time (q0 is a multiple of 4). ----
+    const int q0 = 4 * qb;
+    const int ktop = min(q0 + 3, N - 1);
+    auto own_step = [&](int kc, const Stage<D>& cur, const Stage<D>& nxt, const bf16* ycur, bf16* ynxt) {
+        if (kc == ktop) {
+            issue_km(cur, kc);
+            issue_v(cur, kc);
+            issue_own(cur, const_cast<bf16*>(ycur), kc);
+            wait_vmem();
+            __syncthreads();
         }
+        if (kc > 0) {
+            issue_km(nxt, kc - 1);
+            issue_v(nxt, kc - 1);
+            if (kc > q0) issue_own(nxt, ynxt, kc - 1);
+        }
+        if (active && kc <= qc) {
+            if (kc == qc) {
+                const bool carry = kc > 0;
+                scan_step<D, GATE, true>(st, cur, ycur, l32, hh, iloc, carry, c2);
+                if (carry) {
+#pragma unroll
+                    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+                    if (GATE) st.dab += static_cast<double>(cur.loc[C]);
+                }
+            } else {
+                dense_step<GATE>(st, cur, l32, hh);
+            }
+        }
+        wait_vmem();
+        __syncthreads();
     };
-    auto dense = [&](const Stage<D>& sg) { dense_step<GATE>(st, sg, l32, hh); };
+    if (ktop >= q0 + 3) own_step(q0 + 3, set1, set0, dg1.y, dg0.y);
+    if (ktop >= q0 + 2) own_step(q0 + 2, set0, set1, dg0.y, dg1.y);
+    if (ktop >= q0 + 1) own_step(q0 + 1, set1, set0, dg1.y, dg0.y);
+    own_step(q0, set0, set1, dg0.y, dg1.y);
 
-    // top chunk kc0: diagonal for the waves of query chunk kc0.  When the
-    // block has both query chunks, the next chunk (2qb) is diagonal for waves
-    // 0, 1; the stage sets are chosen so that the loop starts on set 0.
-    const int kc0 = min(2 * qb + 1, N - 1);
-    const bool both = kc0 == 2 * qb + 1;
-    auto top = [&](const Stage<D>& cur, const Stage<D>& nxt) {
-        issue(cur, kc0);
-        load_diag(kc0);
-        wait_vmem();
-        __syncthreads();
-        if (kc0 > 0) issue(nxt, kc0 - 1);
-        if (active && qc == kc0) diag(cur, kc0);
-        wait_vmem();
-        __syncthreads();
-    };
-    if (both) top(stage0, stage1);
-    else top(stage1, stage0);
-    int kc = kc0 - 1;
-    if (both && kc >= 0) {
-        load_diag(kc);
-        wait_vmem();
-        __syncthreads();
-        if (kc > 0) issue(stage0, kc - 1);
-        if (active) {
-            if (qc == kc) diag(stage1, kc);
-            else dense(stage1);
+    // ---- chunks q0-1 .. 0 in phases.  Chunk k's K~/-M^T/gate terms sit in
+    // set k % 2, its V tile in that set's V tile.  Every wave runs
+    //     for k = q0-1 .. 0:  M(k); barrier; V(k); barrier        then PV(0)
+    // where M(k) = PV(k+1) (k < q0-1), logits and carry of k, and V(k) = the
+    // probabilities of k.  The followers (waves 0..3) enter one barrier late,
+    // so between two barriers one wave of each SIMD is in a matrix phase and
+    // the other in a vector phase.  Copies: at the start of its M(k) a leader
+    // issues its blocks of chunk k-1 (K~/-M^T) and V(k); at the start of its
+    // V(k) a follower issues its blocks of chunk k-2 and V(k-1) -- the same
+    // moment, one phase after the buffers' last reads.  Leaders wait for their
+    // copies at the end of V(k), followers at the end of M(k): two phases
+    // later, and before the barrier that opens the first phase reading them. ----
+    if (q0 > 0) {
+        // copies of the phase loop, issued out of the compiler's sight (it
+        // would otherwise pair a copy issued on one role's path with a read
+        // on the other's and wait for it); each wave waits for its own.
+        auto ktile = [&](bf16* lds, const bf16* g) {
+            dma_lds16(g, loff, reinterpret_cast<char*>(lds) + wave_u * 1024);
+        };
+        auto kissue = [&](const Stage<D>& sg, int kc) {
+            ktile(sg.k, kt + (size_t)kc * TILE);
+            ktile(sg.mt, mtg + (size_t)kc * TILE);
+            if (GATE && wave_u < 2)
+                dma_lds16(gbg + (size_t)kc * C * 16 + wave_u * 512, lane * 16, sg.gb + wave_u * 512);
+            if (GATE && wave_u == 2) {
+                dma_lds4(locg + kc * C, lane * 4, sg.loc);
+                if (lane == 0) dma_lds4(csg + kc, 0, sg.loc + C);
+            }
+        };
+        // the first matrix phase has no pending probabilities: its PV product
+        // adds zero (P = 0 against the V tile of chunk q0, which is staged)
+        f32x16 s[2];
+        bf16x8 pB[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pB[i] = bf16x8{};
+        const bool go = active;
+        if (!leader) {
+            if (q0 >= 2) kissue(set0, q0 - 2);
+            phase_barrier();
         }
-        wait_vmem();
-        __syncthreads();
-        --kc;
-    }
-    while (kc >= 0) {
-        if (kc > 0) issue(stage1, kc - 1);
-        if (active) dense(stage0);
-        wait_vmem();
-        __syncthreads();
-        if (--kc < 0) break;
-        if (kc > 0) issue(stage0, kc - 1);
-        if (active) dense(stage1);
-        wait_vmem();
-        __syncthreads();
-        --kc;
+        auto iter = [&](int k, const Stage<D>& ck, const Stage<D>& cn) {
+            // ck: chunk k and V(k); cn: chunk k +- 1 and V(k +- 1).  Chunks
+            // left of q0 are full, so V is copied without a guard.
+            if (leader) {
+                if (k >= 1) kissue(cn, k - 1);
+                if (k < q0 - 1) dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
+            }
+            if (go) pp_mphase<GATE, true>(st, s, pB, ck, cn.v, l32, hh);
+            if (!leader) wait_vmem();
+            phase_barrier();
+            if (!leader) {
+                if (k >= 2) kissue(ck, k - 2);
+                if (k >= 1) dma_lds16(vin + (size_t)(k - 1) * TILE, vloff, cn.v + wave_u * 512);
+            }
+            if (go) pp_vphase<GATE>(st, s, pB);
+            if (leader) wait_vmem();
+            phase_barrier();
+        };
+        for (int k = q0 - 1; k >= 0; k -= 2) {     // k odd, then k - 1 even
+            iter(k, set1, set0);
+            iter(k - 1, set0, set1);
+        }
+        if (go) pp_mphase<GATE, false>(st, s, pB, set0, set0.v, l32, hh);
+        if (leader) phase_barrier();
     }
     scan_store<D, GATE>(a, st, u, hh);
+    };
+
+    // Persistent workgroups, one per CU.  The query blocks qb and nqb-1-qb of
+    // a head together cost the same for every qb (the work of a block grows
+    // linearly with qb), so each workgroup takes whole pairs, dealt
+    // round-robin.  When BH and the grid are multiples of 8, workgroup b runs
+    // on XCD b % 8 (workgroups are dealt to the 8 XCDs in turn) and takes
+    // only heads h with h % 8 == b % 8, so a head's chunks are shared in one
+    // XCD's L2.
+    const int G = gridDim.x;
+    const int P = (nqb + 1) / 2;                 // pairs per head (an odd nqb leaves one block alone)
+    const bool by_xcd = (a.BH % 8) == 0 && (G % 8) == 0;
+    const int R = by_xcd ? G / 8 : G;
+    const int r = by_xcd ? blockIdx.x / 8 : blockIdx.x;
+    const int xcd = by_xcd ? blockIdx.x % 8 : 0;
+    const int npairs = (by_xcd ? a.BH / 8 : a.BH) * P;
+    for (int t = 0;; ++t) {                      // t-th block of this workgroup: pair r + R (t / 2), heavy half first
+        const int j = r + R * (t >> 1);
+        if (j >= npairs) break;
+        const int i = j / P, pr = j % P;
+        const int qb = (t & 1) ? pr : nqb - 1 - pr;
+        if ((t & 1) && qb == nqb - 1 - pr) continue;   // the lone middle block of an odd nqb
+        __syncthreads();                         // the previous block's tiles are no longer read
+        typedef const __attribute__((address_space(4))) FwdArgs* ArgPtr;
+        ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+        int ln = static_cast<int>(threadIdx.x & 63);
+        asm volatile("" : "+s"(ap), "+v"(ln));
+        item(by_xcd ? xcd + 8 * i : i, qb, *(const FwdArgs*)ap, ln);
+    }
 }
 
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s) {
     const dim3 grid(a.BH * a.nqb), block(256);
     if (a.D == 64) {
-        if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64_kernel<true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_fwd_bf16_d64_kernel<false>), grid, block, 0, s, a);
+        // persistent: one workgroup per CU (at most one per pair of query blocks)
+        int dev = 0, ncu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const long pairs = (long)a.BH * (((a.N + 3) / 4 + 1) / 2);
+        long g = ncu < pairs ? ncu : pairs;
+        if (g >= 8 && a.BH % 8 == 0) g -= g % 8;
+        const dim3 gridp(static_cast<unsigned>(g)), block8(512);
+        if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<true>), gridp, block8, 0, s, a);
+        else hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<false>), gridp, block8, 0, s, a);
     } else if (a.D == 128) {
         if (gate) hipLaunchKernelGGL((path_fwd_bf16_kernel<128, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((path_fwd_bf16_kernel<128, false>), grid, block, 0, s, a);

@@ -139,6 +139,33 @@ def test_bf16_heads_not_multiple_of_8():
     _check(out, ro, "bf16", "bf16 BH=5 out")
 
 
+def test_bf16_odd_query_block_count():
+    """N = 11 chunks: three blocks of four query chunks per head, so one block
+    of each head has no partner of equal and opposite weight."""
+    inp = generate(2, 4, 700, 64, dtype="bf16", gate=True, seed=45)
+    out, lse = _run_fwd(inp, 0.125)
+    ro, rl = _oracle_full(inp, 0.125)
+    _check(out, ro, "bf16", "bf16 BH=8 L=700 out")
+    _check(lse, rl, "bf16", "bf16 BH=8 L=700 lse")
+
+
+def test_bf16_more_block_pairs_than_workgroups():
+    """B*H = 9 heads of 16384 tokens: 9 * 32 pairs of query blocks, more than
+    one per CU, dealt without the per-XCD grouping (9 is not a multiple of 8).
+    Sampled rows of the first, a middle and the last head."""
+    L, s = 16384, 0.125
+    inp = generate(1, 9, L, 64, dtype="bf16", gate=True, seed=46)
+    out, lse = _run_fwd(inp, s)
+    rng = np.random.default_rng(146)
+    rows = _sample_rows(L, rng)
+    heads = [0, 4, 8]
+    hi = np.repeat(heads, len(rows))
+    ri = np.tile(rows, len(heads))
+    ro, rl, _, _ = oracle.rows(inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f, s, hi, ri)
+    _check(out.reshape(-1, L, 64)[hi, ri], ro, "bf16", f"BH=9 L=16k sampled out ({len(hi)} rows)")
+    _check(lse.reshape(-1, L)[hi, ri], rl, "bf16", "BH=9 L=16k sampled lse")
+
+
 def test_bf16_beta_zero_is_causal_attention():
     inp = generate(1, 2, 256, 64, dtype="bf16", gate=False, seed=42)
     inp.beta.zero_()
