@@ -692,19 +692,19 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
 // ---------------------------------------------------------------------------
 // d = 64, two waves per SIMD in alternating phases.
 //
-// A workgroup of 8 waves holds query chunks 4qb .. 4qb+3; waves w and w+4
-// (which the hardware places on the same SIMD) take the two 32-query halves
-// of chunk 4qb + w%4.  The block's own chunks are walked as in the 4-wave
-// kernel (every wave steps through each chunk, with a barrier per chunk).
-// Every chunk left of them is split per wave into a matrix phase (PV of the
-// previous chunk, logits and carry of this one: 26 MFMAs) and a vector phase
-// (the probabilities: 32 exps).  Waves 4..7 run one phase ahead of waves
-// 0..3 and a workgroup barrier separates the phases, so on every SIMD one
-// wave's MFMAs run while the other wave's vector instructions issue.
+// A workgroup of 8 waves holds query chunks 4qb .. 4qb+3 of one head; wave w
+// runs on SIMD w % 4 (the hardware deals a workgroup's waves to the SIMDs in
+// turn).  Query chunk 4qb + j is split between waves j and 7 - j, on two
+// different SIMDs.  The block's own chunks are walked with every wave in step
+// (a barrier per chunk); there each SIMD has at most one wave on a diagonal
+// step.  Every chunk left of them is split per wave into a matrix phase (PV
+// of the previous chunk, logits and carry of this one: 26 MFMAs) and a vector
+// phase (the probabilities: 32 exps).  Waves 4..7 run one phase ahead of
+// waves 0..3 and a workgroup barrier separates the phases, so on every SIMD
+// one wave's MFMAs run while the other wave's vector instructions issue.
 //
-// Staging: the key chunk's K~, -M^T, gate rows and sums (set k % 2) and its
-// V tile (V set k % 2) are copied two phases before their first use; a wave
-// waits for its copies only at the barrier that ends a leader vector phase.
+// Staging: a key chunk's K~, -M^T, V, gate rows and sums sit in stage set
+// k % 2 and are copied two phases before their first use.
 // ---------------------------------------------------------------------------
 
 // Matrix phase of one wave: O^T += V^T P^T for the pending probabilities pB
@@ -875,9 +875,12 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const unsigned loff = tile64_lane_offset(wave_u, lane);
     const unsigned vloff = vtile_lane_offset(wave_u, lane);
     const float c2 = a.scale2;
+    // query chunk 4qb + j: waves j (rows 0-31) and 7 - j (rows 32-63), which
+    // run on different SIMDs (wave w runs on SIMD w % 4), so that no SIMD has
+    // two diagonal steps at once in the own-chunk steps below
     WaveState<D, GATE> st;
-    const ScanSetup<D, GATE> u =
-        scan_setup<D, GATE>(a, st, head, qb, 4 * qb + (wave_u & 3), (wave_u >> 2) * 32 + l32, l32, hh);
+    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, head, qb, 4 * qb + (leader ? 7 - wave_u : wave_u),
+                                                     (wave_u >> 2) * 32 + l32, l32, hh);
     const int qc = u.qc, iloc = u.iloc;
     const bool active = u.active;
     vtr_offsets(st.voff, lane);
