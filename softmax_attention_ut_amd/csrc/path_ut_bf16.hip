@@ -73,8 +73,10 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& acc, int half, float sign) 
 
 }  // namespace
 
+// Three workgroups per CU where LDS allows it (d = 64 without Z: 46 KB, held
+// to 136 VGPRs by the bound); the other instances need more LDS per workgroup.
 template <int D, bool WITH_Z>
-__global__ __launch_bounds__(256) void path_ut_bf16_kernel(const UtArgs a) {
+__global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf16_kernel(const UtArgs a) {
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
     constexpr int PT = C + 8;     // pitch of [x][token-slot] bf16 tiles
