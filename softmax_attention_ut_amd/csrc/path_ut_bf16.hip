@@ -109,28 +109,38 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     const size_t rowbase = (size_t)head * Lp + p0;
     const size_t chunkbase = (size_t)head * N + c;
 
-    // ---- phase 0: stage W, K (rows), W^T (token slots), beta ----
+    // ---- phase 0: stage W, K (rows), W^T (token slots), beta.  Every load
+    // is issued before the first LDS write, so the stage waits for memory
+    // once. ----
     {
         const bf16* w = static_cast<const bf16*>(a.w) + ((size_t)head * L + p0) * D;
         const bf16* k = static_cast<const bf16*>(a.k) + ((size_t)head * L + p0) * D;
         const bf16* v = static_cast<const bf16*>(a.v) + ((size_t)head * L + p0) * D;
         constexpr int UPR = D / 8;
-        for (int u = tid; u < C * UPR; u += 256) {
-            const int r = u / UPR, d0 = (u % UPR) * 8;
-            bf16x8 wv = {}, kv = {}, vv = {};
+        constexpr int NU = C * UPR / 256;          // 16-byte units per thread
+        bf16x8 wv[NU], kv[NU], vv[NU];
+#pragma unroll
+        for (int it = 0; it < NU; ++it) {
+            const int u = tid + 256 * it, r = u / UPR, d0 = (u % UPR) * 8;
+            wv[it] = kv[it] = vv[it] = bf16x8{};
             if (r < nvalid) {
-                wv = ld8(w + (size_t)r * D + d0);
-                kv = ld8(k + (size_t)r * D + d0);
-                if (VT) vv = ld8(v + (size_t)r * D + d0);
+                wv[it] = ld8(w + (size_t)r * D + d0);
+                kv[it] = ld8(k + (size_t)r * D + d0);
+                if (VT) vv[it] = ld8(v + (size_t)r * D + d0);
             }
-            *reinterpret_cast<bf16x8*>(sW + r * PW + d0) = wv;
-            *reinterpret_cast<bf16x8*>(sK + r * PW + d0) = kv;
-            if (VT) *reinterpret_cast<bf16x8*>(sV + r * PW + d0) = vv;
+        }
+        const float bta = (tid < C && tid < nvalid) ? a.beta[(size_t)head * L + p0 + tid] : 0.f;
+#pragma unroll
+        for (int it = 0; it < NU; ++it) {
+            const int u = tid + 256 * it, r = u / UPR, d0 = (u % UPR) * 8;
+            *reinterpret_cast<bf16x8*>(sW + r * PW + d0) = wv[it];
+            *reinterpret_cast<bf16x8*>(sK + r * PW + d0) = kv[it];
+            if (VT) *reinterpret_cast<bf16x8*>(sV + r * PW + d0) = vv[it];
             const int slot = permk(r);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sWt[permk(d0 + e) * PT + slot] = wv[e];
+            for (int e = 0; e < 8; ++e) sWt[permk(d0 + e) * PT + slot] = wv[it][e];
         }
-        if (tid < C) sB[tid] = tid < nvalid ? a.beta[(size_t)head * L + p0 + tid] : 0.f;
+        if (tid < C) sB[tid] = bta;
     }
     __syncthreads();
 
