@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     const size_t rowbase = (size_t)head * Lp + p0;
     const size_t chunkbase = (size_t)head * N + c;
 
+    float lf_in = 0.f;
     // ---- phase 0: stage W, K (rows), W^T (token slots), beta.  Every load
     // is issued before the first LDS write, so the stage waits for memory
     // once. ----
@@ -130,6 +131,8 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             }
         }
         const float bta = (tid < C && tid < nvalid) ? a.beta[(size_t)head * L + p0 + tid] : 0.f;
+        // wave 1's log f for the gate terms (phase 2), loaded with the rest
+        if (wave == 1 && a.loc) lf_in = lane < nvalid ? a.log_f[(size_t)head * L + p0 + lane] : 0.f;
 #pragma unroll
         for (int it = 0; it < NU; ++it) {
             const int u = tid + 256 * it, r = u / UPR, d0 = (u % UPR) * 8;
@@ -204,8 +207,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             // forget gate: chunk-local suffix sums in log2 units, fp64.  Lane s
             // holds log2 f_s; an inclusive suffix scan over the 64 lanes gives
             // x_s = sum_{s' >= s}, so loc_s = -(x_s - log2 f_s), csum = x_0.
-            const double lf = lane < nvalid ? (double)a.log_f[(size_t)head * L + p0 + lane] * 1.4426950408889634
-                                            : 0.0;
+            const double lf = lane < nvalid ? (double)lf_in * 1.4426950408889634 : 0.0;
             double x = lf;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
