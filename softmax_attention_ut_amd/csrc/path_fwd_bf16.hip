@@ -807,6 +807,190 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
     st.l_run += psum;
 }
 
+// The d = 64 diagonal step of one wave (its own chunk), in three parts.
+//
+// Products: the rank-C form of the diagonal step (Chinese notes, training
+// strategy: full-matrix form), in the transposed orientation, with the query
+// not yet scaled by c2:
+//     X^T = W Q^T,  S^T = K~ Q^T + g (g_j = -loc_j / c2, two bf16 terms)
+//     S^T += Y^T strictUpper(X)^T          (keys m > i of the query's row i)
+//     Q^T += (-U^T) lower(X)^T             (the query carried to its chunk start)
+template <bool GATE>
+__device__ __forceinline__ void diag64_products(WaveState<64, GATE>& st, f32x16 s[2], const Stage<64>& sg,
+                                               const bf16* sy, int l32, int hh, int iloc, float c2) {
+    constexpr int D = 64, C = 64, KS = 4;
+    // each operand group is read under the MFMAs of the group before it
+    bf16x8 opw[2 * KS], opk[2 * KS], opy[2 * KS], opu[2 * KS];
+    f32x16 x[2];
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            x[kt2][v] = 0.f;
+            s[kt2][v] = 0.f;
+        }
+    float gl8[2] = {0.f, 0.f};
+    if (GATE) {
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) gl8[kt2] = sg.loc[32 * kt2 + l32];
+    }
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opw[KS * kt2 + ks] = lds8(sg.w + (32 * kt2 + l32) * D + st.offD[ks]);
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
+    // X^T = W Q^T
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) x[kt2] = mfma32(opw[KS * kt2 + ks], st.qB[ks], x[kt2]);
+    __builtin_amdgcn_sched_group_barrier(0x100, GATE ? 10 : 8, 0);   // W reads (+ gate terms)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                                     // X MFMAs, K~ reads between them
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opy[KS * kt2 + ks] = lds8(sy + (32 * kt2 + l32) * C + st.offD[ks]);
+    // S^T = K~ Q^T + g
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
+    if (GATE) {
+        bf16x8 ones = {};
+        if (hh == 0) {
+            ones[0] = static_cast<bf16>(1.f);
+            ones[1] = static_cast<bf16>(1.f);
+        }
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) {
+            const float g = -gl8[kt2] * (1.f / c2);
+            const bf16 gh = static_cast<bf16>(g);
+            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
+            bf16x8 ag = {};
+            if (hh == 0) {
+                ag[0] = gh;
+                ag[1] = gl;
+            }
+            s[kt2] = mfma32(ag, ones, s[kt2]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                                     // logit MFMAs, Y reads between them
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // split X^T at the query's row: xu = strictly upper part (m > i), x keeps m <= i
+    bf16x8 xu[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int v = 8 * (ks & 1) + t;
+            const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const float xv = x[ks >> 1][v];
+            xu[ks][t] = static_cast<bf16>(m > iloc ? xv : 0.f);
+            x[ks >> 1][v] = (m <= iloc) ? xv : 0.f;
+        }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) opu[KS * dt + ks] = lds8(sg.u + (32 * dt + l32) * C + st.offD[ks]);
+    // S^T += Y^T strictUpper(X)^T
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opy[KS * kt2 + ks], xu[ks], s[kt2]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {                                     // Y MFMAs, -U^T reads between them
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Q^T += (-U^T) lower(X)^T
+    bf16x8 xB[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) xB[ks] = pack8(x[ks >> 1], ks & 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) st.qacc[dt] = mfma32(opu[KS * dt + ks], xB[ks], st.qacc[dt]);
+}
+
+// Softmax: the causal mask (keys j <= i), the first running maximum and the
+// probabilities of z = c2 S + a_i; then the query, now at its chunk start, is
+// scaled by c2 and repacked, and the gate offset moves past the chunk (csum:
+// its gate sum).
+template <bool GATE>
+__device__ __forceinline__ void diag64_softmax(WaveState<64, GATE>& st, f32x16 s[2], bf16x8 pB[4],
+                                               int hh, int iloc, float c2, float csum) {
+    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            if ((32 * kt2 + 8 * (v >> 2) + 4 * hh + (v & 3)) > iloc) s[kt2][v] = -INFINITY;
+            mx = fmaxf(mx, s[kt2][v]);
+        }
+    mx = pair_max(mx);
+    const float cand = fmaf(mx, c2, a_i);
+    if (__any(cand > st.m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(st.m_run, cand);
+        const float alpha = fast_exp2(st.m_run - m_new);
+        st.m_run = m_new;
+        st.l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
+    }
+    const float msub = st.m_run - a_i;
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
+        }
+    }
+    st.l_run += psum;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    if (GATE) st.dab += static_cast<double>(csum);
+}
+
+// The whole step: products, softmax, then O^T += V^T P^T with the chunk's V.
+template <bool GATE>
+__device__ __forceinline__ void diag_step64(WaveState<64, GATE>& st, const Stage<64>& sg, const bf16* sy,
+                                            int l32, int hh, int iloc, float c2) {
+    f32x16 s[2];
+    bf16x8 pB[4];
+    const float csum = GATE ? sg.loc[64] : 0.f;
+    diag64_products<GATE>(st, s, sg, sy, l32, hh, iloc, c2);
+    diag64_softmax<GATE>(st, s, pB, hh, iloc, c2, csum);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) st.oacc[dt] = mfma32(pv_operand(sg.v, st.voff, dt, ks), pB[ks], st.oacc[dt]);
+}
+
 // Workgroup barrier without a memory fence: stage copies stay in flight
 // across it (each wave waits for its own copies explicitly); the clobber keeps
 // the compiler from moving LDS accesses across it.
@@ -951,17 +1135,7 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         }
         if (active && kc <= qc) {
             if (kc == qc) {
-                const bool carry = kc > 0;
-                scan_step<D, GATE, true>(st, cur, ycur, l32, hh, iloc, carry, c2);
-                if (carry) {
-#pragma unroll
-                    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
-#pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-                    if (GATE) st.dab += static_cast<double>(cur.loc[C]);
-                }
+                diag_step64<GATE>(st, cur, ycur, l32, hh, iloc, c2);
             } else {
                 dense_step<GATE>(st, cur, l32, hh);
             }
