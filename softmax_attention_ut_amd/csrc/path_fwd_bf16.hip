@@ -709,15 +709,16 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
 
 // Matrix phase of one wave: O^T += V^T P^T for the pending probabilities pB
 // (V tile sv), then with QK the logits of the staged chunk sg (left in s as
-// z - m_run) and the carry of the query through it.
+// z - m_run), and the -M^T operands of the chunk's carry read into opm (the
+// carry's MFMAs are issued in the vector phase, where they fill the matrix
+// pipe while the other wave of the SIMD issues the next logits).
 //
 // Issue order: the PV operands are read first and the logit operands (K~
 // rows, bias rows) after them, so that the PV MFMAs cover the latency of the
-// latter; the -M^T operands are read in the shadow of the logit MFMAs, and
-// the carry MFMAs come last.
+// latter; the -M^T operands are read in the shadow of the logit MFMAs.
 template <bool GATE, bool QK>
 __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], const bf16x8 pB[4],
-                                          const Stage<64>& sg, const bf16* sv, int l32, int hh) {
+                                          bf16x8 opm[8], const Stage<64>& sg, const bf16* sv, int l32, int hh) {
     constexpr int D = 64, KS = 4;
     const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
     const unsigned lower = hh ? 0u : ~0u;
@@ -760,7 +761,6 @@ __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], 
         split3(a_i - st.m_run, h, m, l);
         bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
     }
-    bf16x8 opm[2 * KS];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -783,21 +783,21 @@ __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], 
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) st.qacc[dt] = mfma32(opm[KS * dt + ks], st.qB[ks], st.qacc[dt]);
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     if (GATE) st.dab += static_cast<double>(csum);
 }
 
-// Vector phase of one wave: the carried query's new operand, and the logits s
-// turned into probabilities pB (raising the running maximum when a row sum
-// passes kRescaleTrigger).
+// Vector phase of one wave: the carry of the query through the chunk,
+// Q^T += (-M^T) Q^T (operands opm from the matrix phase; the MFMAs go first
+// and run under the probabilities), the logits s turned into probabilities
+// pB (raising the running maximum when a row sum passes kRescaleTrigger),
+// and the carried query's new operand.
 template <bool GATE>
-__device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 s[2], bf16x8 pB[4]) {
+__device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
+                                          const bf16x8 opm[8]) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) st.qacc[dt] = mfma32(opm[4 * dt + ks], st.qB[ks], st.qacc[dt]);
     float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
     if (__any(!(psum <= kRescaleTrigger))) {
         const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
@@ -805,6 +805,8 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
         psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
     }
     st.l_run += psum;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
 }
 
 // The d = 64 diagonal step of one wave (its own chunk), in three parts.
@@ -1180,7 +1182,7 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         // the first matrix phase has no pending probabilities: its PV product
         // adds zero (P = 0 against the V tile of chunk q0, which is staged)
         f32x16 s[2];
-        bf16x8 pB[4];
+        bf16x8 pB[4], opm[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) pB[i] = bf16x8{};
         const bool go = active;
@@ -1195,14 +1197,14 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
                 if (k >= 1) kissue(cn, k - 1);
                 if (k < q0 - 1) dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
             }
-            if (go) pp_mphase<GATE, true>(st, s, pB, ck, cn.v, l32, hh);
+            if (go) pp_mphase<GATE, true>(st, s, pB, opm, ck, cn.v, l32, hh);
             if (!leader) wait_vmem();
             phase_barrier();
             if (!leader) {
                 if (k >= 2) kissue(ck, k - 2);
                 if (k >= 1) dma_lds16(vin + (size_t)(k - 1) * TILE, vloff, cn.v + wave_u * 512);
             }
-            if (go) pp_vphase<GATE>(st, s, pB);
+            if (go) pp_vphase<GATE>(st, s, pB, opm);
             if (leader) wait_vmem();
             phase_barrier();
         };
@@ -1210,7 +1212,7 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
             iter(k, set1, set0);
             iter(k - 1, set0, set1);
         }
-        if (go) pp_mphase<GATE, false>(st, s, pB, set0, set0.v, l32, hh);
+        if (go) pp_mphase<GATE, false>(st, s, pB, opm, set0, set0.v, l32, hh);
         if (leader) phase_barrier();
     }
     scan_store<D, GATE>(a, st, u, hh);
