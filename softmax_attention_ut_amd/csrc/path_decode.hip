@@ -131,31 +131,66 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
 }
 
 template <int D>
-__global__ __launch_bounds__(D) void path_decode_combine_kernel(const DecodeArgs a) {
-    const int head = blockIdx.x, e = threadIdx.x;
-    const float* part = a.part + (size_t)head * a.nsplit * (D + 2);
+__global__ __launch_bounds__(256) void path_decode_combine_kernel(const DecodeArgs a) {
+    // One workgroup per head.  The splits' maxima and row sums are read in
+    // parallel (one split per thread) and reduced across the workgroup; each
+    // output element is then summed over the splits by 256 / D threads, whose
+    // loads do not depend on one another.
+    constexpr int NG = 256 / D;           // threads per output element
+    __shared__ float sred[4];
+    __shared__ float so[NG][D];
+    const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ns = a.nsplit;
+    const float* part = a.part + (size_t)head * ns * (D + 2);
+    auto block_reduce = [&](float x, bool is_max) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float y = __shfl_xor(x, off, 64);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        if (lane == 0) sred[wave] = x;
+        __syncthreads();
+        const float r = is_max ? fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]))
+                               : (sred[0] + sred[1]) + (sred[2] + sred[3]);
+        __syncthreads();
+        return r;
+    };
     float mm = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) mm = fmaxf(mm, part[s * (D + 2) + D]);
-    float ll = 0.f, oo = 0.f;
-    for (int s = 0; s < a.nsplit; ++s) {
-        const float ms = part[s * (D + 2) + D];
-        if (ms == -INFINITY) continue;
-        const float sc = exp2f(ms - mm);
-        ll += part[s * (D + 2) + D + 1] * sc;
-        oo += part[s * (D + 2) + e] * sc;
+    for (int sp = tid; sp < ns; sp += 256) mm = fmaxf(mm, part[(size_t)sp * (D + 2) + D]);
+    mm = block_reduce(mm, true);
+    float ll = 0.f;
+    for (int sp = tid; sp < ns; sp += 256) {
+        const float ms = part[(size_t)sp * (D + 2) + D];
+        if (ms != -INFINITY) ll += part[(size_t)sp * (D + 2) + D + 1] * exp2f(ms - mm);
     }
-    static_cast<bf16*>(a.out)[(size_t)head * D + e] = static_cast<bf16>(oo / ll);
-    if (e == 0 && a.lse) a.lse[head] = (mm + log2f(ll)) * kLn2;
+    ll = block_reduce(ll, false);
+    const int e = tid % D, gs = tid / D;
+    float oo = 0.f;
+#pragma unroll 4
+    for (int sp = gs; sp < ns; sp += NG) {
+        const float ms = part[(size_t)sp * (D + 2) + D];
+        const float ov = part[(size_t)sp * (D + 2) + e];
+        if (ms != -INFINITY) oo += ov * exp2f(ms - mm);
+    }
+    so[gs][e] = oo;
+    __syncthreads();
+    if (tid < D) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sum += so[g][tid];
+        static_cast<bf16*>(a.out)[(size_t)head * D + tid] = static_cast<bf16>(sum / ll);
+    }
+    if (tid == 0 && a.lse) a.lse[head] = (mm + log2f(ll)) * kLn2;
 }
 
 hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s) {
     const dim3 grid(a.nsplit, a.BH), block(256);
     if (D == 64) {
         hipLaunchKernelGGL(path_decode_split_kernel<64>, grid, block, 0, s, a);
-        hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
     } else if (D == 128) {
         hipLaunchKernelGGL(path_decode_split_kernel<128>, grid, block, 0, s, a);
-        hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(128), 0, s, a);
+        hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }
