@@ -207,7 +207,8 @@ def bench_decode(args, cfg, torch, pa, inputs):
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
         "roofline": {"kernel": "path_decode_split_kernel<128> + combine", "bound": "hbm",
                      "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None},
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": _traffic("path_decode_d128_L8k.md", "path_decode.hip")},
     }
     return res, None
 
