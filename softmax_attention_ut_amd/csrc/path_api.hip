@@ -194,7 +194,7 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w, const 
 
 size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype) {
     if (B < 1 || H < 1 || T_max < 1 || dtype != PATH_BF16 || (d != 64 && d != 128)) return 0;
-    const size_t nsplit_max = ((size_t)T_max + 255) / 256;
+    const size_t nsplit_max = ((size_t)T_max + kDecodeSplitQuantum - 1) / kDecodeSplitQuantum;
     return align256((size_t)B * H * nsplit_max * (d + 2) * sizeof(float));
 }
 
@@ -216,8 +216,6 @@ int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* 
     a.out = out_t; a.lse = lse_t;
     a.part = static_cast<float*>(workspace);
     a.BH = B * H; a.t = t; a.T_max = T_max;
-    a.keys_per_split = 256;
-    a.nsplit = (t + 1 + a.keys_per_split - 1) / a.keys_per_split;
     a.scale2 = scale * kLog2e;
     return launch_path_decode(a, d, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PATH_OK : PATH_ERR_HIP;

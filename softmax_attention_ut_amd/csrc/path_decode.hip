@@ -10,9 +10,10 @@
 // the cache: per key, w.k and q.k are reduced together, the updated key is
 // stored, and the score is q.k - beta (w.k)(q.w).
 //
-// Split-sequence layout: block (split, head) owns 256 consecutive slots and
-// writes a partial (m, l, o) in log2 units; path_decode_combine merges the
-// splits of a head.  Each group of G = D/8 lanes owns one key (16 bytes per
+// Split-sequence layout: block (split, head) owns a run of consecutive slots
+// (a multiple of 64, sized so that every block of the step is resident at
+// once) and writes a partial (m, l, o) in log2 units; path_decode_combine
+// merges the splits of a head.  Each group of G = D/8 lanes owns one key (16 bytes per
 // lane), so a wave streams 64/G keys per pass with 16-byte accesses.
 #include "path_internal.h"
 
@@ -57,53 +58,71 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
 
-    for (int jb = j0; jb < j1; jb += KPB) {
-        const int j = jb + wave * KPW + g;
-        const bool ok = j < j1;
-        float kf[8], vf[8];
-        if (ok) {
-            const bf16x8 k8 = (j < t) ? *reinterpret_cast<const bf16x8*>(kc + (size_t)j * D + 8 * gl)
-                                      : *reinterpret_cast<const bf16x8*>(kh + 8 * gl);
-            const bf16x8 v8 = (j < t) ? *reinterpret_cast<const bf16x8*>(vc + (size_t)j * D + 8 * gl)
-                                      : *reinterpret_cast<const bf16x8*>(vh + 8 * gl);
+    // Two keys per lane group per pass (the second KPB keys after the
+    // first), their loads issued together so that each wave has two lines
+    // of K and of V in flight.
+    for (int jb = j0; jb < j1; jb += 2 * KPB) {
+        int jj[2];
+        bool ok[2];
+        bf16x8 k8[2], v8[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { kf[e] = static_cast<float>(k8[e]); vf[e] = static_cast<float>(v8[e]); }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) { kf[e] = 0.f; vf[e] = 0.f; }
+        for (int h = 0; h < 2; ++h) {
+            jj[h] = jb + h * KPB + wave * KPW + g;
+            ok[h] = jj[h] < j1;
+            k8[h] = v8[h] = bf16x8{};
+            if (ok[h]) {
+                k8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl)
+                                    : *reinterpret_cast<const bf16x8*>(kh + 8 * gl);
+                v8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl)
+                                    : *reinterpret_cast<const bf16x8*>(vh + 8 * gl);
+            }
         }
-        float pw = 0.f, pq = 0.f;
+        float s[2], pw[2], pq[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pw += wf[e] * kf[e]; pq += qf[e] * kf[e]; }
+        for (int h = 0; h < 2; ++h) {
+            pw[h] = 0.f;
+            pq[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kf = static_cast<float>(k8[h][e]);
+                pw[h] += wf[e] * kf;
+                pq[h] += qf[e] * kf;
+            }
+        }
 #pragma unroll
         for (int off = G / 2; off > 0; off >>= 1) {
-            pw += __shfl_xor(pw, off, G);
-            pq += __shfl_xor(pq, off, G);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                pw[h] += __shfl_xor(pw[h], off, G);
+                pq[h] += __shfl_xor(pq[h], off, G);
+            }
         }
-        if (ok) {
-            float s;
-            if (j < t) {
-                const float ba = beta * pw;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            s[h] = -INFINITY;
+            if (!ok[h]) continue;
+            if (jj[h] < t) {
+                const float ba = beta * pw[h];
                 bf16x8 k8n;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) k8n[e] = static_cast<bf16>(kf[e] - ba * wf[e]);
-                *reinterpret_cast<bf16x8*>(kc + (size_t)j * D + 8 * gl) = k8n;
-                s = pq - ba * qw;
-            } else {   // j == t: the new key enters unchanged
-                bf16x8 k8n, v8n;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { k8n[e] = static_cast<bf16>(kf[e]); v8n[e] = static_cast<bf16>(vf[e]); }
-                *reinterpret_cast<bf16x8*>(kc + (size_t)j * D + 8 * gl) = k8n;
-                *reinterpret_cast<bf16x8*>(vc + (size_t)j * D + 8 * gl) = v8n;
-                s = pq;
+                for (int e = 0; e < 8; ++e) k8n[e] = static_cast<bf16>(static_cast<float>(k8[h][e]) - ba * wf[e]);
+                *reinterpret_cast<bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl) = k8n;
+                s[h] = (pq[h] - ba * qw) * a.scale2;
+            } else {   // j == t: the new key and value enter unchanged
+                *reinterpret_cast<bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl) = k8[h];
+                *reinterpret_cast<bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl) = v8[h];
+                s[h] = pq[h] * a.scale2;
             }
-            s *= a.scale2;
-            const float mn = fmaxf(m, s);
+        }
+        if (ok[0]) {   // ok[1] implies ok[0]
+            const float mn = fmaxf(m, fmaxf(s[0], s[1]));
             const float sc = exp2f(m - mn);
-            const float p = exp2f(s - mn);
-            l = l * sc + p;
+            const float p0 = exp2f(s[0] - mn);
+            const float p1 = ok[1] ? exp2f(s[1] - mn) : 0.f;
+            l = l * sc + p0 + p1;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = o[e] * sc + p * vf[e];
+            for (int e = 0; e < 8; ++e)
+                o[e] = o[e] * sc + p0 * static_cast<float>(v8[0][e]) + p1 * static_cast<float>(v8[1][e]);
             m = mn;
         }
     }
@@ -183,16 +202,51 @@ __global__ __launch_bounds__(256) void path_decode_combine_kernel(const DecodeAr
     if (tid == 0 && a.lse) a.lse[head] = (mm + log2f(ll)) * kLn2;
 }
 
-hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s) {
+// Workgroups of the split kernel that fit on the current device at once
+// (its CU count times the kernel's occupancy), queried once per device and d.
+static hipError_t resident_split_blocks(int D, int& n) {
+    static int cache[64][2];
+    int dev = 0, ncu = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int* slot = (dev >= 0 && dev < 64) ? &cache[dev][D == 128] : nullptr;
+    if (slot && *slot > 0) {
+        n = *slot;
+        return hipSuccess;
+    }
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<64>, 256, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128>, 256, 0);
+    if (e != hipSuccess) return e;
+    n = ncu * (per_cu > 0 ? per_cu : 1);
+    if (slot) *slot = n;
+    return hipSuccess;
+}
+
+hipError_t launch_path_decode(const DecodeArgs& args, int D, hipStream_t s) {
+    if (D != 64 && D != 128) return hipErrorInvalidValue;
+    // Split the t + 1 keys of each head so that all (split, head) workgroups
+    // run in one round: a second, partly filled round would leave most CUs
+    // idle for its whole length.  Splits are multiples of 64 keys (whole
+    // passes of a workgroup), at most ceil(T_max / 64) of them.
+    int resident = 0;
+    hipError_t e = resident_split_blocks(D, resident);
+    if (e != hipSuccess) return e;
+    DecodeArgs a = args;
+    const int nkeys = a.t + 1;
+    const int want = (resident + a.BH - 1) / a.BH;               // splits per head
+    int kps = (nkeys + want - 1) / want;
+    kps = ((kps + kDecodeSplitQuantum - 1) / kDecodeSplitQuantum) * kDecodeSplitQuantum;
+    a.keys_per_split = kps;
+    a.nsplit = (nkeys + kps - 1) / kps;
     const dim3 grid(a.nsplit, a.BH), block(256);
     if (D == 64) {
         hipLaunchKernelGGL(path_decode_split_kernel<64>, grid, block, 0, s, a);
         hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
-    } else if (D == 128) {
+    } else {
         hipLaunchKernelGGL(path_decode_split_kernel<128>, grid, block, 0, s, a);
         hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
-    } else {
-        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

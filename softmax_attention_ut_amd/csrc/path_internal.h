@@ -155,9 +155,13 @@ struct DecodeArgs {
     void* out;
     float* lse;
     float* part;           // [BH][nsplit][D + 2] partial (o, m, l)
-    int BH, t, T_max, nsplit, keys_per_split;
+    int BH, t, T_max, nsplit, keys_per_split;   // split sizes: set by launch_path_decode
     float scale2;
 };
+
+// Decode splits are multiples of this many keys, so a head has at most
+// ceil(T_max / kDecodeSplitQuantum) splits (the workspace holds that many).
+constexpr int kDecodeSplitQuantum = 64;
 
 // Host-side launchers (return hipError_t of the launch).
 hipError_t launch_path_ut_f32(const UtArgs& a, hipStream_t s);

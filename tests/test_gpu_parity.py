@@ -284,3 +284,10 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
 def test_decode_small_ragged(d):
     inp = generate(1, 3, 231, d, dtype="bf16", gate=False, seed=50)
     _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, [0, 1, 2], key_samples=40)
+
+
+def test_decode_short_prefix():
+    # t from 5 to 69: one split of 64 keys, then two (the split size is a
+    # multiple of 64 keys)
+    inp = generate(1, 2, 70, 64, dtype="bf16", gate=False, seed=52)
+    _decode_and_check(inp, 0.125, 5, 70, [0, 1], key_samples=10)
