@@ -127,6 +127,39 @@ def test_ut_identity_orientation():
     np.testing.assert_allclose(np.diag(tinv), beta, atol=1e-15)
 
 
+@pytest.mark.parametrize("seed", [5, 6])
+def test_ut_closed_forms(seed):
+    """Entries of the UT quantities in closed form, from explicit transitions
+    (no linear solve): T^{-1}[m][m] = beta_m and, for m > n,
+        T^{-1}[m][n] = -beta_m beta_n w_m^T H_{m-1} ... H_{n+1} w_n,
+    and the rows of U = T^{-1} W are U_m = beta_m w_m^T H_{m-1} ... H_0, so
+    ||U_m|| <= beta_m for unit w and 0 <= beta <= 2 (each H is then
+    non-expansive).  A transposed product order or a dropped beta fails."""
+    rng = np.random.default_rng(seed)
+    L, d = 9, 5
+    w = rng.standard_normal((L, d))
+    w /= np.linalg.norm(w, axis=1, keepdims=True)
+    beta = rng.uniform(0.05, 1.95, L)
+    H = [oracle.transition(w[t], beta[t]) for t in range(L)]
+
+    def prod(lo, hi):   # H_hi ... H_lo, H_lo applied first; identity if empty
+        P = np.eye(d)
+        for t in range(lo, hi + 1):
+            P = H[t] @ P
+        return P
+
+    tinv = oracle.ut_tinv(w, beta)
+    for m in range(L):
+        assert abs(tinv[m, m] - beta[m]) < 1e-15
+        for n in range(m):
+            ref = -beta[m] * beta[n] * (w[m] @ prod(n + 1, m - 1) @ w[n])
+            assert abs(tinv[m, n] - ref) < 1e-13
+    U = tinv @ w
+    for m in range(L):
+        np.testing.assert_allclose(U[m], beta[m] * (w[m] @ prod(0, m - 1)), atol=1e-13)
+    assert np.all(np.linalg.norm(U, axis=1) <= beta + 1e-13)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_full_matrix_form_matches_definition(seed):
     """lower(QK^T) - lower(QW^T) T^{-1} strictLower(WK^T) (Chinese notes,
