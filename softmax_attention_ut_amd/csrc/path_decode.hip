@@ -151,55 +151,44 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
 
 template <int D>
 __global__ __launch_bounds__(256) void path_decode_combine_kernel(const DecodeArgs a) {
-    // One workgroup per head.  The splits' maxima and row sums are read in
-    // parallel (one split per thread) and reduced across the workgroup; each
-    // output element is then summed over the splits by 256 / D threads, whose
-    // loads do not depend on one another.
-    constexpr int NG = 256 / D;           // threads per output element
-    __shared__ float sred[4];
-    __shared__ float so[NG][D];
-    const int head = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // One workgroup per head.  The head's partials (contiguous, nsplit rows
+    // of D + 2 floats) are read into LDS in one coalesced round per group of
+    // up to SG splits; thread e < D then folds the group into its running
+    // (m, l, o_e): group maximum from LDS, weights exp2(m_s - m).
+    constexpr int SG = 48;                // splits per LDS group (25 KB at D = 128)
+    __shared__ float sp[SG * (D + 2)];
+    const int head = blockIdx.x, tid = threadIdx.x;
     const int ns = a.nsplit;
     const float* part = a.part + (size_t)head * ns * (D + 2);
-    auto block_reduce = [&](float x, bool is_max) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float y = __shfl_xor(x, off, 64);
-            x = is_max ? fmaxf(x, y) : x + y;
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += SG) {
+        const int n = min(SG, ns - s0);
+        const float* src = part + (size_t)s0 * (D + 2);
+        if (s0 > 0) __syncthreads();      // the previous group is no longer read
+        for (int i = tid; i < n * (D + 2); i += 256) sp[i] = src[i];
+        __syncthreads();
+        if (tid < D) {
+            float mg = m;
+            for (int sIdx = 0; sIdx < n; ++sIdx) mg = fmaxf(mg, sp[sIdx * (D + 2) + D]);
+            if (mg != -INFINITY) {
+                const float c = exp2f(m - mg);
+                l *= c;
+                o *= c;
+                for (int sIdx = 0; sIdx < n; ++sIdx) {
+                    const float ms = sp[sIdx * (D + 2) + D];
+                    if (ms == -INFINITY) continue;
+                    const float wgt = exp2f(ms - mg);
+                    l += sp[sIdx * (D + 2) + D + 1] * wgt;
+                    o += sp[sIdx * (D + 2) + tid] * wgt;
+                }
+                m = mg;
+            }
         }
-        if (lane == 0) sred[wave] = x;
-        __syncthreads();
-        const float r = is_max ? fmaxf(fmaxf(sred[0], sred[1]), fmaxf(sred[2], sred[3]))
-                               : (sred[0] + sred[1]) + (sred[2] + sred[3]);
-        __syncthreads();
-        return r;
-    };
-    float mm = -INFINITY;
-    for (int sp = tid; sp < ns; sp += 256) mm = fmaxf(mm, part[(size_t)sp * (D + 2) + D]);
-    mm = block_reduce(mm, true);
-    float ll = 0.f;
-    for (int sp = tid; sp < ns; sp += 256) {
-        const float ms = part[(size_t)sp * (D + 2) + D];
-        if (ms != -INFINITY) ll += part[(size_t)sp * (D + 2) + D + 1] * exp2f(ms - mm);
     }
-    ll = block_reduce(ll, false);
-    const int e = tid % D, gs = tid / D;
-    float oo = 0.f;
-#pragma unroll 4
-    for (int sp = gs; sp < ns; sp += NG) {
-        const float ms = part[(size_t)sp * (D + 2) + D];
-        const float ov = part[(size_t)sp * (D + 2) + e];
-        if (ms != -INFINITY) oo += ov * exp2f(ms - mm);
-    }
-    so[gs][e] = oo;
-    __syncthreads();
     if (tid < D) {
-        float sum = 0.f;
-#pragma unroll
-        for (int g = 0; g < NG; ++g) sum += so[g][tid];
-        static_cast<bf16*>(a.out)[(size_t)head * D + tid] = static_cast<bf16>(sum / ll);
+        static_cast<bf16*>(a.out)[(size_t)head * D + tid] = static_cast<bf16>(o / l);
+        if (tid == 0 && a.lse) a.lse[head] = (m + log2f(l)) * kLn2;
     }
-    if (tid == 0 && a.lse) a.lse[head] = (mm + log2f(ll)) * kLn2;
 }
 
 // Workgroups of the split kernel that fit on the current device at once
