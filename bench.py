@@ -170,50 +170,62 @@ def bench_decode(args, cfg, torch, pa, inputs):
     B, H, L, T, d = cfg.B, cfg.H, cfg.L, cfg.L_total, cfg.d
     pre = lambda t: t[:, :, :L].contiguous()
     kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
-    steps_in = [{k: g[k][:, :, t].contiguous() for k in ("q", "k", "v", "w", "beta")}
-                for t in range(L, T)]
+    fc = pa.fcache_from_prefill(pre(g["log_f"]), T) if cfg.gate else None
+    names = ("q", "k", "v", "w", "beta") + (("log_f",) if cfg.gate else ())
+    steps_in = [{k: g[k][:, :, t].contiguous() for k in names} for t in range(L, T)]
+
+    def step(s, t):
+        if cfg.gate:
+            pa.path_decode_step_gated(kc, vc, fc, s["q"], s["k"], s["v"], s["w"], s["beta"],
+                                      s["log_f"], o, ls, t, cfg.scale, ws, stream)
+        else:
+            pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, t,
+                                cfg.scale, ws, stream)
     ws = pa.decode_workspace(B, H, T, d, pa.PATH_BF16, kc.device)
     o = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
     ls = torch.empty(B, H, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     kc0, vc0 = kc.clone(), vc.clone()
+    fc0 = fc.clone() if cfg.gate else None
     n = min(args.steps, T - L) if args.steps else T - L
     n = T - L if n <= 0 else n
     # warmup on a copy of the cache, then restore
     for i in range(min(args.warmup, n)):
-        s = steps_in[i]
-        pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, L + i,
-                            cfg.scale, ws, stream)
+        step(steps_in[i], L + i)
     kc.copy_(kc0)
     vc.copy_(vc0)
+    if cfg.gate:
+        fc.copy_(fc0)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(n):
-        s = steps_in[i]
-        pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, L + i,
-                            cfg.scale, ws, stream)
+        step(steps_in[i], L + i)
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = wall * 1e3 / n
     step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
-    bytes_total = sum(B * H * ((L + i) * d * 2 * 3 + 4 * d * 2) for i in range(n))
+    # per key: read k, write k, read v (bf16), and with the gate read F_j (fp32)
+    per_key = d * 2 * 3 + (4 if cfg.gate else 0)
+    bytes_total = sum(B * H * ((L + i) * per_key + 4 * d * 2) for i in range(n))
     gbs = bytes_total / (sum(step_ms) * 1e-3) / 1e9
     res = {
-        "metric": "PaTH decode tokens/s and HBM GB/s (bf16, d=128, in-place key update)",
+        "metric": (f"PaTH{'-FoX' if cfg.gate else ''} decode tokens/s and HBM GB/s "
+                   f"(bf16, d={d}, in-place key update)"),
         "value": B * n / (wall), "unit": "tokens/s",
         "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {n} PaTH decode steps after a prefill of "
+        "config": {"workload": f"{cfg.name}: {n} PaTH{'-FoX' if cfg.gate else ''} decode steps after a prefill of "
                                f"L={L}, B={B} H={H} d={d}, bf16 K/V cache",
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
-        "roofline": {"kernel": "path_decode_split_kernel<128> + combine", "bound": "hbm",
-                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "roofline": {"kernel": f"path_decode_split_kernel<{d}, {'true' if cfg.gate else 'false'}> + combine",
+                     "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": _traffic("path_decode_d128_L8k.md", "path_decode.hip")},
+                     "traffic": (_traffic("path_decode_d128_L8k.md", "path_decode.hip")
+                                 if cfg.name == "d128_L8k_decode" else None)},
     }
     return res, None
 
@@ -274,7 +286,7 @@ def main():
         print(json.dumps(res), flush=True)
         return
     cfg = inputs.CONFIGS[args.workload]
-    if args.workload == "d128_L8k_decode":
+    if args.workload.endswith("_decode"):
         res, inp = bench_decode(args, cfg, torch, pa, inputs)
     else:
         res, inp = bench_fwd(args, cfg, torch, pa, inputs)

@@ -177,6 +177,36 @@ int path_decode_step(void* k_cache, void* v_cache,
                      int dtype, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/*
+ * PaTH-FoX decode (the forget gate of PaTH-FoX in the decode step).  The
+ * PaTH-FoX weight multiplies the PaTH one by the product of the forget gates
+ * f_{j+1} .. f_t (Chinese notes, PaTH-FoX extension), i.e. adds
+ * F_t - F_j to the logit of key j, with F_t = sum_{s<=t} log f_s (natural
+ * log); the in-place key update and the rest of the step are those of
+ * path_decode_step.  The gate cache holds F_j per slot.
+ *
+ * path_fcache_from_prefill fills f_cache[0..L) from a prefill's log f:
+ *   log_f       [B][H][L] float32 (log f, not f).
+ *   f_cache     [B][H][T_max] float32, T_max >= L; slots [0, L) written
+ *               (accumulated in fp64, stored as fp32).
+ *
+ * path_decode_step_gated is path_decode_step plus:
+ *   f_cache     [B][H][T_max] float32 holding F_0 .. F_{t-1}; slot t is
+ *               written with F_t = F_{t-1} + log_f_t (F_{-1} = 0).
+ *   log_f_t     [B][H] float32, log f of token t.
+ * Both return PATH_ERR_INVALID for a null gate pointer or bad sizes, checked
+ * before any launch; the caller owns the gate cache.
+ */
+int path_fcache_from_prefill(const float* log_f, float* f_cache, int B, int H, int L,
+                             int T_max, void* stream);
+int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache,
+                           const void* q_t, const void* k_t, const void* v_t,
+                           const void* w_t, const float* beta_t, const float* log_f_t,
+                           void* out_t, float* lse_t,
+                           int B, int H, int t, int T_max, int d, float scale,
+                           int dtype, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

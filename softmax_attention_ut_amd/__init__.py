@@ -28,7 +28,8 @@ STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported size or chunk",
 EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes",
            "path_attn_fwd", "path_attn_fwd_prepare", "path_attn_fwd_scan",
            "path_kcache_workspace_bytes", "path_kcache_from_prefill",
-           "path_decode_workspace_bytes", "path_decode_step")
+           "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
+           "path_decode_step_gated")
 
 
 class PathError(RuntimeError):
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.path_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.path_decode_step.restype = I
     lib.path_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.path_fcache_from_prefill.restype = I
+    lib.path_fcache_from_prefill.argtypes = [P, P, I, I, I, I, P]
+    lib.path_decode_step_gated.restype = I
+    lib.path_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
     _lib = lib
     return lib
 
@@ -186,6 +191,32 @@ def path_decode_step(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t,
     _check(st, "path_decode_step")
 
 
+def path_fcache_from_prefill(log_f, f_cache, stream=None):
+    """log_f [B,H,L] float32; f_cache [B,H,T_max] float32 (slots [0,L) written)."""
+    lib = load_library()
+    _require_cuda(log_f, f_cache)
+    B, H, L = log_f.shape
+    T_max = f_cache.shape[2]
+    st = lib.path_fcache_from_prefill(_p(log_f), _p(f_cache), B, H, L, T_max, _stream(stream))
+    _check(st, "path_fcache_from_prefill")
+
+
+def path_decode_step_gated(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t,
+                           out_t, lse_t, t, scale, workspace=None, stream=None):
+    """path_decode_step with the PaTH-FoX gate: f_cache [B,H,T_max] float32
+    (F_0 .. F_{t-1} in, F_t written), log_f_t [B,H] float32."""
+    lib = load_library()
+    _require_cuda(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t, lse_t,
+                  workspace)
+    B, H, T_max, d = k_cache.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_decode_step_gated(_p(k_cache), _p(v_cache), _p(f_cache), _p(q_t), _p(k_t),
+                                    _p(v_t), _p(w_t), _p(beta_t), _p(log_f_t), _p(out_t),
+                                    _p(lse_t), B, H, int(t), T_max, d, float(scale),
+                                    _dt(k_cache), _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_decode_step_gated")
+
+
 # ---------------------------------------------------------------------------
 # conveniences (allocate with torch, then call the C ABI)
 # ---------------------------------------------------------------------------
@@ -220,6 +251,13 @@ def kcache_from_prefill(k, v, w, beta, T_max, stream=None):
     vc = torch.zeros(B, H, T_max, d, dtype=k.dtype, device=k.device)
     path_kcache_from_prefill(k, v, w, beta, kc, vc, ws, stream)
     return kc, vc
+
+
+def fcache_from_prefill(log_f, T_max, stream=None):
+    B, H, L = log_f.shape
+    fc = torch.zeros(B, H, T_max, dtype=torch.float32, device=log_f.device)
+    path_fcache_from_prefill(log_f, fc, stream)
+    return fc
 
 
 def decode_workspace(B, H, T_max, d, dtype, device):

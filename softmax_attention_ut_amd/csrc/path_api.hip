@@ -198,10 +198,11 @@ size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype) {
     return align256((size_t)B * H * nsplit_max * (d + 2) * sizeof(float));
 }
 
-int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
-                     const void* v_t, const void* w_t, const float* beta_t, void* out_t,
-                     float* lse_t, int B, int H, int t, int T_max, int d, float scale,
-                     int dtype, void* workspace, size_t ws_bytes, void* stream) {
+static int decode_step(void* k_cache, void* v_cache, float* f_cache, const void* q_t,
+                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                       const float* log_f_t, void* out_t, float* lse_t, int B, int H, int t,
+                       int T_max, int d, float scale, int dtype, void* workspace, size_t ws_bytes,
+                       void* stream) {
     if (B < 1 || H < 1 || T_max < 1 || t < 0 || t >= T_max || !valid_dtype(dtype))
         return PATH_ERR_INVALID;
     if (dtype != PATH_BF16 || (d != 64 && d != 128)) return PATH_ERR_UNSUPPORTED;
@@ -217,8 +218,37 @@ int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* 
     a.part = static_cast<float*>(workspace);
     a.BH = B * H; a.t = t; a.T_max = T_max;
     a.scale2 = scale * kLog2e;
+    a.log_f = log_f_t; a.f_cache = f_cache;
     return launch_path_decode(a, d, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PATH_OK : PATH_ERR_HIP;
+}
+
+int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
+                     const void* v_t, const void* w_t, const float* beta_t, void* out_t,
+                     float* lse_t, int B, int H, int t, int T_max, int d, float scale,
+                     int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    return decode_step(k_cache, v_cache, nullptr, q_t, k_t, v_t, w_t, beta_t, nullptr, out_t, lse_t,
+                       B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream);
+}
+
+int path_fcache_from_prefill(const float* log_f, float* f_cache, int B, int H, int L, int T_max,
+                             void* stream) {
+    if (B < 1 || H < 1 || L < 1 || T_max < L || !log_f || !f_cache) return PATH_ERR_INVALID;
+    FcacheArgs a{};
+    a.log_f = log_f; a.f_cache = f_cache;
+    a.BH = B * H; a.L = L; a.T_max = T_max;
+    return launch_path_fcache(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PATH_OK
+                                                                                 : PATH_ERR_HIP;
+}
+
+int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache, const void* q_t,
+                           const void* k_t, const void* v_t, const void* w_t,
+                           const float* beta_t, const float* log_f_t, void* out_t, float* lse_t,
+                           int B, int H, int t, int T_max, int d, float scale, int dtype,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    if (!f_cache || !log_f_t) return PATH_ERR_INVALID;
+    return decode_step(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t,
+                       lse_t, B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -19,7 +19,7 @@
 
 namespace path {
 
-template <int D>
+template <int D, bool GATE>
 __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs a) {
     constexpr int G = D / 8;              // lanes per key
     constexpr int KPW = 64 / G;           // keys per wave pass
@@ -40,6 +40,15 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
     bf16* kc = static_cast<bf16*>(a.k_cache) + (size_t)head * a.T_max * D;
     bf16* vc = static_cast<bf16*>(a.v_cache) + (size_t)head * a.T_max * D;
     const float beta = a.beta[head];
+    // forget gate (PaTH-FoX): the logit of key j gains F_t - F_j (natural
+    // log, F = inclusive prefix sum of log f), taken to log2 units.  F_t is
+    // formed from the cached F_{t-1}; the first split appends it to the cache.
+    const float* fc = GATE ? a.f_cache + (size_t)head * a.T_max : nullptr;
+    float f_t = 0.f;
+    if (GATE) {
+        f_t = (t > 0 ? fc[t - 1] : 0.f) + a.log_f[head];
+        if (split == 0 && tid == 0) a.f_cache[(size_t)head * a.T_max + t] = f_t;
+    }
 
     float qf[8], wf[8];
     {
@@ -65,6 +74,7 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
         int jj[2];
         bool ok[2];
         bf16x8 k8[2], v8[2];
+        float fj[2] = {0.f, 0.f};
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             jj[h] = jb + h * KPB + wave * KPW + g;
@@ -75,6 +85,7 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
                                     : *reinterpret_cast<const bf16x8*>(kh + 8 * gl);
                 v8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl)
                                     : *reinterpret_cast<const bf16x8*>(vh + 8 * gl);
+                if (GATE) fj[h] = (jj[h] < t) ? fc[jj[h]] : f_t;
             }
         }
         float s[2], pw[2], pq[2];
@@ -113,6 +124,7 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
                 *reinterpret_cast<bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl) = v8[h];
                 s[h] = pq[h] * a.scale2;
             }
+            if (GATE) s[h] += (f_t - fj[h]) * kLog2e;
         }
         if (ok[0]) {   // ok[1] implies ok[0]
             const float mn = fmaxf(m, fmaxf(s[0], s[1]));
@@ -205,8 +217,8 @@ static hipError_t resident_split_blocks(int D, int& n) {
     }
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<64>, 256, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128>, 256, 0);
+    e = D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<64, true>, 256, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128, true>, 256, 0);
     if (e != hipSuccess) return e;
     n = ncu * (per_cu > 0 ? per_cu : 1);
     if (slot) *slot = n;
@@ -230,13 +242,49 @@ hipError_t launch_path_decode(const DecodeArgs& args, int D, hipStream_t s) {
     a.keys_per_split = kps;
     a.nsplit = (nkeys + kps - 1) / kps;
     const dim3 grid(a.nsplit, a.BH), block(256);
+    const bool gate = a.f_cache != nullptr;
     if (D == 64) {
-        hipLaunchKernelGGL(path_decode_split_kernel<64>, grid, block, 0, s, a);
+        if (gate) hipLaunchKernelGGL((path_decode_split_kernel<64, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((path_decode_split_kernel<64, false>), grid, block, 0, s, a);
         hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
     } else {
-        hipLaunchKernelGGL(path_decode_split_kernel<128>, grid, block, 0, s, a);
+        if (gate) hipLaunchKernelGGL((path_decode_split_kernel<128, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((path_decode_split_kernel<128, false>), grid, block, 0, s, a);
         hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
     }
+    return hipGetLastError();
+}
+
+// Gate cache of a FoX prefill: F_j = sum_{s <= j} log f_s for j < L, one
+// workgroup per head.  Each thread sums a contiguous run of L / 256 tokens
+// in fp64, the runs' totals are scanned across the workgroup, and each
+// thread then writes its run's prefix sums (rounded to fp32).
+__global__ __launch_bounds__(256) void path_fcache_kernel(const FcacheArgs a) {
+    __shared__ double sTot[256];
+    const int head = blockIdx.x, tid = threadIdx.x;
+    const int run = (a.L + 255) / 256;
+    const int r0 = min(tid * run, a.L), r1 = min(r0 + run, a.L);
+    const float* lf = a.log_f + (size_t)head * a.L;
+    double tot = 0.0;
+    for (int j = r0; j < r1; ++j) tot += static_cast<double>(lf[j]);
+    sTot[tid] = tot;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {     // inclusive scan of the run totals
+        const double y = tid >= off ? sTot[tid - off] : 0.0;
+        __syncthreads();
+        sTot[tid] += y;
+        __syncthreads();
+    }
+    double acc = sTot[tid] - tot;                 // sum before this run
+    float* fc = a.f_cache + (size_t)head * a.T_max;
+    for (int j = r0; j < r1; ++j) {
+        acc += static_cast<double>(lf[j]);
+        fc[j] = static_cast<float>(acc);
+    }
+}
+
+hipError_t launch_path_fcache(const FcacheArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(path_fcache_kernel, dim3(a.BH), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

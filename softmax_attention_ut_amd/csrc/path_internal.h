@@ -157,6 +157,14 @@ struct DecodeArgs {
     float* part;           // [BH][nsplit][D + 2] partial (o, m, l)
     int BH, t, T_max, nsplit, keys_per_split;   // split sizes: set by launch_path_decode
     float scale2;
+    const float* log_f;    // [BH] log f_t, or null (no forget gate)
+    float* f_cache;        // [BH][T_max] prefix sums of log f, or null (no forget gate)
+};
+
+struct FcacheArgs {
+    const float* log_f;    // [BH][L]
+    float* f_cache;        // [BH][T_max]
+    int BH, L, T_max;
 };
 
 // Decode splits are multiples of this many keys, so a head has at most
@@ -170,5 +178,6 @@ hipError_t launch_path_fwd_f32(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s);
 hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s);
+hipError_t launch_path_fcache(const FcacheArgs& a, hipStream_t s);
 
 }  // namespace path

@@ -64,6 +64,9 @@ CONFIGS = {
     "fox_L16k": PathConfig("fox_L16k", 1, 16, 16384, 64, "bf16", True, 3),
     "d128_L8k_decode": PathConfig("d128_L8k_decode", 2, 32, 8192, 128, "bf16",
                                   False, 4, decode_steps=256),
+    # beyond the five: the same prefill + decode shape with the PaTH-FoX gate
+    "fox_d128_L8k_decode": PathConfig("fox_d128_L8k_decode", 2, 32, 8192, 128, "bf16",
+                                      True, 5, decode_steps=256),
 }
 
 

@@ -87,6 +87,21 @@ def test_decode_argument_errors_before_launch():
     assert lib.path_decode_step(*args(3, 16, 64, pa.PATH_BF16, 8)) == -4
 
 
+def test_gated_decode_argument_errors_before_launch():
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = lib.path_decode_workspace_bytes(1, 1, 16, 64, pa.PATH_BF16)
+    # (k_cache, v_cache, f_cache, q, k, v, w, beta, log_f, out, lse, B, H, t, T_max, d, ...)
+    args = lambda fc, lf, t: (p, p, fc, p, p, p, p, p, lf, p, None, 1, 1, t, 16, 64, 0.1,
+                              pa.PATH_BF16, p, ws, None)
+    assert lib.path_decode_step_gated(*args(None, p, 3)) == -1     # no gate cache
+    assert lib.path_decode_step_gated(*args(p, None, 3)) == -1     # no log f
+    assert lib.path_decode_step_gated(*args(p, p, 16)) == -1       # t >= T_max
+    assert lib.path_fcache_from_prefill(p, p, 1, 1, 20, 16, None) == -1   # T_max < L
+    assert lib.path_fcache_from_prefill(None, p, 1, 1, 8, 16, None) == -1
+    assert lib.path_fcache_from_prefill(p, p, 0, 1, 8, 16, None) == -1
+
+
 def test_kcache_argument_errors_before_launch():
     lib = pa.load_library()
     p = ctypes.c_void_p(4096)

@@ -241,8 +241,10 @@ def test_d128_prefill_kcache_and_decode():
 def _decode_and_check(inp, scale, L, T, heads, key_samples):
     g = _dev(inp)
     B, H, _, d = inp.q.shape
+    gated = inp.log_f is not None
     pre = lambda t: t[:, :, :L].contiguous()
     kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
+    fc = pa.fcache_from_prefill(pre(g["log_f"]), T) if gated else None
     torch.cuda.synchronize()
     rng = np.random.default_rng(7)
     keys = sorted(set(rng.integers(0, L, key_samples).tolist()) | {0, L - 1, max(L - 64, 0)})
@@ -257,9 +259,12 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
     for t in range(L, T):
         o = torch.empty(B, H, d, dtype=kc.dtype, device=kc.device)
         ls = torch.empty(B, H, dtype=torch.float32, device=kc.device)
-        pa.path_decode_step(kc, vc, g["q"][:, :, t].contiguous(), g["k"][:, :, t].contiguous(),
-                            g["v"][:, :, t].contiguous(), g["w"][:, :, t].contiguous(),
-                            g["beta"][:, :, t].contiguous(), o, ls, t, scale, ws)
+        step_in = [g[n][:, :, t].contiguous() for n in ("q", "k", "v", "w", "beta")]
+        if gated:
+            pa.path_decode_step_gated(kc, vc, fc, *step_in, g["log_f"][:, :, t].contiguous(), o, ls,
+                                      t, scale, ws)
+        else:
+            pa.path_decode_step(kc, vc, *step_in, o, ls, t, scale, ws)
         outs.append(o)
         lses.append(ls)
     torch.cuda.synchronize()
@@ -268,8 +273,14 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
     rows = np.arange(L, T)
     hi = np.repeat(heads, len(rows))
     ri = np.tile(rows, len(heads))
-    ro, rl, _, _ = oracle.rows(inp.q, inp.k, inp.v, inp.w, inp.beta, None, scale, hi, ri)
+    ro, rl, _, _ = oracle.rows(inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f, scale, hi, ri)
     _check(got[hi, ri - L], ro, "bf16", f"decode {T - L} steps out")
+    if gated:   # the gate cache holds the prefix sums of log f (fp32)
+        ref_f = np.cumsum(inp.log_f.double().numpy().reshape(B * H, -1)[:, :T], axis=1)
+        got_f = fc.double().cpu().numpy().reshape(B * H, T)
+        err = np.max(np.abs(got_f - ref_f) / np.maximum(1.0, np.abs(ref_f)))
+        print(f"gate cache: max rel err {err:.2e}")
+        assert err < 1e-5
     _check(gotl[hi, ri - L], rl, "bf16", f"decode {T - L} steps lse")
     # the cache after the last step against the oracle's in-place updated keys
     keys = sorted(set(rng.integers(0, T, key_samples).tolist()) | {0, T - 1})
@@ -284,6 +295,13 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
 def test_decode_small_ragged(d):
     inp = generate(1, 3, 231, d, dtype="bf16", gate=False, seed=50)
     _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, [0, 1, 2], key_samples=40)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_gated(d):
+    # PaTH-FoX decode: the gate cache from the prefill, then gated steps
+    inp = generate(1, 3, 231, d, dtype="bf16", gate=True, seed=53)
+    _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, [0, 1, 2], key_samples=30)
 
 
 def test_decode_short_prefix():
