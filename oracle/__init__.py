@@ -11,7 +11,10 @@ Two kinds of functions live here:
   definition, and selected transported keys;
 * numpy fp64 evaluations written straight from the pages' formulas, used to
   pin the C code and each other on tiny inputs: explicit d x d transition
-  matrices, the UT transform, and the full-matrix form of the logits.
+  matrices, the UT transform, and the full-matrix form of the logits;
+* the transition parameters w_t, beta_t from the layer input (low-rank map,
+  short convolution, L2 normalisation; 2 sigmoid), the reference of the
+  transition-prep kernel.
 
 Every function cites the passage it follows (PaTH paper pages: the Dutch
 technical summary and the Chinese paper notes).  All parts are pinned by
@@ -226,3 +229,33 @@ def full_matrix_logits(q, k, w, beta, scale):
     a = scale * a
     a[np.triu_indices(q.shape[0], 1)] = -np.inf
     return a
+
+
+def transition_prep(x, w_down, w_up, conv, u, b, d):
+    """The transition parameters of every token from the layer input
+    (Chinese notes, key design; Dutch summary section 2): w_t = L2-normalised
+    short convolution (filter size 3) of a low-rank linear map of x_t, per
+    head, and beta_t = 2 sigmoid(u^T x_t + b) per head.
+
+    Readings where the pages are silent: the low-rank map is
+    z_t = W_up (W_down x_t); the convolution is causal and depthwise,
+    c_t = conv[:, 0] z_t + conv[:, 1] z_{t-1} + conv[:, 2] z_{t-2} (zero
+    before the first token), with no bias or activation; each head's d-vector
+    is divided by its norm, a zero vector staying zero.
+
+    x [B, L, Dm]; w_down [r, Dm]; w_up [H*d, r]; conv [H*d, 3]; u [H, Dm];
+    b [H].  Returns w [B, H, L, d] and beta [B, H, L], fp64."""
+    x, w_down, w_up, conv, u, b = (np.asarray(t, dtype=np.float64)
+                                   for t in (x, w_down, w_up, conv, u, b))
+    B, L, _ = x.shape
+    H = u.shape[0]
+    z = (x @ w_down.T) @ w_up.T                        # [B, L, H*d]
+    c = conv[:, 0] * z
+    c[:, 1:] += conv[:, 1] * z[:, :-1]
+    c[:, 2:] += conv[:, 2] * z[:, :-2]
+    c = c.reshape(B, L, H, d).transpose(0, 2, 1, 3)    # [B, H, L, d]
+    n = np.linalg.norm(c, axis=-1, keepdims=True)
+    w = np.divide(c, n, out=np.zeros_like(c), where=n > 0)
+    logit = x @ u.T + b                                # [B, L, H]
+    beta = 2.0 / (1.0 + np.exp(-logit))
+    return w, beta.transpose(0, 2, 1)

@@ -325,3 +325,88 @@ def test_oracle_regression_fixture():
     out, lse, _, _ = oracle.recurrent(inp.q, inp.k, inp.v, inp.w, inp.beta, None, cfg.scale)
     np.testing.assert_allclose(out[0, 0], np.array(rec["out"]), atol=1e-12)
     np.testing.assert_allclose(lse[0, 0], np.array(rec["lse"]), atol=1e-12)
+
+
+def _prep_identity(B=2, L=7, H=3, d=4, seed=9):
+    """Inputs whose low-rank map is the identity (r = Dm = H*d)."""
+    rng = np.random.default_rng(seed)
+    Dm = H * d
+    x = rng.standard_normal((B, L, Dm))
+    return x, np.eye(Dm), np.eye(Dm), H, d
+
+
+@pytest.mark.parametrize("tap", [0, 1, 2])
+def test_transition_prep_shift_taps(tap):
+    """With z = x and a single convolution tap at lag `tap`, w_t is the head's
+    slice of x_{t-tap} divided by its norm (zero before the first token), and
+    beta = 2 sigmoid(0) = 1 for u = 0, b = 0.  A non-causal or reversed
+    convolution, a norm over the wrong axis or a head/d interleave fails."""
+    x, wd, wu, H, d = _prep_identity()
+    B, L, Dm = x.shape
+    conv = np.zeros((Dm, 3))
+    conv[:, tap] = 1.0
+    w, beta = oracle.transition_prep(x, wd, wu, conv, np.zeros((H, Dm)), np.zeros(H), d)
+    assert w.shape == (B, H, L, d) and beta.shape == (B, H, L)
+    for b_ in range(B):
+        for h in range(H):
+            for t in range(L):
+                if t < tap:
+                    assert np.all(w[b_, h, t] == 0.0)
+                    continue
+                seg = x[b_, t - tap, h * d:(h + 1) * d]
+                np.testing.assert_allclose(w[b_, h, t], seg / np.sqrt(np.sum(seg * seg)), atol=1e-14)
+    np.testing.assert_allclose(beta, 1.0, atol=0)
+
+
+def test_transition_prep_conv_and_gate_values():
+    """Three taps add up (linearity of the convolution in the taps, with the
+    un-normalised sum checked through the direction), and
+    beta = 2 sigmoid(u.x + b) takes its closed values: b = ln 3 gives 1.5,
+    u.x + b = -ln 3 gives 0.5; beta stays in (0, 2)."""
+    x, wd, wu, H, d = _prep_identity(L=9)
+    B, L, Dm = x.shape
+    taps = np.array([0.5, -2.0, 0.25])
+    conv = np.tile(taps, (Dm, 1))
+    w, _ = oracle.transition_prep(x, wd, wu, conv, np.zeros((H, Dm)), np.zeros(H), d)
+    for t in range(2, L):
+        c = taps[0] * x[:, t] + taps[1] * x[:, t - 1] + taps[2] * x[:, t - 2]
+        for h in range(H):
+            seg = c[:, h * d:(h + 1) * d]
+            np.testing.assert_allclose(w[:, h, t], seg / np.linalg.norm(seg, axis=-1, keepdims=True),
+                                       atol=1e-13)
+    _, beta = oracle.transition_prep(x, wd, wu, conv, np.zeros((H, Dm)), np.full(H, np.log(3.0)), d)
+    np.testing.assert_allclose(beta, 1.5, atol=1e-15)
+    u = np.zeros((H, Dm))
+    u[:, 0] = 1.0
+    bias = -np.log(3.0) - x[0, 0, 0]
+    _, beta = oracle.transition_prep(x, wd, wu, conv, u, np.full(H, bias), d)
+    np.testing.assert_allclose(beta[0, :, 0], 0.5, atol=1e-15)
+    assert np.all((beta > 0) & (beta < 2))
+
+
+def test_transition_prep_low_rank_invariants():
+    """A random low-rank map: every nonzero w_t is a unit vector, scaling W_up
+    by a positive factor changes nothing and by -1 flips the sign (the norm is
+    taken after the map), and a rank-1 map makes every head's w_t (t >= 2)
+    parallel to that head's slice of the map's single column."""
+    rng = np.random.default_rng(12)
+    B, L, H, d, Dm, r = 2, 8, 3, 5, 11, 4
+    x = rng.standard_normal((B, L, Dm))
+    wd = rng.standard_normal((r, Dm))
+    wu = rng.standard_normal((H * d, r))
+    conv = rng.standard_normal((H * d, 3))
+    u = rng.standard_normal((H, Dm))
+    b = rng.standard_normal(H)
+    w, beta = oracle.transition_prep(x, wd, wu, conv, u, b, d)
+    np.testing.assert_allclose(np.linalg.norm(w, axis=-1), 1.0, atol=1e-13)
+    w2, beta2 = oracle.transition_prep(x, wd, 3.5 * wu, conv, u, b, d)
+    np.testing.assert_allclose(w2, w, atol=1e-13)
+    np.testing.assert_allclose(beta2, beta, atol=0)
+    w3, _ = oracle.transition_prep(x, wd, -wu, conv, u, b, d)
+    np.testing.assert_allclose(w3, -w, atol=1e-13)
+    col = rng.standard_normal(H * d)
+    conv1 = np.tile([1.0, 0.0, 0.0], (H * d, 1))
+    w4, _ = oracle.transition_prep(x, wd[:1], col[:, None], conv1, u, b, d)
+    for h in range(H):
+        e = col[h * d:(h + 1) * d] / np.linalg.norm(col[h * d:(h + 1) * d])
+        np.testing.assert_allclose(np.abs(w4[:, h] @ e), 1.0, atol=1e-13)
