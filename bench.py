@@ -9,7 +9,10 @@ synthetic inputs already resident in HBM.  Default workload: PaTH-FoX,
 B=8, H=24, L=4096, d=64, bf16.  Other forward workloads: bf16_L1k,
 fox_L16k, d128_L8k_prefill (B=2, H=32, L=8192, d=128).  With --workload
 d128_L8k_decode the step is one decode step (in-place key-cache update +
-one-token attention) and the 256 steps after that prefill are timed.
+one-token attention) and the 256 steps after that prefill are timed.  With
+--workload transition_L4k the step is one path_transition_prep launch (w and
+beta of every token from the layer input; B=8, L=4096, width 1536, rank 64,
+H=24, d=64).
 
 Prints one JSON line: effective TFLOP/s (2*B*H*L^2*d per forward), tokens/s,
 the roofline of the dominant kernel (HIP events on its launch stream) and the
@@ -230,6 +233,81 @@ def bench_decode(args, cfg, torch, pa, inputs):
     return res, None
 
 
+def transition_bytes_flops(cfg):
+    """Algorithmic HBM bytes and FLOPs of one path_transition_prep launch:
+    read x (bf16) once and the weights once, write w (bf16) and beta (fp32);
+    the low-rank map and the beta projection 2 (r + H) Dm per token, the up
+    projection 2 H d r, the convolution and the norm 8 H d per token."""
+    B, L, Dm, r, H, d = cfg.B, cfg.L, cfg.Dm, cfg.r, cfg.H, cfg.d
+    weights = (r + H) * Dm * 2 + H * d * r * 2 + H * d * 3 * 4 + H * 4
+    nbytes = B * L * Dm * 2 + B * H * L * d * 2 + B * H * L * 4 + weights
+    flops = B * L * (2.0 * (r + H) * Dm + 2.0 * H * d * r + 8.0 * H * d)
+    return nbytes, flops
+
+
+def bench_transition(args, cfg, torch, pa, inputs):
+    inp = inputs.generate_transition(cfg.B, cfg.L, cfg.Dm, cfg.r, cfg.H, cfg.d, seed=cfg.seed)
+    g = {k: t.cuda() for k, t in vars(inp).items()}
+    w = torch.empty(cfg.B, cfg.H, cfg.L, cfg.d, dtype=torch.bfloat16, device="cuda")
+    beta = torch.empty(cfg.B, cfg.H, cfg.L, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.path_transition_prep(g["x"], g["w_down"], g["w_up"], g["conv"], g["u"], g["b"], w,
+                                beta, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    nbytes, flops = transition_bytes_flops(cfg)
+    gbs = nbytes / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "PaTH transition parameters (w, beta) from the layer input: tokens/s and HBM GB/s",
+        "value": cfg.B * cfg.L / (ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={cfg.B} L={cfg.L} width={cfg.Dm} rank={cfg.r} "
+                               f"H={cfg.H} d={cfg.d}, bf16 in, bf16 w + fp32 beta out",
+                   "global_batch": cfg.B, "seq_len": cfg.L, "parallelism": "single GPU"},
+        "tflops": flops / (kern_ms * 1e-3) / 1e12,
+        "roofline": {"kernel": f"path_transition_kernel<{cfg.d}, {cfg.r}>", "bound": "hbm",
+                     "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": _traffic("path_transition_L4k.md", "path_transition.hip"),
+                     "algorithmic_bytes_per_launch": nbytes},
+    }
+    return res, inp
+
+
+def transition_cpu_baseline(inp, cfg, threads):
+    """The fp64 oracle (numpy) on the first sequence of the same inputs with
+    `threads` BLAS threads, extrapolated to the whole batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    import oracle
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        oracle.transition_prep(inp.x[:1].double().numpy(), inp.w_down.double().numpy(),
+                               inp.w_up.double().numpy(), inp.conv.double().numpy(),
+                               inp.u.double().numpy(), inp.b.double().numpy(), cfg.d)
+        dt = time.perf_counter() - t0
+    t_full = dt * cfg.B
+    return {"value": cfg.B * cfg.L / t_full, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"1 of {cfg.B} sequences ({cfg.L} tokens), fp64 numpy oracle, "
+                      f"{dt:.2f} s wall; job time extrapolated x{cfg.B}"}
+
+
 def copy_calibration(mib, torch):
     """A plain device-to-device copy of a known size: its FETCH_SIZE /
     WRITE_SIZE counters calibrate the HBM-traffic figures of the kernels."""
@@ -283,6 +361,13 @@ def main():
         res, inp = bench_fwd(args, cfg, torch, pa, inputs)
         res["config"]["workload"] = (f"d128_L8k_prefill: PaTH forward B={cfg.B} H={cfg.H} "
                                      f"L={cfg.L} d={cfg.d} bf16 (the prefill of d128_L8k_decode)")
+        print(json.dumps(res), flush=True)
+        return
+    if args.workload in inputs.TRANSITION_CONFIGS:
+        cfg = inputs.TRANSITION_CONFIGS[args.workload]
+        res, inp = bench_transition(args, cfg, torch, pa, inputs)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = transition_cpu_baseline(inp, cfg, max(1, args.cpu_threads))
         print(json.dumps(res), flush=True)
         return
     cfg = inputs.CONFIGS[args.workload]

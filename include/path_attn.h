@@ -207,6 +207,41 @@ int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache,
                            int dtype, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/*
+ * Transition parameters of every token from the layer input, the step ahead
+ * of the attention (Chinese notes, "key design": w_t from a low-rank linear
+ * layer, a short convolution of filter size 3 and an L2 normalisation;
+ * beta_t = 2 sigmoid(u^T x_t + b); Dutch summary section 2, "Kernmechanisme"):
+ * for token t and head h,
+ *     z_t    = W_up (W_down x_t)                           (low-rank map)
+ *     c_t    = conv[:,0] * z_t + conv[:,1] * z_{t-1} + conv[:,2] * z_{t-2}
+ *              (depthwise and causal; z before the first token is 0)
+ *     w_t    = c_t[h*d .. h*d+d) / || c_t[h*d .. h*d+d) ||   (0 if that is 0)
+ *     beta_t = 2 sigmoid(u_h . x_t + b_h)
+ * Readings where the pages are silent: no bias in the low-rank map, no bias
+ * or activation in the convolution, one norm per head's d-vector.
+ *
+ *   x       [B][L][Dm]   bf16   layer input (token-major)
+ *   w_down  [r][Dm]      bf16
+ *   w_up    [H*d][r]     bf16
+ *   conv    [H*d][3]     float32, tap k multiplies z_{t-k}
+ *   u       [H][Dm]      bf16
+ *   b       [H]          float32
+ *   w       [B][H][L][d] bf16 out, the layout path_attn_fwd takes
+ *   beta    [B][H][L]    float32 out
+ * dtype must be PATH_BF16 (PATH_F32: PATH_ERR_UNSUPPORTED).  Supported sizes:
+ * d in {64, 128}, r in {32, 64}, r + H <= 128, Dm a positive multiple of 128
+ * (else PATH_ERR_UNSUPPORTED); a null pointer or a size below 1 is
+ * PATH_ERR_INVALID.  Products accumulate in float32 (the low-rank
+ * intermediate W_down x_t enters the second product as a bf16 pair, high and
+ * low part); w is rounded to bf16 once, after the normalisation.  The inputs
+ * are only read; w and beta are overwritten.
+ */
+int path_transition_prep(const void* x, const void* w_down, const void* w_up,
+                         const float* conv, const void* u, const float* b,
+                         void* w, float* beta, int B, int L, int Dm, int r, int H,
+                         int d, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

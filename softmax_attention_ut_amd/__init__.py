@@ -29,7 +29,7 @@ EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes"
            "path_attn_fwd", "path_attn_fwd_prepare", "path_attn_fwd_scan",
            "path_kcache_workspace_bytes", "path_kcache_from_prefill",
            "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
-           "path_decode_step_gated")
+           "path_decode_step_gated", "path_transition_prep")
 
 
 class PathError(RuntimeError):
@@ -77,6 +77,8 @@ def load_library(path: str = LIB_PATH):
     lib.path_fcache_from_prefill.argtypes = [P, P, I, I, I, I, P]
     lib.path_decode_step_gated.restype = I
     lib.path_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.path_transition_prep.restype = I
+    lib.path_transition_prep.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     _lib = lib
     return lib
 
@@ -217,6 +219,21 @@ def path_decode_step_gated(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t
     _check(st, "path_decode_step_gated")
 
 
+def path_transition_prep(x, w_down, w_up, conv, u, b, w, beta, stream=None):
+    """x [B,L,Dm]; w_down [r,Dm]; w_up [H*d,r]; conv [H*d,3] float32; u [H,Dm];
+    b [H] float32 -> w [B,H,L,d] (written), beta [B,H,L] float32 (written)."""
+    lib = load_library()
+    _require_cuda(x, w_down, w_up, conv, u, b, w, beta)
+    B, L, Dm = x.shape
+    r = w_down.shape[0]
+    H = u.shape[0]
+    d = w.shape[-1]
+    st = lib.path_transition_prep(_p(x), _p(w_down), _p(w_up), _p(conv), _p(u), _p(b),
+                                  _p(w), _p(beta), B, L, Dm, r, H, d, _dt(x),
+                                  _stream(stream))
+    _check(st, "path_transition_prep")
+
+
 # ---------------------------------------------------------------------------
 # conveniences (allocate with torch, then call the C ABI)
 # ---------------------------------------------------------------------------
@@ -265,3 +282,14 @@ def decode_workspace(B, H, T_max, d, dtype, device):
     if n == 0:
         raise PathError(-2, "path_decode_workspace_bytes")
     return _workspace(n, device)
+
+
+def transition_prep(x, w_down, w_up, conv, u, b, d, stream=None):
+    """Transition parameters (w, beta) of every token; returns
+    w [B,H,L,d] in x's dtype and beta [B,H,L] float32."""
+    B, L, _ = x.shape
+    H = u.shape[0]
+    w = torch.empty(B, H, L, d, dtype=x.dtype, device=x.device)
+    beta = torch.empty(B, H, L, dtype=torch.float32, device=x.device)
+    path_transition_prep(x, w_down, w_up, conv, u, b, w, beta, stream)
+    return w, beta

@@ -167,6 +167,18 @@ struct FcacheArgs {
     int BH, L, T_max;
 };
 
+struct TransArgs {
+    const void* x;         // [B][L][Dm] bf16
+    const void* w_down;    // [R][Dm] bf16
+    const void* w_up;      // [H*D][R] bf16
+    const float* conv;     // [H*D][3]
+    const void* u;         // [H][Dm] bf16
+    const float* b;        // [H]
+    void* w;               // [B][H][L][D] bf16
+    float* beta;           // [B][H][L]
+    int B, L, Dm, R, H, D, ntile;   // ntile: token tiles per sequence (set by the launcher)
+};
+
 // Decode splits are multiples of this many keys, so a head has at most
 // ceil(T_max / kDecodeSplitQuantum) splits (the workspace holds that many).
 constexpr int kDecodeSplitQuantum = 64;
@@ -179,5 +191,6 @@ hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s);
 hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s);
 hipError_t launch_path_fcache(const FcacheArgs& a, hipStream_t s);
+hipError_t launch_path_transition(TransArgs a, hipStream_t s);
 
 }  // namespace path

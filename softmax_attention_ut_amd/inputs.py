@@ -125,3 +125,61 @@ def generate_config(cfg: PathConfig, *, B=None, H=None) -> PathInputs:
     return generate(B or cfg.B, H or cfg.H, cfg.L_total, cfg.d,
                     dtype=cfg.dtype, gate=cfg.gate, seed=cfg.seed,
                     clip_beta=cfg.clip_beta)
+
+
+# ---------------------------------------------------------------------------
+# Transition-parameter inputs: the layer input x and the weights of the
+# low-rank map, the short convolution and the beta projection.
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class TransitionConfig:
+    name: str
+    B: int
+    L: int
+    Dm: int             # layer width
+    r: int              # rank of the low-rank map
+    H: int
+    d: int
+    seed: int
+
+
+# The ~760M layer shape (width 1536 = 24 heads x 64) at 4K tokens; the rank
+# of the low-rank map is not given on the pages, 64 is taken here.
+TRANSITION_CONFIGS = {
+    "transition_L4k": TransitionConfig("transition_L4k", 8, 4096, 1536, 64, 24, 64, 6),
+}
+
+
+@dataclasses.dataclass
+class TransitionInputs:
+    """CPU tensors: x [B,L,Dm], w_down [r,Dm], w_up [H*d,r], u [H,Dm] in bf16;
+    conv [H*d,3] and b [H] float32."""
+    x: torch.Tensor
+    w_down: torch.Tensor
+    w_up: torch.Tensor
+    conv: torch.Tensor
+    u: torch.Tensor
+    b: torch.Tensor
+
+
+def generate_transition(B, L, Dm, r, H, d, *, seed=0) -> TransitionInputs:
+    """float64 draws in this order, then rounded: x ~ N(0,1); w_down ~
+    N(0,1)/sqrt(Dm); w_up ~ N(0,1)/sqrt(r); conv ~ N(0,1)/sqrt(3);
+    u ~ N(0,1)/sqrt(Dm); b ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, L, Dm))
+    w_down = rng.standard_normal((r, Dm)) / math.sqrt(Dm)
+    w_up = rng.standard_normal((H * d, r)) / math.sqrt(r)
+    conv = rng.standard_normal((H * d, 3)) / math.sqrt(3.0)
+    u = rng.standard_normal((H, Dm)) / math.sqrt(Dm)
+    b = rng.standard_normal(H)
+
+    def bf(a):
+        return torch.from_numpy(a).to(torch.bfloat16).contiguous()
+
+    def f32(a):
+        return torch.from_numpy(a).to(torch.float32).contiguous()
+
+    return TransitionInputs(x=bf(x), w_down=bf(w_down), w_up=bf(w_up), conv=f32(conv),
+                            u=bf(u), b=f32(b))

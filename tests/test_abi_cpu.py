@@ -116,6 +116,28 @@ def test_kcache_argument_errors_before_launch():
                                         p, ws - 1, None) == -4
 
 
+def test_transition_argument_errors_before_launch():
+    """Every call here is rejected on the host (fake pointers are never
+    dereferenced): null pointers and sizes below 1 are invalid, shapes outside
+    d in {64, 128}, r in {32, 64}, r + H <= 128, Dm % 128 == 0 unsupported."""
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+
+    def call(B=1, L=64, Dm=256, r=64, H=4, d=64, dt=pa.PATH_BF16, x=p, conv=p):
+        return lib.path_transition_prep(x, p, p, conv, p, p, p, p, B, L, Dm, r, H, d, dt, None)
+
+    assert call(x=None) == -1
+    assert call(conv=None) == -1
+    assert call(B=0) == -1
+    assert call(L=0) == -1
+    assert call(dt=5) == -1
+    assert call(dt=pa.PATH_F32) == -2
+    assert call(d=32) == -2
+    assert call(r=48) == -2
+    assert call(r=64, H=65) == -2          # r + H > 128
+    assert call(Dm=200) == -2              # not a multiple of 128
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         pa._lib_backup = pa._lib
