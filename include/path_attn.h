@@ -208,6 +208,52 @@ int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache,
                            void* stream);
 
 /*
+ * Paged key/value cache.  With the keys updated in place, decoding is plain
+ * softmax decoding over one cache, so paged caches and split-sequence
+ * decoding apply unchanged (Chinese notes, inference paragraph; Dutch
+ * summary section 3, "Inferentie").  The cache is a pool of pages instead of
+ * one [B][H][T_max][d] array:
+ *
+ *   k_pool, v_pool  [num_blocks][H][page][d] dtype: page p holds `page`
+ *                   consecutive slots of every head of one sequence.
+ *   block_table     [B][max_blocks] int32 (device): slot j of sequence b is
+ *                   slot j % page of page block_table[b][j / page].
+ *   page            a positive multiple of 64; the capacity of a sequence is
+ *                   max_blocks * page slots.
+ * The caller owns the pool and the table and keeps the table's entries for
+ * every slot a call touches within [0, num_blocks).  A page number outside
+ * that range is never dereferenced: its slots are left out (no fault, but
+ * the result is then not the attention defined above).
+ *
+ * path_kcache_from_prefill_paged is path_kcache_from_prefill writing the
+ * transformed keys and the values through the table (slots [0, L); L <=
+ * max_blocks * page); workspace as path_kcache_workspace_bytes.
+ *
+ * path_decode_step_paged is path_decode_step (and, with f_cache and log_f_t
+ * both non-NULL, path_decode_step_gated) on a paged cache: the in-place key
+ * update, the append at slot t and the attention go through the table, with
+ * t < max_blocks * page.  f_cache, if given, is contiguous
+ * [B][H][max_blocks * page] float32.  Workspace: path_decode_workspace_bytes
+ * with T_max = max_blocks * page.  The arithmetic and the split of the keys
+ * are those of the contiguous call, so the results are identical to it.
+ * Bad sizes, a null table or only one of f_cache / log_f_t:
+ * PATH_ERR_INVALID; a page that is not a multiple of 64: PATH_ERR_UNSUPPORTED.
+ */
+int path_kcache_from_prefill_paged(const void* k, const void* v, const void* w,
+                                   const float* beta, void* k_pool, void* v_pool,
+                                   const int* block_table, int num_blocks, int max_blocks,
+                                   int page, int B, int H, int L, int d, int dtype,
+                                   void* workspace, size_t ws_bytes, void* stream);
+int path_decode_step_paged(void* k_pool, void* v_pool, const int* block_table,
+                           int num_blocks, int max_blocks, int page,
+                           float* f_cache, const float* log_f_t,
+                           const void* q_t, const void* k_t, const void* v_t,
+                           const void* w_t, const float* beta_t,
+                           void* out_t, float* lse_t,
+                           int B, int H, int t, int d, float scale, int dtype,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Transition parameters of every token from the layer input, the step ahead
  * of the attention (Chinese notes, "key design": w_t from a low-rank linear
  * layer, a short convolution of filter size 3 and an L2 normalisation;

@@ -29,7 +29,8 @@ EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes"
            "path_attn_fwd", "path_attn_fwd_prepare", "path_attn_fwd_scan",
            "path_kcache_workspace_bytes", "path_kcache_from_prefill",
            "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
-           "path_decode_step_gated", "path_transition_prep")
+           "path_decode_step_gated", "path_transition_prep",
+           "path_kcache_from_prefill_paged", "path_decode_step_paged")
 
 
 class PathError(RuntimeError):
@@ -77,6 +78,12 @@ def load_library(path: str = LIB_PATH):
     lib.path_fcache_from_prefill.argtypes = [P, P, I, I, I, I, P]
     lib.path_decode_step_gated.restype = I
     lib.path_decode_step_gated.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.path_kcache_from_prefill_paged.restype = I
+    lib.path_kcache_from_prefill_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                                   P, S, P]
+    lib.path_decode_step_paged.restype = I
+    lib.path_decode_step_paged.argtypes = [P, P, P, I, I, I, P, P, P, P, P, P, P, P, P, I, I, I,
+                                           I, F, I, P, S, P]
     lib.path_transition_prep.restype = I
     lib.path_transition_prep.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     _lib = lib
@@ -217,6 +224,43 @@ def path_decode_step_gated(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t
                                     _p(lse_t), B, H, int(t), T_max, d, float(scale),
                                     _dt(k_cache), _p(workspace), ws_bytes, _stream(stream))
     _check(st, "path_decode_step_gated")
+
+
+def path_kcache_from_prefill_paged(k, v, w, beta, k_pool, v_pool, block_table,
+                                   workspace=None, stream=None):
+    """k,v,w [B,H,L,d]; beta [B,H,L]; k_pool, v_pool [num_blocks,H,page,d];
+    block_table [B,max_blocks] int32."""
+    lib = load_library()
+    _require_cuda(k, v, w, beta, k_pool, v_pool, block_table, workspace)
+    B, H, L, d = k.shape
+    num_blocks, _, page, _ = k_pool.shape
+    max_blocks = block_table.shape[1]
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_kcache_from_prefill_paged(_p(k), _p(v), _p(w), _p(beta), _p(k_pool),
+                                            _p(v_pool), _p(block_table), num_blocks,
+                                            max_blocks, page, B, H, L, d, _dt(k),
+                                            _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_kcache_from_prefill_paged")
+
+
+def path_decode_step_paged(k_pool, v_pool, block_table, q_t, k_t, v_t, w_t, beta_t, out_t,
+                           lse_t, t, scale, f_cache=None, log_f_t=None, workspace=None,
+                           stream=None):
+    """pools [num_blocks,H,page,d]; block_table [B,max_blocks] int32;
+    q_t,k_t,v_t,w_t,out_t [B,H,d]; beta_t, lse_t [B,H]; optional PaTH-FoX gate
+    f_cache [B,H,max_blocks*page] and log_f_t [B,H]."""
+    lib = load_library()
+    _require_cuda(k_pool, v_pool, block_table, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t,
+                  f_cache, log_f_t, workspace)
+    num_blocks, H, page, d = k_pool.shape
+    B, max_blocks = block_table.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_decode_step_paged(_p(k_pool), _p(v_pool), _p(block_table), num_blocks,
+                                    max_blocks, page, _p(f_cache), _p(log_f_t), _p(q_t),
+                                    _p(k_t), _p(v_t), _p(w_t), _p(beta_t), _p(out_t),
+                                    _p(lse_t), B, H, int(t), d, float(scale), _dt(k_pool),
+                                    _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_decode_step_paged")
 
 
 def path_transition_prep(x, w_down, w_up, conv, u, b, w, beta, stream=None):

@@ -162,9 +162,12 @@ size_t path_kcache_workspace_bytes(int B, int H, int L, int d, int dtype) {
     return fwd_plan(B, H, L, d, dtype, chunk, false, true).total;
 }
 
-int path_kcache_from_prefill(const void* k, const void* v, const void* w, const float* beta,
-                             void* k_cache, void* v_cache, int B, int H, int L, int T_max,
-                             int d, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+static int kcache_from_prefill(const void* k, const void* v, const void* w, const float* beta,
+                               void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                               int d, int dtype, void* workspace, size_t ws_bytes, void* stream,
+                               const CacheMap& map) {
     int chunk = kBf16Chunk;
     if (!valid_dtype(dtype)) return PATH_ERR_INVALID;
     if (dtype != PATH_BF16) return PATH_ERR_UNSUPPORTED;
@@ -189,7 +192,43 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w, const 
     c.kt = u.kt; c.w = w; c.zt = u.zt; c.v = v;
     c.k_cache = k_cache; c.v_cache = v_cache;
     c.BH = BH; c.L = L; c.N = N; c.T_max = T_max;
+    c.map = map;
     return launch_path_kcache(c, d, s) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
+// 0 = ok: a page pool of num_blocks pages of `page` slots (a multiple of
+// 64), each sequence's pages listed in block_table [B][max_blocks]
+static int check_pages(const int* block_table, int num_blocks, int max_blocks, int page,
+                       int B, int H, CacheMap& map) {
+    if (!block_table || num_blocks < 1 || max_blocks < 1 || page < 1) return PATH_ERR_INVALID;
+    if (page % 64 != 0) return PATH_ERR_UNSUPPORTED;
+    if ((long long)max_blocks * page >= (1LL << 31)) return PATH_ERR_UNSUPPORTED;
+    if ((long long)num_blocks * H * page >= (1LL << 40)) return PATH_ERR_UNSUPPORTED;
+    map = CacheMap{block_table, page, max_blocks, num_blocks, H, max_blocks * page};
+    (void)B;
+    return PATH_OK;
+}
+
+extern "C" {
+
+int path_kcache_from_prefill(const void* k, const void* v, const void* w, const float* beta,
+                             void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                             int d, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    const CacheMap map{nullptr, 0, 0, 0, H, T_max};
+    return kcache_from_prefill(k, v, w, beta, k_cache, v_cache, B, H, L, T_max, d, dtype,
+                               workspace, ws_bytes, stream, map);
+}
+
+int path_kcache_from_prefill_paged(const void* k, const void* v, const void* w,
+                                   const float* beta, void* k_pool, void* v_pool,
+                                   const int* block_table, int num_blocks, int max_blocks,
+                                   int page, int B, int H, int L, int d, int dtype,
+                                   void* workspace, size_t ws_bytes, void* stream) {
+    CacheMap map{};
+    const int st = check_pages(block_table, num_blocks, max_blocks, page, B, H, map);
+    if (st != PATH_OK) return st;
+    return kcache_from_prefill(k, v, w, beta, k_pool, v_pool, B, H, L, map.T_max, d, dtype,
+                               workspace, ws_bytes, stream, map);
 }
 
 size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype) {
@@ -202,7 +241,7 @@ static int decode_step(void* k_cache, void* v_cache, float* f_cache, const void*
                        const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
                        const float* log_f_t, void* out_t, float* lse_t, int B, int H, int t,
                        int T_max, int d, float scale, int dtype, void* workspace, size_t ws_bytes,
-                       void* stream) {
+                       void* stream, const CacheMap& map) {
     if (B < 1 || H < 1 || T_max < 1 || t < 0 || t >= T_max || !valid_dtype(dtype))
         return PATH_ERR_INVALID;
     if (dtype != PATH_BF16 || (d != 64 && d != 128)) return PATH_ERR_UNSUPPORTED;
@@ -219,6 +258,7 @@ static int decode_step(void* k_cache, void* v_cache, float* f_cache, const void*
     a.BH = B * H; a.t = t; a.T_max = T_max;
     a.scale2 = scale * kLog2e;
     a.log_f = log_f_t; a.f_cache = f_cache;
+    a.map = map;
     return launch_path_decode(a, d, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PATH_OK : PATH_ERR_HIP;
 }
@@ -227,8 +267,9 @@ int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* 
                      const void* v_t, const void* w_t, const float* beta_t, void* out_t,
                      float* lse_t, int B, int H, int t, int T_max, int d, float scale,
                      int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    const CacheMap map{nullptr, 0, 0, 0, H, T_max};
     return decode_step(k_cache, v_cache, nullptr, q_t, k_t, v_t, w_t, beta_t, nullptr, out_t, lse_t,
-                       B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream);
+                       B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream, map);
 }
 
 int path_fcache_from_prefill(const float* log_f, float* f_cache, int B, int H, int L, int T_max,
@@ -247,8 +288,25 @@ int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache, const v
                            int B, int H, int t, int T_max, int d, float scale, int dtype,
                            void* workspace, size_t ws_bytes, void* stream) {
     if (!f_cache || !log_f_t) return PATH_ERR_INVALID;
+    const CacheMap map{nullptr, 0, 0, 0, H, T_max};
     return decode_step(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t,
-                       lse_t, B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream);
+                       lse_t, B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream, map);
+}
+
+int path_decode_step_paged(void* k_pool, void* v_pool, const int* block_table, int num_blocks,
+                           int max_blocks, int page, float* f_cache, const float* log_f_t,
+                           const void* q_t, const void* k_t, const void* v_t, const void* w_t,
+                           const float* beta_t, void* out_t, float* lse_t, int B, int H, int t,
+                           int d, float scale, int dtype, void* workspace, size_t ws_bytes,
+                           void* stream) {
+    if ((f_cache == nullptr) != (log_f_t == nullptr)) return PATH_ERR_INVALID;
+    if (B < 1 || H < 1) return PATH_ERR_INVALID;
+    CacheMap map{};
+    const int st = check_pages(block_table, num_blocks, max_blocks, page, B, H, map);
+    if (st != PATH_OK) return st;
+    return decode_step(k_pool, v_pool, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t,
+                       lse_t, B, H, t, map.T_max, d, scale, dtype, workspace, ws_bytes, stream,
+                       map);
 }
 
 }  // extern "C"

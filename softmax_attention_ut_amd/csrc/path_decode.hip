@@ -19,7 +19,7 @@
 
 namespace path {
 
-template <int D, bool GATE>
+template <int D, bool GATE, bool PAGED>
 __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs a) {
     constexpr int G = D / 8;              // lanes per key
     constexpr int KPW = 64 / G;           // keys per wave pass
@@ -37,8 +37,12 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
     const bf16* wh = static_cast<const bf16*>(a.w) + (size_t)head * D;
     const bf16* kh = static_cast<const bf16*>(a.k) + (size_t)head * D;
     const bf16* vh = static_cast<const bf16*>(a.v) + (size_t)head * D;
-    bf16* kc = static_cast<bf16*>(a.k_cache) + (size_t)head * a.T_max * D;
-    bf16* vc = static_cast<bf16*>(a.v_cache) + (size_t)head * a.T_max * D;
+    // contiguous: rows head * T_max + j.  Paged: a pass of 2 KPB keys never
+    // crosses a 64-key boundary and pages are multiples of 64 keys, so the
+    // whole pass is in one page, looked up once per pass (a uniform load).
+    bf16* const kbase = static_cast<bf16*>(a.k_cache);
+    bf16* const vbase = static_cast<bf16*>(a.v_cache);
+    long long rb = (long long)head * a.T_max;     // cache row of slot j: rb + j
     const float beta = a.beta[head];
     // forget gate (PaTH-FoX): the logit of key j gains F_t - F_j (natural
     // log, F = inclusive prefix sum of log f), taken to log2 units.  F_t is
@@ -71,6 +75,12 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
     // first), their loads issued together so that each wave has two lines
     // of K and of V in flight.
     for (int jb = j0; jb < j1; jb += 2 * KPB) {
+        if (PAGED) {
+            // rows of this pass: (page * H + h) * P + (j % P) = r + (j - jb)
+            const long long r = cache_row(a.map, head, jb);
+            if (r < 0) continue;          // a page outside the pool: left out
+            rb = r - jb;
+        }
         int jj[2];
         bool ok[2];
         bf16x8 k8[2], v8[2];
@@ -81,9 +91,9 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
             ok[h] = jj[h] < j1;
             k8[h] = v8[h] = bf16x8{};
             if (ok[h]) {
-                k8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl)
+                k8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(kbase + (rb + jj[h]) * D + 8 * gl)
                                     : *reinterpret_cast<const bf16x8*>(kh + 8 * gl);
-                v8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl)
+                v8[h] = (jj[h] < t) ? *reinterpret_cast<const bf16x8*>(vbase + (rb + jj[h]) * D + 8 * gl)
                                     : *reinterpret_cast<const bf16x8*>(vh + 8 * gl);
                 if (GATE) fj[h] = (jj[h] < t) ? fc[jj[h]] : f_t;
             }
@@ -117,11 +127,11 @@ __global__ __launch_bounds__(256) void path_decode_split_kernel(const DecodeArgs
                 bf16x8 k8n;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) k8n[e] = static_cast<bf16>(static_cast<float>(k8[h][e]) - ba * wf[e]);
-                *reinterpret_cast<bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl) = k8n;
+                *reinterpret_cast<bf16x8*>(kbase + (rb + jj[h]) * D + 8 * gl) = k8n;
                 s[h] = (pq[h] - ba * qw) * a.scale2;
             } else {   // j == t: the new key and value enter unchanged
-                *reinterpret_cast<bf16x8*>(kc + (size_t)jj[h] * D + 8 * gl) = k8[h];
-                *reinterpret_cast<bf16x8*>(vc + (size_t)jj[h] * D + 8 * gl) = v8[h];
+                *reinterpret_cast<bf16x8*>(kbase + (rb + jj[h]) * D + 8 * gl) = k8[h];
+                *reinterpret_cast<bf16x8*>(vbase + (rb + jj[h]) * D + 8 * gl) = v8[h];
                 s[h] = pq[h] * a.scale2;
             }
             if (GATE) s[h] += (f_t - fj[h]) * kLog2e;
@@ -217,8 +227,8 @@ static hipError_t resident_split_blocks(int D, int& n) {
     }
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<64, true>, 256, 0)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128, true>, 256, 0);
+    e = D == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<64, true, true>, 256, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128, true, true>, 256, 0);
     if (e != hipSuccess) return e;
     n = ncu * (per_cu > 0 ? per_cu : 1);
     if (slot) *slot = n;
@@ -242,16 +252,18 @@ hipError_t launch_path_decode(const DecodeArgs& args, int D, hipStream_t s) {
     a.keys_per_split = kps;
     a.nsplit = (nkeys + kps - 1) / kps;
     const dim3 grid(a.nsplit, a.BH), block(256);
-    const bool gate = a.f_cache != nullptr;
+    const bool gate = a.f_cache != nullptr, paged = a.map.table != nullptr;
+#define PATH_SPLIT(DD, GG, PP) hipLaunchKernelGGL((path_decode_split_kernel<DD, GG, PP>), grid, block, 0, s, a)
     if (D == 64) {
-        if (gate) hipLaunchKernelGGL((path_decode_split_kernel<64, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_decode_split_kernel<64, false>), grid, block, 0, s, a);
+        if (paged) { if (gate) PATH_SPLIT(64, true, true); else PATH_SPLIT(64, false, true); }
+        else { if (gate) PATH_SPLIT(64, true, false); else PATH_SPLIT(64, false, false); }
         hipLaunchKernelGGL(path_decode_combine_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
     } else {
-        if (gate) hipLaunchKernelGGL((path_decode_split_kernel<128, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_decode_split_kernel<128, false>), grid, block, 0, s, a);
+        if (paged) { if (gate) PATH_SPLIT(128, true, true); else PATH_SPLIT(128, false, true); }
+        else { if (gate) PATH_SPLIT(128, true, false); else PATH_SPLIT(128, false, false); }
         hipLaunchKernelGGL(path_decode_combine_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
     }
+#undef PATH_SPLIT
     return hipGetLastError();
 }
 

@@ -134,14 +134,32 @@ struct FwdArgs {
     float scale2;          // scale * log2(e)
 };
 
+// Where cache slot j of head bh = b * H + h lives, in rows of D elements:
+// contiguous caches [BH][T_max][D] when `table` is null, else a page pool
+// [num_blocks][H][page][D] with page `table[b * max_blocks + j / page]`.
+// Pages outside [0, num_blocks) are never dereferenced (row < 0).
+struct CacheMap {
+    const int* table;      // [B][max_blocks] or null
+    int page, max_blocks, num_blocks, H, T_max;
+};
+
+__device__ __forceinline__ long long cache_row(const CacheMap& c, int bh, int j) {
+    if (!c.table) return (long long)bh * c.T_max + j;
+    const int b = bh / c.H, h = bh - b * c.H;
+    const int blk = c.table[(size_t)b * c.max_blocks + j / c.page];
+    if (blk < 0 || blk >= c.num_blocks) return -1;
+    return ((long long)blk * c.H + h) * c.page + (j % c.page);
+}
+
 struct KcacheArgs {
     const void* kt;        // keys carried to their chunk end (bf16, d permuted)
     const void* w;         // input w [BH][L][D]
     const void* zt;
     const void* v;         // input values [BH][L][D]
-    void* k_cache;         // [BH][T_max][D]
+    void* k_cache;         // contiguous [BH][T_max][D] or a page pool (see map)
     void* v_cache;
     int BH, L, N, T_max;
+    CacheMap map;
 };
 
 struct DecodeArgs {
@@ -159,6 +177,7 @@ struct DecodeArgs {
     float scale2;
     const float* log_f;    // [BH] log f_t, or null (no forget gate)
     float* f_cache;        // [BH][T_max] prefix sums of log f, or null (no forget gate)
+    CacheMap map;          // K/V slot addresses (contiguous or paged)
 };
 
 struct FcacheArgs {

@@ -131,13 +131,15 @@ __global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
     if (!active || j >= L) return;
     // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t (the d rows
     // of -Z^T are stored permuted for this)
-    bf16* kout = static_cast<bf16*>(a.k_cache) + ((size_t)head * a.T_max + j) * D;
+    const long long row = cache_row(a.map, head, j);
+    if (row < 0) return;
+    bf16* kout = static_cast<bf16*>(a.k_cache) + row * D;
 #pragma unroll
     for (int ks = 0; ks < KSD; ++ks)
         *reinterpret_cast<bf16x8*>(kout + 16 * ks + 8 * hh) = pack8k(kacc[ks >> 1], ks & 1);
     // values are copied unchanged, 4 bf16 per lane half
     const bf16* vin = static_cast<const bf16*>(a.v) + ((size_t)head * L + j) * D;
-    bf16* vout = static_cast<bf16*>(a.v_cache) + ((size_t)head * a.T_max + j) * D;
+    bf16* vout = static_cast<bf16*>(a.v_cache) + row * D;
 #pragma unroll
     for (int e = 4 * hh; e < D; e += 8)
         *reinterpret_cast<bf16x4*>(vout + e) = *reinterpret_cast<const bf16x4*>(vin + e);

@@ -138,6 +138,39 @@ def test_transition_argument_errors_before_launch():
     assert call(Dm=200) == -2              # not a multiple of 128
 
 
+def test_paged_argument_errors_before_launch():
+    """Paged decode and prefill hand-off: a null table, bad page counts, a page
+    that is not a multiple of 64, t beyond the capacity and a half-given gate
+    are rejected on the host (fake pointers are never dereferenced)."""
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = lib.path_decode_workspace_bytes(1, 1, 256, 64, pa.PATH_BF16)
+
+    def dec(table=p, nb=4, mb=4, page=64, fc=None, lf=None, t=10, d=64, wsb=ws):
+        return lib.path_decode_step_paged(p, p, table, nb, mb, page, fc, lf, p, p, p, p, p, p,
+                                          None, 1, 1, t, d, 0.1, pa.PATH_BF16, p, wsb, None)
+
+    assert dec(table=None) == -1
+    assert dec(nb=0) == -1
+    assert dec(mb=0) == -1
+    assert dec(page=0) == -1
+    assert dec(page=48) == -2
+    assert dec(t=256) == -1                 # capacity is max_blocks * page = 256
+    assert dec(fc=p) == -1                  # gate cache without log f
+    assert dec(lf=p) == -1
+    assert dec(d=96) == -2
+    assert dec(wsb=8) == -4
+    kws = lib.path_kcache_workspace_bytes(1, 1, 128, 64, pa.PATH_BF16)
+
+    def pre(table=p, mb=2, page=64, L=128):
+        return lib.path_kcache_from_prefill_paged(p, p, p, p, p, p, table, 4, mb, page, 1, 1, L,
+                                                  64, pa.PATH_BF16, p, kws, None)
+
+    assert pre(table=None) == -1
+    assert pre(page=100) == -2
+    assert pre(mb=1) == -1                  # 128 tokens do not fit one 64-slot page
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         pa._lib_backup = pa._lib
