@@ -172,19 +172,40 @@ def bench_decode(args, cfg, torch, pa, inputs):
     g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
     B, H, L, T, d = cfg.B, cfg.H, cfg.L, cfg.L_total, cfg.d
     pre = lambda t: t[:, :, :L].contiguous()
-    kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
-    fc = pa.fcache_from_prefill(pre(g["log_f"]), T) if cfg.gate else None
+    page = args.page
+    if page:
+        # a pool of pages of `page` slots in a shuffled order (plus spares),
+        # one block table row per sequence
+        max_blocks = (T + page - 1) // page
+        num_blocks = B * max_blocks + 8
+        perm = torch.randperm(num_blocks, generator=torch.Generator().manual_seed(0))
+        table = perm[:B * max_blocks].reshape(B, max_blocks).to(torch.int32).cuda()
+        kc = torch.zeros(num_blocks, H, page, d, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        kws = torch.empty(pa.path_kcache_workspace_bytes(B, H, L, d, pa.PATH_BF16),
+                          dtype=torch.uint8, device="cuda")
+        pa.path_kcache_from_prefill_paged(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]),
+                                          kc, vc, table, kws)
+    else:
+        kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
+    Tcap = max_blocks * page if page else T       # slots the cache holds
+    fc = pa.fcache_from_prefill(pre(g["log_f"]), Tcap) if cfg.gate else None
     names = ("q", "k", "v", "w", "beta") + (("log_f",) if cfg.gate else ())
     steps_in = [{k: g[k][:, :, t].contiguous() for k in names} for t in range(L, T)]
 
     def step(s, t):
-        if cfg.gate:
+        if page:
+            pa.path_decode_step_paged(kc, vc, table, s["q"], s["k"], s["v"], s["w"], s["beta"], o,
+                                      ls, t, cfg.scale, f_cache=fc,
+                                      log_f_t=s["log_f"] if cfg.gate else None, workspace=ws,
+                                      stream=stream)
+        elif cfg.gate:
             pa.path_decode_step_gated(kc, vc, fc, s["q"], s["k"], s["v"], s["w"], s["beta"],
                                       s["log_f"], o, ls, t, cfg.scale, ws, stream)
         else:
             pa.path_decode_step(kc, vc, s["q"], s["k"], s["v"], s["w"], s["beta"], o, ls, t,
                                 cfg.scale, ws, stream)
-    ws = pa.decode_workspace(B, H, T, d, pa.PATH_BF16, kc.device)
+    ws = pa.decode_workspace(B, H, Tcap, d, pa.PATH_BF16, kc.device)
     o = torch.empty(B, H, d, dtype=torch.bfloat16, device="cuda")
     ls = torch.empty(B, H, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -222,13 +243,15 @@ def bench_decode(args, cfg, torch, pa, inputs):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {n} PaTH{'-FoX' if cfg.gate else ''} decode steps after a prefill of "
-                               f"L={L}, B={B} H={H} d={d}, bf16 K/V cache",
+                               f"L={L}, B={B} H={H} d={d}, bf16 K/V cache"
+                               + (f" in pages of {page} slots (shuffled block table)" if page else ""),
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
-        "roofline": {"kernel": f"path_decode_split_kernel<{d}, {'true' if cfg.gate else 'false'}> + combine",
+        "roofline": {"kernel": f"path_decode_split_kernel<{d}, {'true' if cfg.gate else 'false'}, "
+                               f"{'true' if page else 'false'}> + combine",
                      "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS,
                      "traffic": (_traffic("path_decode_d128_L8k.md", "path_decode.hip")
-                                 if cfg.name == "d128_L8k_decode" else None)},
+                                 if cfg.name == "d128_L8k_decode" and not page else None)},
     }
     return res, None
 
@@ -335,6 +358,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="fox_L4k")
     ap.add_argument("--cpu-threads", type=int, default=8)
+    ap.add_argument("--page", type=int, default=0,
+                    help="decode workloads: use a paged K/V cache with pages of this many slots")
     ap.add_argument("--cpu-heads", type=int, default=32,
                     help="heads the oracle baseline runs (the sample it extrapolates from)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
