@@ -1225,6 +1225,10 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     // on XCD b % 8 (workgroups are dealt to the 8 XCDs in turn) and takes
     // only heads h with h % 8 == b % 8, so a head's chunks are shared in one
     // XCD's L2.
+    //
+    // When every query block of the launch fits on the CUs at once
+    // (a.single), each workgroup takes one block instead: a pair would make
+    // the step last a heavy plus a light block while other CUs idle.
     const int G = gridDim.x;
     const int P = (nqb + 1) / 2;                 // pairs per head (an odd nqb leaves one block alone)
     const bool by_xcd = (a.BH % 8) == 0 && (G % 8) == 0;
@@ -1232,12 +1236,21 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const int r = by_xcd ? blockIdx.x / 8 : blockIdx.x;
     const int xcd = by_xcd ? blockIdx.x % 8 : 0;
     const int npairs = (by_xcd ? a.BH / 8 : a.BH) * P;
+    const bool single = a.single != 0;
     for (int t = 0;; ++t) {                      // t-th block of this workgroup: pair r + R (t / 2), heavy half first
-        const int j = r + R * (t >> 1);
-        if (j >= npairs) break;
-        const int i = j / P, pr = j % P;
-        const int qb = (t & 1) ? pr : nqb - 1 - pr;
-        if ((t & 1) && qb == nqb - 1 - pr) continue;   // the lone middle block of an odd nqb
+        int i, qb;
+        if (single) {                            // block r of this workgroup's heads, heaviest first
+            if (t > 0) break;
+            i = r / nqb;
+            qb = nqb - 1 - r % nqb;
+        } else {
+            const int j = r + R * (t >> 1);
+            if (j >= npairs) break;
+            const int pr = j % P;
+            i = j / P;
+            qb = (t & 1) ? pr : nqb - 1 - pr;
+            if ((t & 1) && qb == nqb - 1 - pr) continue;   // the lone middle block of an odd nqb
+        }
         __syncthreads();                         // the previous block's tiles are no longer read
         typedef const __attribute__((address_space(4))) FwdArgs* ArgPtr;
         ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
@@ -1247,17 +1260,22 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     }
 }
 
-hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s) {
+hipError_t launch_path_fwd_bf16(const FwdArgs& args, bool gate, hipStream_t s) {
+    FwdArgs a = args;
     const dim3 grid(a.BH * a.nqb), block(256);
     if (a.D == 64) {
-        // persistent: one workgroup per CU (at most one per pair of query blocks)
+        // persistent: one workgroup per CU (at most one per pair of query
+        // blocks), or one per query block when all of them fit at once
         int dev = 0, ncu = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        const long pairs = (long)a.BH * (((a.N + 3) / 4 + 1) / 2);
-        long g = ncu < pairs ? ncu : pairs;
-        if (g >= 8 && a.BH % 8 == 0) g -= g % 8;
+        const long nqb4 = (a.N + 3) / 4;
+        const long blocks = (long)a.BH * nqb4;
+        const long pairs = (long)a.BH * ((nqb4 + 1) / 2);
+        a.single = blocks <= ncu ? 1 : 0;
+        long g = a.single ? blocks : (ncu < pairs ? ncu : pairs);
+        if (!a.single && g >= 8 && a.BH % 8 == 0) g -= g % 8;
         const dim3 gridp(static_cast<unsigned>(g)), block8(512);
         if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<true>), gridp, block8, 0, s, a);
         else hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<false>), gridp, block8, 0, s, a);

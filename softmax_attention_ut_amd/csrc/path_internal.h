@@ -132,6 +132,7 @@ struct FwdArgs {
     float* lse;
     int BH, L, N, C, D, nqb;
     float scale2;          // scale * log2(e)
+    int single;            // d = 64 scan: one query block per workgroup (set by the launcher)
 };
 
 // Where cache slot j of head bh = b * H + h lives, in rows of D elements:

@@ -140,13 +140,24 @@ def test_bf16_heads_not_multiple_of_8():
 
 
 def test_bf16_odd_query_block_count():
-    """N = 11 chunks: three blocks of four query chunks per head, so one block
-    of each head has no partner of equal and opposite weight."""
+    """N = 11 chunks: three blocks of four query chunks per head (24 blocks,
+    fewer than the CUs: one block per workgroup)."""
     inp = generate(2, 4, 700, 64, dtype="bf16", gate=True, seed=45)
     out, lse = _run_fwd(inp, 0.125)
     ro, rl = _oracle_full(inp, 0.125)
     _check(out, ro, "bf16", "bf16 BH=8 L=700 out")
     _check(lse, rl, "bf16", "bf16 BH=8 L=700 lse")
+
+
+def test_bf16_odd_query_block_count_paired():
+    """N = 11 chunks and B*H = 96: 288 query blocks, more than the CUs, so
+    the blocks are dealt in pairs of equal weight, with the lone middle block
+    of each head (odd block count) dealt on its own."""
+    inp = generate(4, 24, 700, 64, dtype="bf16", gate=True, seed=47)
+    out, lse = _run_fwd(inp, 0.125)
+    ro, rl = _oracle_full(inp, 0.125)
+    _check(out, ro, "bf16", "bf16 BH=96 L=700 out")
+    _check(lse, rl, "bf16", "bf16 BH=96 L=700 lse")
 
 
 def test_bf16_more_block_pairs_than_workgroups():
