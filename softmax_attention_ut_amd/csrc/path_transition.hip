@@ -9,22 +9,25 @@
 // fifth, mostly empty MFMA token tile (the "halo"), so every token's w
 // depends only on its own workgroup.
 //
-// Stage 1 (HBM-bound: every element of x is read once):
+// Stage 1 (every element of x is read once from HBM; every workgroup reads
+// the whole of [W_down; u] from L2, which costs more than the x reads):
 //     [W_down; u] (r + H channels) x x^T on 16x16x32 bf16 MFMA, fp32
 //     accumulators.  x is staged in LDS 128 columns at a time (double
 //     buffered, one barrier per stage) and read as the B operand by all four
-//     waves; wave q computes channel tiles q and q + 4 for all 64 tokens, with
-//     its weight rows read from global memory (they are shared by every
-//     workgroup and stay in L2).  Channels < r are y = W_down x; the rest give
-//     beta.  y goes to LDS as a bf16 (high, low) pair.
-//     x is copied two steps ahead of its use, the weights one step ahead.
+//     waves; wave q computes channel tiles q and q + 4 for all 64 (+2) tokens,
+//     with its weight rows read from global memory.  Channels < r are
+//     y = W_down x; the rest give beta.  y goes to LDS as a bf16 (high, low)
+//     pair.  x is copied two steps ahead of its use, the weights one step
+//     ahead.
 // Stage 2 (per head, one wave per head):
 //     W_up[head] x y^T on MFMA (high and low parts of y), so a lane holds one
-//     token and four consecutive channels.  The convolution along tokens is a
-//     shift across the 16 lanes of a DPP row (the previous token tile supplies
-//     the first lanes), the squared norm is summed over the lane's channels
-//     and across the four lane groups, and the normalised bf16 rows are
-//     staged in LDS and written as whole 16-byte units.
+//     token and four consecutive channels.  The four token tiles interleave
+//     the tokens (tile tt holds tokens 4 j + tt of lane column j), so the
+//     convolution's tokens one and two back are mostly in the same lane; the
+//     rest come through one DPP row shift per four values, with the halo
+//     entering at lane 0.  The squared norm is summed over the lane's
+//     channels and across the four lane groups, and the normalised bf16 rows
+//     are staged in LDS and written as whole 16-byte units.
 #include "path_attn.h"
 #include "path_internal.h"
 
