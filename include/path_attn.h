@@ -24,9 +24,11 @@
  *   - dtype: PATH_F32 (q,k,v,w,out in float32) or PATH_BF16 (bfloat16).
  *     beta, log_f and lse are always float32.
  *   - The caller owns every buffer, including the workspace; the library
- *     allocates nothing and keeps no global state, so calls on different
- *     streams with different workspaces may run concurrently.  Calls that
- *     share a workspace or a cache race unless ordered by the caller.
+ *     allocates nothing and keeps no global state apart from a per-device
+ *     cache of one occupancy query (filled on the first decode call on a
+ *     device, thread-safe), so calls on different streams with different
+ *     workspaces may run concurrently.  Calls that share a workspace or a
+ *     cache race unless ordered by the caller.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream).  Argument checks run on the host before any HIP call;
  *     a negative path_status_t is returned and nothing is launched.  A failed

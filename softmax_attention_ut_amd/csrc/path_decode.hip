@@ -17,6 +17,8 @@
 // lane), so a wave streams 64/G keys per pass with 16-byte accesses.
 #include "path_internal.h"
 
+#include <atomic>
+
 namespace path {
 
 template <int D, bool GATE, bool PAGED>
@@ -214,16 +216,21 @@ __global__ __launch_bounds__(256) void path_decode_combine_kernel(const DecodeAr
 }
 
 // Workgroups of the split kernel that fit on the current device at once
-// (its CU count times the kernel's occupancy), queried once per device and d.
+// (its CU count times the kernel's occupancy), queried once per device and d
+// and kept in a process-wide cache (atomic: concurrent first calls may both
+// query and store the same value).
 static hipError_t resident_split_blocks(int D, int& n) {
-    static int cache[64][2];
+    static std::atomic<int> cache[64][2];
     int dev = 0, ncu = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    int* slot = (dev >= 0 && dev < 64) ? &cache[dev][D == 128] : nullptr;
-    if (slot && *slot > 0) {
-        n = *slot;
-        return hipSuccess;
+    std::atomic<int>* slot = (dev >= 0 && dev < 64) ? &cache[dev][D == 128] : nullptr;
+    if (slot) {
+        const int v = slot->load(std::memory_order_relaxed);
+        if (v > 0) {
+            n = v;
+            return hipSuccess;
+        }
     }
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -231,7 +238,7 @@ static hipError_t resident_split_blocks(int D, int& n) {
                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, path_decode_split_kernel<128, true, true>, 256, 0);
     if (e != hipSuccess) return e;
     n = ncu * (per_cu > 0 ? per_cu : 1);
-    if (slot) *slot = n;
+    if (slot) slot->store(n, std::memory_order_relaxed);
     return hipSuccess;
 }
 
