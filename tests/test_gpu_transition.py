@@ -56,6 +56,7 @@ CASES = [
     (2, 125, 384, 64, 3, 128),
     (1, 190, 128, 32, 6, 128),
     (1, 300, 512, 64, 64, 64),      # r + H = 128
+    (1, 1000, 4096, 64, 32, 128),   # the width of 32 heads of 128 (32 column steps)
 ]
 
 
