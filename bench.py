@@ -136,6 +136,7 @@ def bench_fwd(args, cfg, torch, pa, inputs):
     ms = wall * 1e3 / args.steps
     prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    step_ev = sorted(e[0].elapsed_time(e[2]) for e in evs)
     f = flop_model(B, H, L, d)
     achieved = f["scan"] / (scan_ms * 1e-3) / 1e12
     # the committed counter summary covers the 4k FoX workload only
@@ -156,6 +157,10 @@ def bench_fwd(args, cfg, torch, pa, inputs):
         "tflops_algorithmic": f["alg"] / (ms * 1e-3) / 1e12,
         "mfma_peak_frac_algorithmic": f["alg"] / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "stage_ms": {"prepare(path_ut)": prep_ms, "scan(path_fwd)": scan_ms},
+        # per-step HIP-event times (prepare + scan), inputs resident, L2 not flushed
+        "step_ms_events": {"median": step_ev[len(step_ev) // 2], "min": step_ev[0],
+                           "mean": sum(step_ev) / len(step_ev)},
+        "l2_flushed": False,
         "roofline": {"kernel": (f"path_fwd_bf16_d64pp_kernel<{'true' if cfg.gate else 'false'}>" if d == 64
                                 else f"path_fwd_bf16_kernel<{d},{'true' if cfg.gate else 'false'}>"),
                      "bound": "mfma",
