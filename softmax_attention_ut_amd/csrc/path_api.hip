@@ -199,13 +199,12 @@ static int kcache_from_prefill(const void* k, const void* v, const void* w, cons
 // 0 = ok: a page pool of num_blocks pages of `page` slots (a multiple of
 // 64), each sequence's pages listed in block_table [B][max_blocks]
 static int check_pages(const int* block_table, int num_blocks, int max_blocks, int page,
-                       int B, int H, CacheMap& map) {
+                       int H, CacheMap& map) {
     if (!block_table || num_blocks < 1 || max_blocks < 1 || page < 1) return PATH_ERR_INVALID;
     if (page % 64 != 0) return PATH_ERR_UNSUPPORTED;
     if ((long long)max_blocks * page >= (1LL << 31)) return PATH_ERR_UNSUPPORTED;
     if ((long long)num_blocks * H * page >= (1LL << 40)) return PATH_ERR_UNSUPPORTED;
     map = CacheMap{block_table, page, max_blocks, num_blocks, H, max_blocks * page};
-    (void)B;
     return PATH_OK;
 }
 
@@ -225,7 +224,7 @@ int path_kcache_from_prefill_paged(const void* k, const void* v, const void* w,
                                    int page, int B, int H, int L, int d, int dtype,
                                    void* workspace, size_t ws_bytes, void* stream) {
     CacheMap map{};
-    const int st = check_pages(block_table, num_blocks, max_blocks, page, B, H, map);
+    const int st = check_pages(block_table, num_blocks, max_blocks, page, H, map);
     if (st != PATH_OK) return st;
     return kcache_from_prefill(k, v, w, beta, k_pool, v_pool, B, H, L, map.T_max, d, dtype,
                                workspace, ws_bytes, stream, map);
@@ -302,7 +301,7 @@ int path_decode_step_paged(void* k_pool, void* v_pool, const int* block_table, i
     if ((f_cache == nullptr) != (log_f_t == nullptr)) return PATH_ERR_INVALID;
     if (B < 1 || H < 1) return PATH_ERR_INVALID;
     CacheMap map{};
-    const int st = check_pages(block_table, num_blocks, max_blocks, page, B, H, map);
+    const int st = check_pages(block_table, num_blocks, max_blocks, page, H, map);
     if (st != PATH_OK) return st;
     return decode_step(k_pool, v_pool, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t,
                        lse_t, B, H, t, map.T_max, d, scale, dtype, workspace, ws_bytes, stream,
