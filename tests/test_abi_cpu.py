@@ -4,6 +4,8 @@ any HIP call."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -169,6 +171,42 @@ def test_paged_argument_errors_before_launch():
     assert pre(table=None) == -1
     assert pre(page=100) == -2
     assert pre(mb=1) == -1                  # 128 tokens do not fit one 64-slot page
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "path_attn.h"
+int main(void) {
+    /* host-only calls: no device is touched */
+    if (strstr(path_version(), "gfx950") == NULL) return 1;
+    if (strcmp(path_status_string(PATH_ERR_WORKSPACE), "workspace missing or too small")) return 2;
+    if (path_attn_fwd_workspace_bytes(8, 24, 4096, 64, PATH_BF16, 0) == 0) return 3;
+    if (path_attn_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 1, 64, 64, 0.125f,
+                      PATH_BF16, 0, NULL, 0, NULL) != PATH_ERR_INVALID) return 4;
+    printf("ok\n");
+    return 0;
+}
+"""
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="needs gcc")
+def test_plain_c_client_compiles_links_and_calls(tmp_path):
+    """The boundary is a C ABI: a C99 program compiles against the header
+    alone, links against libpath_attn.so and calls its host queries (no
+    Python, no torch, no device access)."""
+    lib = pa.load_library()
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    libdir = os.path.dirname(pa.LIB_PATH)
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        str(src), "-o", str(exe), "-L", libdir, "-l:libpath_attn.so",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", (out.returncode, out.stdout, out.stderr)
+    assert lib is not None
 
 
 def test_missing_library_fails_loudly(tmp_path):
