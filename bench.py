@@ -359,8 +359,8 @@ def copy_calibration(mib, torch):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fox_L4k")
     ap.add_argument("--cpu-threads", type=int, default=8)
     ap.add_argument("--page", type=int, default=0,
