@@ -14,7 +14,10 @@ Two kinds of functions live here:
   matrices, the UT transform, and the full-matrix form of the logits;
 * the transition parameters w_t, beta_t from the layer input (low-rank map,
   short convolution, L2 normalisation; 2 sigmoid), the reference of the
-  transition-prep kernel.
+  transition-prep kernel;
+* the gradients of the forward (the backward pass used in training), by
+  reverse-mode differentiation of the recurrent form in plain fp64 PyTorch
+  CPU ops.
 
 Every function cites the passage it follows (PaTH paper pages: the Dutch
 technical summary and the Chinese paper notes).  All parts are pinned by
@@ -259,3 +262,56 @@ def transition_prep(x, w_down, w_up, conv, u, b, d):
     logit = x @ u.T + b                                # [B, L, H]
     beta = 2.0 / (1.0 + np.exp(-logit))
     return w, beta.transpose(0, 2, 1)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of the forward)
+# ---------------------------------------------------------------------------
+
+def _forward_torch(q, k, v, w, beta, log_f, scale):
+    """The recurrent in-place key-update form (Dutch summary section 3,
+    "Inferentie"; Chinese notes, inference paragraph) in fp64 torch ops, all
+    heads at once: at step t every cached key is multiplied by H_t, key t is
+    appended, and query t attends over the cache with the optional PaTH-FoX
+    bias F_t - F_j (Chinese notes, PaTH-FoX).  q, k, v, w: [..., L, d];
+    beta, log_f: [..., L].  Returns out [..., L, d]."""
+    import torch
+    L = q.shape[-2]
+    F = None if log_f is None else torch.cumsum(log_f, dim=-1)
+    keys = None
+    outs = []
+    for t in range(L):
+        if keys is None:
+            keys = k[..., :1, :]
+        else:
+            wt = w[..., t, :]                                         # [..., d]
+            proj = (keys * wt[..., None, :]).sum(-1)                  # w_t . k_j, [..., t]
+            keys = keys - beta[..., t, None, None] * proj[..., None] * wt[..., None, :]
+            keys = torch.cat([keys, k[..., t:t + 1, :]], dim=-2)
+        s = scale * (keys * q[..., t, None, :]).sum(-1)               # [..., t + 1]
+        if F is not None:
+            s = s + (F[..., t, None] - F[..., :t + 1])
+        p = torch.softmax(s, dim=-1)
+        outs.append((p[..., None] * v[..., :t + 1, :]).sum(-2))
+    return torch.stack(outs, dim=-2)
+
+
+def backward(q, k, v, w, beta, log_f, scale, d_out):
+    """Gradients of sum(d_out * out) with respect to q, k, v, w, beta and
+    log_f (None without the gate), out being the PaTH(-FoX) forward.  The
+    pages say only that training uses the same blockwise algorithm (English
+    summary; Dutch summary section 3); the backward is read as the exact
+    gradient of the forward.  Reverse-mode differentiation of the recurrent
+    form above, fp64, for small inputs (its graph holds O(L^2 d) values per
+    head).  Returns a dict of fp64 numpy arrays: dq, dk, dv, dw, dbeta and,
+    with the gate, dlog_f."""
+    import torch
+    names = ["q", "k", "v", "w", "beta"] + ([] if log_f is None else ["log_f"])
+    vals = [q, k, v, w, beta] + ([] if log_f is None else [log_f])
+    ts = [torch.tensor(_f64(x), dtype=torch.float64, requires_grad=True) for x in vals]
+    tq, tk, tv, tw, tb = ts[:5]
+    tf = ts[5] if log_f is not None else None
+    out = _forward_torch(tq, tk, tv, tw, tb, tf, float(scale))
+    loss = (out * torch.tensor(_f64(d_out), dtype=torch.float64)).sum()
+    grads = torch.autograd.grad(loss, ts)
+    return {"d" + n: g.numpy() for n, g in zip(names, grads)}

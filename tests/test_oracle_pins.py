@@ -410,3 +410,91 @@ def test_transition_prep_low_rank_invariants():
     for h in range(H):
         e = col[h * d:(h + 1) * d] / np.linalg.norm(col[h * d:(h + 1) * d])
         np.testing.assert_allclose(np.abs(w4[:, h] @ e), 1.0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of the forward)
+# ---------------------------------------------------------------------------
+
+def _bwd_inputs(seed, L, d, gate, BH=1, unit_w=False):
+    q, k, v, w, beta, log_f = _rand(seed, L, d, gate=gate, BH=BH, unit_w=unit_w)
+    d_out = np.random.default_rng(seed + 1000).standard_normal(q.shape)
+    return q, k, v, w, beta, log_f, d_out
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_backward_matches_finite_differences_of_the_c_forward(gate):
+    """Every gradient entry equals the central difference of
+    sum(d_out * out) with out from the C recurrence (pinned above), a forward
+    that shares nothing with the differentiated torch form.  h = 1e-5: the
+    difference error is O(h^2), far below the tolerance."""
+    s, h = 0.7, 1e-5
+    q, k, v, w, beta, log_f, d_out = _bwd_inputs(21, 6, 3, gate)
+    g = oracle.backward(q, k, v, w, beta, log_f, s, d_out)
+    inputs = {"q": q, "k": k, "v": v, "w": w, "beta": beta}
+    if gate:
+        inputs["log_f"] = log_f
+
+    def loss(vals):
+        out, _, _, _ = oracle.recurrent(vals["q"], vals["k"], vals["v"], vals["w"],
+                                        vals["beta"], vals.get("log_f"), s)
+        return float(np.sum(d_out * out))
+
+    for name, arr in inputs.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            for sign in (1.0, -1.0):
+                pert = {n: a.copy() for n, a in inputs.items()}
+                pert[name][idx] += sign * h
+                fd[idx] += sign * loss(pert)
+            fd[idx] /= 2 * h
+        np.testing.assert_allclose(g["d" + name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_backward_dv_is_probabilities_transposed_times_d_out(gate):
+    """out = P V, so dV = P^T dO with P the softmax of the explicit-product
+    logits (brute force, pinned above)."""
+    s = 0.5
+    q, k, v, w, beta, log_f, d_out = _bwd_inputs(22, 9, 4, gate)
+    g = oracle.backward(q, k, v, w, beta, log_f, s, d_out)
+    logits = oracle.bruteforce_logits(q[0], k[0], w[0], beta[0],
+                                      None if log_f is None else log_f[0], s)
+    P = softmax(logits, axis=-1)
+    np.testing.assert_allclose(g["dv"][0], P.T @ d_out[0], atol=1e-12)
+
+
+def test_backward_beta_zero_is_causal_attention_backward():
+    """beta = 0 makes every transition the identity: dq, dk, dv equal the
+    gradients of causal softmax attention (torch SDPA, fp64), and the
+    logits no longer depend on w, so dw = 0."""
+    s = 0.25
+    q, k, v, w, beta, _, d_out = _bwd_inputs(23, 12, 5, False, BH=2)
+    beta = np.zeros_like(beta)
+    g = oracle.backward(q, k, v, w, beta, None, s, d_out)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=s)
+    dq, dk, dv = torch.autograd.grad((out * torch.tensor(d_out)).sum(), (tq, tk, tv))
+    np.testing.assert_allclose(g["dq"], dq.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dk"], dk.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dv"], dv.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dw"], 0.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_backward_transition_scaling_invariance_and_index_base(gate):
+    """H_t = I - beta_t w_t w_t^T is unchanged by w_t -> c w_t, beta_t ->
+    beta_t / c^2, so the derivative in c at c = 1 vanishes:
+    w_t . dw_t = 2 beta_t dbeta_t for every t.  H_0, beta_0 and f_0 never
+    enter a logit (0-based index), so their gradients are zero."""
+    s = 0.6
+    q, k, v, w, beta, log_f, d_out = _bwd_inputs(24, 10, 4, gate, BH=2)
+    g = oracle.backward(q, k, v, w, beta, log_f, s, d_out)
+    lhs = np.sum(w * g["dw"], axis=-1)
+    np.testing.assert_allclose(lhs, 2.0 * beta * g["dbeta"], atol=1e-12)
+    assert np.all(g["dw"][:, 0] == 0.0) and np.all(g["dbeta"][:, 0] == 0.0)
+    if gate:
+        # log f_0 enters every prefix sum F_t and cancels in F_t - F_j, so its
+        # gradient, the sum of the gradients of all F_t, vanishes (up to the
+        # rounding of that cancellation)
+        np.testing.assert_allclose(g["dlog_f"][:, 0], 0.0, atol=1e-12)
