@@ -249,6 +249,21 @@ def test_d128_prefill_kcache_and_decode():
     _decode_and_check(inp, cfg.scale, L, T, heads, key_samples=64)
 
 
+def test_fox_d128_prefill_kcache_and_gated_decode():
+    """The PaTH-FoX variant of the d=128 workload (B=2, H=32, L=8192 + 256
+    steps, forget gate): the gated prefill (sampled rows), the key cache, the
+    gate cache and 256 gated decode steps (sampled heads) against the oracle."""
+    cfg = CONFIGS["fox_d128_L8k_decode"]
+    inp = generate_config(cfg)
+    L, T = cfg.L, cfg.L_total
+    out, lse = _run_fwd(inp, cfg.scale, L=L)
+    BH = cfg.B * cfg.H
+    heads = [0, 33, BH - 1]
+    _check_sampled(cfg, inp, out, lse, heads, L)
+    del out, lse
+    _decode_and_check(inp, cfg.scale, L, T, heads, key_samples=64)
+
+
 def _decode_and_check(inp, scale, L, T, heads, key_samples):
     g = _dev(inp)
     B, H, _, d = inp.q.shape
