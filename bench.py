@@ -226,16 +226,44 @@ def bench_decode(args, cfg, torch, pa, inputs):
     if cfg.gate:
         fc.copy_(fc0)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(n):
-        step(steps_in[i], L + i)
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / n
-    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    if args.graph:
+        # the n steps captured once in a HIP graph, then replayed from the
+        # restored caches: one launch for the whole run
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        outer = stream
+        stream = side
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for i in range(n):
+                    step(steps_in[i], L + i)
+        stream = outer
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        if cfg.gate:
+            fc.copy_(fc0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = wall * 1e3 / n
+        step_ms = [e0.elapsed_time(e1) / n] * n
+    else:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(n):
+            step(steps_in[i], L + i)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = wall * 1e3 / n
+        step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
     # per key: read k, write k, read v (bf16), and with the gate read F_j (fp32)
     per_key = d * 2 * 3 + (4 if cfg.gate else 0)
     bytes_total = sum(B * H * ((L + i) * per_key + 4 * d * 2) for i in range(n))
@@ -249,7 +277,8 @@ def bench_decode(args, cfg, torch, pa, inputs):
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {n} PaTH{'-FoX' if cfg.gate else ''} decode steps after a prefill of "
                                f"L={L}, B={B} H={H} d={d}, bf16 K/V cache"
-                               + (f" in pages of {page} slots (shuffled block table)" if page else ""),
+                               + (f" in pages of {page} slots (shuffled block table)" if page else "")
+                               + (", replayed from one HIP graph" if args.graph else ""),
                    "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
         "roofline": {"kernel": f"path_decode_split_kernel<{d}, {'true' if cfg.gate else 'false'}, "
                                f"{'true' if page else 'false'}> + combine",
@@ -363,6 +392,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fox_L4k")
     ap.add_argument("--cpu-threads", type=int, default=8)
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: capture the timed steps in one HIP graph and replay it")
     ap.add_argument("--page", type=int, default=0,
                     help="decode workloads: use a paged K/V cache with pages of this many slots")
     ap.add_argument("--cpu-heads", type=int, default=32,
