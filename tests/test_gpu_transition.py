@@ -92,3 +92,40 @@ def test_transition_full_size():
     w, beta = _run(inp, cfg.d)
     w_ref, beta_ref = _ref(inp, cfg.d)
     _check(w, beta, w_ref, beta_ref, cfg.name)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_transition_then_attention(gate):
+    """The layer's chain: w and beta from path_transition_prep feed
+    path_attn_fwd directly (bf16 w, fp32 beta, the layouts both use).  The
+    oracle runs its own chain from the same layer input and weights:
+    oracle.transition_prep in fp64, w rounded to bf16 (nearest even) and
+    beta to fp32 as the attention's inputs, then the recurrent forward.  The
+    two chains may round a w element differently by an ulp; the outputs are
+    held to the bf16 tolerances."""
+    B, L, Dm, r, H, d = 2, 300, 512, 64, 4, 64
+    inp = generate_transition(B, L, Dm, r, H, d, seed=71)
+    rng = np.random.default_rng(72)
+    shape = (B, H, L, d)
+    q, k, v = (torch.from_numpy(rng.standard_normal(shape)).to(torch.bfloat16) for _ in range(3))
+    log_f = (torch.from_numpy(-np.logaddexp(0.0, -(3.0 + rng.standard_normal((B, H, L)))))
+             .to(torch.float32) if gate else None)
+    gw, gbeta = (t.cuda() for t in _run_gpu_params(inp, d))
+    out, lse = pa.attention(q.cuda(), k.cuda(), v.cuda(), gw, gbeta,
+                            None if log_f is None else log_f.cuda(), scale=d ** -0.5)
+    torch.cuda.synchronize()
+    w_ref, beta_ref = _ref(inp, d)
+    w_in = torch.from_numpy(w_ref).to(torch.bfloat16)
+    beta_in = torch.from_numpy(beta_ref).to(torch.float32)
+    ro, rl, _, _ = oracle.recurrent(q, k, v, w_in, beta_in, log_f, d ** -0.5)
+    err = np.abs(out.double().cpu().numpy() - ro)
+    lerr = np.abs(lse.double().cpu().numpy() - rl)
+    print(f"transition -> attention gate={gate}: out max {err.max():.2e} mean {err.mean():.2e}; "
+          f"lse max {lerr.max():.2e}", flush=True)
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    assert lerr.max() <= 2e-2 and lerr.mean() <= 2e-3
+
+
+def _run_gpu_params(inp, d):
+    g = {k: t.cuda() for k, t in vars(inp).items()}
+    return pa.transition_prep(g["x"], g["w_down"], g["w_up"], g["conv"], g["u"], g["b"], d)
