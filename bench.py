@@ -78,25 +78,55 @@ def _traffic(profile_md, kernel_src):
     return float(m.group(1))
 
 
+def host_cpu():
+    """The host's CPU model, logical CPU count and the CPUs this process may
+    run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def default_cpu_threads():
+    """All the host cores this process is given: OMP_NUM_THREADS when the
+    environment sets it (the share of a shared host), else the affinity set."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(inp, cfg, threads, heads):
     """The fp64 oracle (recurrent form), unmodified, on the first `heads`
-    heads of the same inputs with `threads` threads (about 2-3 s wall for 32
-    heads of the 4k workload on 8 threads); extrapolated to the whole job."""
+    heads of the same inputs with `threads` OpenMP threads, then extrapolated
+    to the whole job by the head count (heads are independent and equal in
+    cost, so the job time is linear in them)."""
     import oracle
-    n = max(threads, min(heads, cfg.B * cfg.H))
+    BH = cfg.B * cfg.H
+    n = max(1, min(heads, BH))
     sl = lambda t: None if t is None else t.reshape(-1, *t.shape[2:])[:n]
     t0 = time.perf_counter()
     _, _, _, used = oracle.recurrent(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.w), sl(inp.beta),
                                      sl(inp.log_f), cfg.scale, nthreads=threads)
     dt = time.perf_counter() - t0
-    BH = cfg.B * cfg.H
     t_full = dt * BH / n
     f = flop_model(cfg.B, cfg.H, cfg.L, cfg.d)
-    return {"value": f["eff"] / t_full / 1e12, "unit": "TFLOP/s (effective)",
-            "cores": used, "kind": "oracle",
-            "tokens_per_s": cfg.B * cfg.L / t_full,
-            "sample": f"{n} of {BH} heads, all {cfg.L} rows, fp64 recurrent oracle, "
-                      f"{dt:.2f} s wall; job time extrapolated x{BH / n:.1f}"}
+    res = {"value": f["eff"] / t_full / 1e12, "unit": "TFLOP/s (effective)",
+           "cores": used, "kind": "oracle",
+           "tokens_per_s": cfg.B * cfg.L / t_full,
+           "extrapolated": n < BH, "extrapolation_factor": BH / n,
+           "sample": f"{n} of {BH} heads, all {cfg.L} rows, fp64 recurrent oracle on {used} "
+                     f"threads, {dt:.2f} s wall" + (f"; whole-job time extrapolated x{BH / n:.1f} "
+                                                    f"by head count" if n < BH else "")}
+    res.update(host_cpu())
+    return res
 
 
 def bench_fwd(args, cfg, torch, pa, inputs):
@@ -391,13 +421,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fox_L4k")
-    ap.add_argument("--cpu-threads", type=int, default=8)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="oracle baseline threads (default: all host cores given to this process)")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: capture the timed steps in one HIP graph and replay it")
     ap.add_argument("--page", type=int, default=0,
                     help="decode workloads: use a paged K/V cache with pages of this many slots")
-    ap.add_argument("--cpu-heads", type=int, default=32,
-                    help="heads the oracle baseline runs (the sample it extrapolates from)")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads the oracle baseline runs, the sample it extrapolates from "
+                         "(default: two per thread, about 10-30 s of CPU work at the 4k workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (traffic-counter calibration)")
@@ -428,7 +460,7 @@ def main():
         cfg = inputs.TRANSITION_CONFIGS[args.workload]
         res, inp = bench_transition(args, cfg, torch, pa, inputs)
         if not args.no_cpu_baseline:
-            res["cpu_baseline"] = transition_cpu_baseline(inp, cfg, max(1, args.cpu_threads))
+            res["cpu_baseline"] = transition_cpu_baseline(inp, cfg, args.cpu_threads or default_cpu_threads())
         print(json.dumps(res), flush=True)
         return
     cfg = inputs.CONFIGS[args.workload]
@@ -437,8 +469,8 @@ def main():
     else:
         res, inp = bench_fwd(args, cfg, torch, pa, inputs)
     if inp is not None and not args.no_cpu_baseline:
-        threads = max(1, min(args.cpu_threads, os.cpu_count() or 1, cfg.B * cfg.H))
-        res["cpu_baseline"] = cpu_baseline(inp, cfg, threads, args.cpu_heads)
+        threads = args.cpu_threads or default_cpu_threads()
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, threads, args.cpu_heads or 2 * threads)
     print(json.dumps(res), flush=True)
 
 

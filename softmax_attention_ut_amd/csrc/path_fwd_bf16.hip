@@ -223,6 +223,14 @@ struct Stage {
     bf16* gb;          // d = 64 with gate: bias k-step A rows [C][16]
 };
 
+// Three-term bf16 split, x = h + m + l to about 24 bits.
+__device__ __forceinline__ void split3(float x, bf16& h, bf16& m, bf16& l) {
+    h = static_cast<bf16>(x);
+    const float r = x - static_cast<float>(h);
+    m = static_cast<bf16>(r);
+    l = static_cast<bf16>(r - static_cast<float>(m));
+}
+
 // One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
 template <int D, bool GATE, bool DIAG>
 __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>& sg,
@@ -233,7 +241,9 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
 
     // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys).  With the forget
     // gate, one more k-step adds -loc_j / c2 to every logit of key j (the key
-    // part of the bias, split into two bf16 terms), so that c2 * S holds
+    // part of the bias, split into three bf16 terms: a gate that cuts the past
+    // makes loc_j of order 1e4, and the cancellation against the query's part
+    // must keep fp32 precision), so that c2 * S holds
     // scale*log2(e)*(k~_j . q) + log2 prod f over the key's chunk tail.
     f32x16 s[2], x[2];
 #pragma unroll
@@ -247,16 +257,17 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
         if (GATE) {
-            const float g = -sg.loc[32 * kt2 + l32] * (1.f / c2);
-            const bf16 gh = static_cast<bf16>(g);
-            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
+            bf16 gh, gm, gl;
+            split3(-sg.loc[32 * kt2 + l32] * (1.f / c2), gh, gm, gl);
             bf16x8 ag = {};
             bf16x8 ones = {};
             if (hh == 0) {
                 ag[0] = gh;
-                ag[1] = gl;
+                ag[1] = gm;
+                ag[2] = gl;
                 ones[0] = static_cast<bf16>(1.f);
                 ones[1] = static_cast<bf16>(1.f);
+                ones[2] = static_cast<bf16>(1.f);
             }
             s[kt2] = mfma32(ag, ones, s[kt2]);
         }
@@ -351,14 +362,6 @@ __device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
     }
-}
-
-// Three-term bf16 split, x = h + m + l to about 24 bits.
-__device__ __forceinline__ void split3(float x, bf16& h, bf16& m, bf16& l) {
-    h = static_cast<bf16>(x);
-    const float r = x - static_cast<float>(h);
-    m = static_cast<bf16>(r);
-    l = static_cast<bf16>(r - static_cast<float>(m));
 }
 
 // x with every 32-bit lane word ANDed with msk (0 or ~0)
@@ -814,7 +817,7 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
 // Products: the rank-C form of the diagonal step (Chinese notes, training
 // strategy: full-matrix form), in the transposed orientation, with the query
 // not yet scaled by c2:
-//     X^T = W Q^T,  S^T = K~ Q^T + g (g_j = -loc_j / c2, two bf16 terms)
+//     X^T = W Q^T,  S^T = K~ Q^T + g (g_j = -loc_j / c2, three bf16 terms)
 //     S^T += Y^T strictUpper(X)^T          (keys m > i of the query's row i)
 //     Q^T += (-U^T) lower(X)^T             (the query carried to its chunk start)
 template <bool GATE>
@@ -865,21 +868,22 @@ __device__ __forceinline__ void diag64_products(WaveState<64, GATE>& st, f32x16 
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
-    if (GATE) {
+    if (GATE) {   // the key's gate term -loc_j / c2 as three bf16 terms
         bf16x8 ones = {};
         if (hh == 0) {
             ones[0] = static_cast<bf16>(1.f);
             ones[1] = static_cast<bf16>(1.f);
+            ones[2] = static_cast<bf16>(1.f);
         }
 #pragma unroll
         for (int kt2 = 0; kt2 < 2; ++kt2) {
-            const float g = -gl8[kt2] * (1.f / c2);
-            const bf16 gh = static_cast<bf16>(g);
-            const bf16 gl = static_cast<bf16>(g - static_cast<float>(gh));
+            bf16 gh, gm, gl;
+            split3(-gl8[kt2] * (1.f / c2), gh, gm, gl);
             bf16x8 ag = {};
             if (hh == 0) {
                 ag[0] = gh;
-                ag[1] = gl;
+                ag[1] = gm;
+                ag[2] = gl;
             }
             s[kt2] = mfma32(ag, ones, s[kt2]);
         }

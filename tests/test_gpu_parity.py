@@ -5,6 +5,7 @@ mean-abs <= 2e-3 on the outputs (lse is held to the same bounds).  Inputs
 come from the seeded generator; the oracle sees exactly the rounded tensors
 the GPU receives.
 """
+import concurrent.futures
 import math
 
 import numpy as np
@@ -41,18 +42,29 @@ def _oracle_full(inp, scale, L=None):
     return out, lse
 
 
-def _check_cache(got, ref, n_roundings, what):
-    """Cached keys are stored in bf16 and re-rounded (round-to-nearest-even,
-    relative error <= 2^-9 per element) every time they are carried or
-    updated, so their error grows like sqrt(n_roundings) * 2^-9 in relative
-    norm; the bound below is twice 2^-8 * sqrt(n + 1) per key.  (The outputs
-    computed from the cache are held to the bf16 output tolerances.)"""
-    rel = np.linalg.norm(got - ref, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
-    bound = 2.0 * 2.0 ** -8 * math.sqrt(n_roundings + 1)
-    print(f"{what}: max rel-norm {rel.max():.3e} mean {rel.mean():.3e} (bound {bound:.3e})",
-          flush=True)
+def _check_cache(got, ref, k_in, what, n_roundings):
+    """Cached (bf16) keys against the oracle's fp64 transported keys, per key,
+    as the error norm over the norm of the key as it entered (k_in).  No
+    transition increases a norm (the eigenvalues of I - beta w w^T are 1 and
+    1 - beta, in [-1, 1] for beta in [0, 2]), so every intermediate value of a
+    key, and of any product applied to it, is bounded by its input norm, and
+    each bf16 rounding on its path adds at most 2^-9 of that.  Such errors add
+    up like a random walk: the bound is 2^-8 * sqrt(n + 1) for n roundings,
+    twice the walk's size.  A key's logit error is scale * |q| times this
+    error, so the bound is what the outputs' tolerance can absorb; the outputs
+    computed from the cache are checked against the oracle separately.  The
+    error relative to the key's current norm is printed too: keys carried
+    through thousands of transitions shrink by orders of magnitude, and the
+    same absolute error is then a large relative one."""
+    err = np.linalg.norm(got - ref, axis=-1)
+    rel_in = err / np.maximum(np.linalg.norm(k_in, axis=-1), 1e-30)
+    rel_cur = err / np.maximum(np.linalg.norm(ref, axis=-1), 1e-30)
+    bound = 2.0 ** -8 * math.sqrt(n_roundings + 1)
+    print(f"{what}: error / input norm max {rel_in.max():.3e} mean {rel_in.mean():.3e} "
+          f"(bound {bound:.3e}); error / current norm max {rel_cur.max():.3e} "
+          f"median {np.median(rel_cur):.3e}", flush=True)
     assert np.all(np.isfinite(got)), what
-    assert rel.max() <= bound, (what, rel.max(), bound)
+    assert rel_in.max() <= bound, (what, rel_in.max(), bound)
 
 
 def _check(got, ref, dtype, what=""):
@@ -160,23 +172,6 @@ def test_bf16_odd_query_block_count_paired():
     _check(lse, rl, "bf16", "bf16 BH=96 L=700 lse")
 
 
-def test_bf16_more_block_pairs_than_workgroups():
-    """B*H = 9 heads of 16384 tokens: 9 * 32 pairs of query blocks, more than
-    one per CU, dealt without the per-XCD grouping (9 is not a multiple of 8).
-    Sampled rows of the first, a middle and the last head."""
-    L, s = 16384, 0.125
-    inp = generate(1, 9, L, 64, dtype="bf16", gate=True, seed=46)
-    out, lse = _run_fwd(inp, s)
-    rng = np.random.default_rng(146)
-    rows = _sample_rows(L, rng)
-    heads = [0, 4, 8]
-    hi = np.repeat(heads, len(rows))
-    ri = np.tile(rows, len(heads))
-    ro, rl, _, _ = oracle.rows(inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f, s, hi, ri)
-    _check(out.reshape(-1, L, 64)[hi, ri], ro, "bf16", f"BH=9 L=16k sampled out ({len(hi)} rows)")
-    _check(lse.reshape(-1, L)[hi, ri], rl, "bf16", "BH=9 L=16k sampled lse")
-
-
 def test_bf16_beta_zero_is_causal_attention():
     inp = generate(1, 2, 256, 64, dtype="bf16", gate=False, seed=42)
     inp.beta.zero_()
@@ -200,71 +195,84 @@ def test_bf16_first_transition_never_enters():
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations: sampled rows against the per-row oracle
+# full-size configurations: every head and every row against the recurrent
+# oracle (run on a host thread while the GPU works; ctypes releases the GIL)
 # ---------------------------------------------------------------------------
 
-def _sample_rows(L, rng, n_extra=12):
-    base = {0, 1, 63, 64, 65, 127, 128, L // 2, L - 65, L - 64, L - 2, L - 1}
-    base |= set(rng.integers(0, L, n_extra).tolist())
-    return sorted(r for r in base if 0 <= r < L)
+_POOL = concurrent.futures.ThreadPoolExecutor(max_workers=1)
 
 
-def _check_sampled(cfg, inp, out, lse, heads, L):
-    rng = np.random.default_rng(cfg.seed + 100)
-    rows = _sample_rows(L, rng)
-    hi = np.repeat(heads, len(rows))
-    ri = np.tile(rows, len(heads))
-    sl = lambda t: None if t is None else t[:, :, :L]
-    ro, rl, _, _ = oracle.rows(sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.w), sl(inp.beta),
-                               sl(inp.log_f), cfg.scale, hi, ri)
-    d = inp.q.shape[-1]
-    go = out.reshape(-1, L, d)[hi, ri]
-    gl = lse.reshape(-1, L)[hi, ri]
-    _check(go, ro, "bf16", f"{cfg.name} sampled out ({len(hi)} rows)")
-    _check(gl, rl, "bf16", f"{cfg.name} sampled lse")
+def _oracle_bg(inp, scale, Lcache=0):
+    return _POOL.submit(oracle.recurrent, inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f,
+                        scale, Lcache=Lcache)
 
 
 @pytest.mark.parametrize("name", ["fox_L4k", "fox_L16k"])
-def test_full_size_sampled(name):
+def test_full_size_whole_output(name):
+    """The 4k PaTH-FoX workload (B=8, H=24: every head, so every XCD group
+    and every persistent workgroup's pairs) and the 16k one (B=1, H=16), the
+    whole out and lse against the oracle."""
     cfg = CONFIGS[name]
     inp = generate_config(cfg)
+    fut = _oracle_bg(inp, cfg.scale)
     out, lse = _run_fwd(inp, cfg.scale)
-    BH = cfg.B * cfg.H
-    heads = sorted({0, 1, 7, BH // 2, BH - 1})
-    _check_sampled(cfg, inp, out, lse, heads, cfg.L)
+    ro, rl, _, used = fut.result()
+    print(f"{name}: oracle on {used} threads", flush=True)
+    _check(out, ro, "bf16", f"{name} whole out ({out.size} values)")
+    _check(lse, rl, "bf16", f"{name} whole lse")
+
+
+def test_bf16_more_block_pairs_than_workgroups():
+    """B*H = 9 heads of 16384 tokens: 9 * 32 pairs of query blocks, more than
+    one per CU, dealt without the per-XCD grouping (9 is not a multiple of 8).
+    Whole output."""
+    L, s = 16384, 0.125
+    inp = generate(1, 9, L, 64, dtype="bf16", gate=True, seed=46)
+    fut = _oracle_bg(inp, s)
+    out, lse = _run_fwd(inp, s)
+    ro, rl, _, _ = fut.result()
+    _check(out, ro, "bf16", "BH=9 L=16k whole out")
+    _check(lse, rl, "bf16", "BH=9 L=16k whole lse")
+
+
+def _prefill_decode_whole(cfg):
+    """One oracle recurrence over all L + 256 tokens of every head gives the
+    prefill rows, the 256 decode rows and the key cache after the prefill;
+    the GPU runs the prefill forward, the key-cache hand-off and the 256
+    decode steps."""
+    inp = generate_config(cfg)
+    L, T = cfg.L, cfg.L_total
+    fut = _oracle_bg(inp, cfg.scale, Lcache=L)
+    out, lse = _run_fwd(inp, cfg.scale, L=L)
+    dec = _decode_gpu(inp, cfg.scale, L, T)
+    ro, rl, rkc, used = fut.result()
+    BH, d = cfg.B * cfg.H, cfg.d
+    ro, rl = ro.reshape(BH, T, d), rl.reshape(BH, T)
+    print(f"{cfg.name}: oracle on {used} threads", flush=True)
+    _check(out.reshape(BH, L, d), ro[:, :L], "bf16", f"{cfg.name} prefill whole out")
+    _check(lse.reshape(BH, L), rl[:, :L], "bf16", f"{cfg.name} prefill whole lse")
+    del out, lse
+    _check_decode(inp, cfg.scale, L, T, dec, ro[:, L:], rl[:, L:], rkc.reshape(BH, L, d),
+                  key_samples=64)
 
 
 def test_d128_prefill_kcache_and_decode():
-    """The d=128 workload: prefill (sampled rows), the transformed key cache
-    after the prefill (sampled keys) and 256 decode steps (every step, sampled
-    heads), each against the oracle."""
-    cfg = CONFIGS["d128_L8k_decode"]
-    inp = generate_config(cfg)
-    L, T = cfg.L, cfg.L_total
-    out, lse = _run_fwd(inp, cfg.scale, L=L)
-    BH = cfg.B * cfg.H
-    heads = [0, 5, BH - 1]
-    _check_sampled(cfg, inp, out, lse, heads, L)
-    del out, lse
-    _decode_and_check(inp, cfg.scale, L, T, heads, key_samples=64)
+    """The d=128 workload (B=2, H=32, L=8192, then 256 decode steps): the
+    prefill, the whole key cache after it, every decode step of every head."""
+    _prefill_decode_whole(CONFIGS["d128_L8k_decode"])
 
 
 def test_fox_d128_prefill_kcache_and_gated_decode():
-    """The PaTH-FoX variant of the d=128 workload (B=2, H=32, L=8192 + 256
-    steps, forget gate): the gated prefill (sampled rows), the key cache, the
-    gate cache and 256 gated decode steps (sampled heads) against the oracle."""
-    cfg = CONFIGS["fox_d128_L8k_decode"]
-    inp = generate_config(cfg)
-    L, T = cfg.L, cfg.L_total
-    out, lse = _run_fwd(inp, cfg.scale, L=L)
-    BH = cfg.B * cfg.H
-    heads = [0, 33, BH - 1]
-    _check_sampled(cfg, inp, out, lse, heads, L)
-    del out, lse
-    _decode_and_check(inp, cfg.scale, L, T, heads, key_samples=64)
+    """The PaTH-FoX variant of the d=128 workload (forget gate): gated
+    prefill, key cache, gate cache and 256 gated decode steps, whole."""
+    _prefill_decode_whole(CONFIGS["fox_d128_L8k_decode"])
 
 
-def _decode_and_check(inp, scale, L, T, heads, key_samples):
+def _decode_gpu(inp, scale, L, T):
+    """Prefill hand-off (key, value and gate caches) then decode steps
+    t = L .. T-1 on the GPU.  Returns the caches after the hand-off (host
+    copies), the per-step outputs and lse, and the caches after the last
+    step."""
     g = _dev(inp)
     B, H, _, d = inp.q.shape
     gated = inp.log_f is not None
@@ -272,14 +280,8 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
     kc, vc = pa.kcache_from_prefill(pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]), T)
     fc = pa.fcache_from_prefill(pre(g["log_f"]), T) if gated else None
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    keys = sorted(set(rng.integers(0, L, key_samples).tolist()) | {0, L - 1, max(L - 64, 0)})
-    hi = np.repeat(heads, len(keys))
-    ki = np.tile(keys, len(heads))
-    ref_k = oracle.transported_keys(inp.k, inp.w, inp.beta, L - 1, hi, ki)
-    got_k = kc.double().cpu().numpy().reshape(B * H, T, d)[hi, ki]
-    n_chunks = (L + 63) // 64
-    _check_cache(got_k, ref_k, n_chunks + 2, "kcache after prefill")
+    kc_pre = kc.double().cpu().numpy().reshape(B * H, T, d)[:, :L]
+    vc_pre = vc.double().cpu().numpy().reshape(B * H, T, d)[:, :L]
     ws = pa.decode_workspace(B, H, T, d, pa.PATH_BF16, kc.device)
     outs, lses = [], []
     for t in range(L, T):
@@ -296,42 +298,75 @@ def _decode_and_check(inp, scale, L, T, heads, key_samples):
     torch.cuda.synchronize()
     got = torch.stack(outs, 2).double().cpu().numpy().reshape(B * H, T - L, d)
     gotl = torch.stack(lses, 2).double().cpu().numpy().reshape(B * H, T - L)
-    rows = np.arange(L, T)
-    hi = np.repeat(heads, len(rows))
-    ri = np.tile(rows, len(heads))
-    ro, rl, _, _ = oracle.rows(inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f, scale, hi, ri)
-    _check(got[hi, ri - L], ro, "bf16", f"decode {T - L} steps out")
-    if gated:   # the gate cache holds the prefix sums of log f (fp32)
-        ref_f = np.cumsum(inp.log_f.double().numpy().reshape(B * H, -1)[:, :T], axis=1)
-        got_f = fc.double().cpu().numpy().reshape(B * H, T)
-        err = np.max(np.abs(got_f - ref_f) / np.maximum(1.0, np.abs(ref_f)))
+    return {"kc_pre": kc_pre, "vc_pre": vc_pre, "out": got, "lse": gotl,
+            "kc": kc.double().cpu().numpy().reshape(B * H, T, d),
+            "fc": None if fc is None else fc.double().cpu().numpy().reshape(B * H, T)}
+
+
+def _check_decode(inp, scale, L, T, dec, ro, rl, rkc, key_samples):
+    """ro, rl: the oracle's rows L .. T-1 of every head; rkc: the oracle's
+    key cache after the prefill, every key of every head.  Every check runs
+    and prints before the first failure is raised."""
+    B, H, _, d = inp.q.shape
+    BH = B * H
+    n_chunks = (L + 63) // 64
+    k_in = inp.k.double().numpy().reshape(BH, -1, d)
+    failures = []
+
+    def run(fn, *args):
+        try:
+            fn(*args)
+        except AssertionError as e:
+            failures.append(e)
+    run(_check, dec["out"], ro, "bf16", f"decode {T - L} steps out (every head)")
+    run(_check, dec["lse"], rl, "bf16", f"decode {T - L} steps lse (every head)")
+    run(_check_cache, dec["kc_pre"], rkc, k_in[:, :L], "kcache after prefill (every key)",
+        n_chunks + 2)
+    np.testing.assert_array_equal(dec["vc_pre"], inp.v.double().numpy().reshape(BH, -1, d)[:, :L])
+    if dec["fc"] is not None:   # the gate cache holds the prefix sums of log f (fp32)
+        ref_f = np.cumsum(inp.log_f.double().numpy().reshape(BH, -1)[:, :T], axis=1)
+        err = np.max(np.abs(dec["fc"] - ref_f) / np.maximum(1.0, np.abs(ref_f)))
         print(f"gate cache: max rel err {err:.2e}")
         assert err < 1e-5
-    _check(gotl[hi, ri - L], rl, "bf16", f"decode {T - L} steps lse")
     # the cache after the last step against the oracle's in-place updated keys
-    keys = sorted(set(rng.integers(0, T, key_samples).tolist()) | {0, T - 1})
-    hi = np.repeat(heads, len(keys))
-    ki = np.tile(keys, len(heads))
+    rng = np.random.default_rng(7)
+    keys = sorted(set(rng.integers(0, T, key_samples).tolist()) | {0, L - 1, L, T - 1})
+    hi = np.repeat(np.arange(BH), len(keys))
+    ki = np.tile(keys, BH)
     ref_k = oracle.transported_keys(inp.k, inp.w, inp.beta, T - 1, hi, ki)
-    got_k = kc.double().cpu().numpy().reshape(B * H, T, d)[hi, ki]
-    _check_cache(got_k, ref_k, n_chunks + 2 + (T - L), "kcache after decode")
+    run(_check_cache, dec["kc"][hi, ki], ref_k, k_in[hi, ki],
+        f"kcache after decode ({len(hi)} keys)", n_chunks + 2 + (T - L))
+    if failures:
+        raise failures[0]
+
+
+def _decode_and_check(inp, scale, L, T, key_samples=40):
+    """Small cases: the oracle recurrence over all T tokens, then every
+    decode row, the whole prefill key cache and sampled final keys."""
+    fut = _oracle_bg(inp, scale, Lcache=L)
+    dec = _decode_gpu(inp, scale, L, T)
+    ro, rl, rkc, _ = fut.result()
+    B, H, _, d = inp.q.shape
+    ro, rl = ro.reshape(B * H, T, d), rl.reshape(B * H, T)
+    _check_decode(inp, scale, L, T, dec, ro[:, L:], rl[:, L:], rkc.reshape(B * H, L, d),
+                  key_samples)
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_small_ragged(d):
     inp = generate(1, 3, 231, d, dtype="bf16", gate=False, seed=50)
-    _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, [0, 1, 2], key_samples=40)
+    _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, key_samples=40)
 
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_gated(d):
     # PaTH-FoX decode: the gate cache from the prefill, then gated steps
     inp = generate(1, 3, 231, d, dtype="bf16", gate=True, seed=53)
-    _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, [0, 1, 2], key_samples=30)
+    _decode_and_check(inp, 1 / math.sqrt(d), 170, 231, key_samples=30)
 
 
 def test_decode_short_prefix():
     # t from 5 to 69: one split of 64 keys, then two (the split size is a
     # multiple of 64 keys)
     inp = generate(1, 2, 70, 64, dtype="bf16", gate=False, seed=52)
-    _decode_and_check(inp, 0.125, 5, 70, [0, 1], key_samples=10)
+    _decode_and_check(inp, 0.125, 5, 70, key_samples=10)
