@@ -180,6 +180,32 @@ int path_decode_step(void* k_cache, void* v_cache,
                      void* stream);
 
 /*
+ * path_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, same kernels and the
+ * same results as path_decode_step (bit for bit), but the split partials go
+ * to an array the library keeps in device memory, one per device
+ * (8 MiB, held until the process ends; its address is looked up on the first
+ * call on each device).  Nothing is allocated or freed by this call.
+ *
+ * Limit: B*H * ceil((t+1)/64) * (d+2) * 4 bytes must not exceed 8 MiB
+ * (e.g. B*H = 64, d = 128: t < 16128); larger calls return
+ * PATH_ERR_WORKSPACE before any HIP call.  Argument errors are those of
+ * path_decode_step.
+ *
+ * Every call on one device shares that device's array, and each call
+ * overwrites it before reading it (no clearing is needed): calls that overlap
+ * on one device (different streams or threads, no ordering between them)
+ * race and give undefined results.  Calls on one stream are ordered.
+ */
+int path_decode_step_noalloc(void* k_cache, void* v_cache,
+                             const void* q_t, const void* k_t, const void* v_t,
+                             const void* w_t, const float* beta_t,
+                             void* out_t, float* lse_t,
+                             int B, int H, int t, int T_max, int d, float scale,
+                             int dtype, void* stream);
+
+/*
  * PaTH-FoX decode (the forget gate of PaTH-FoX in the decode step).  The
  * PaTH-FoX weight multiplies the PaTH one by the product of the forget gates
  * f_{j+1} .. f_t (Chinese notes, PaTH-FoX extension), i.e. adds

@@ -30,7 +30,8 @@ EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes"
            "path_kcache_workspace_bytes", "path_kcache_from_prefill",
            "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
            "path_decode_step_gated", "path_transition_prep",
-           "path_kcache_from_prefill_paged", "path_decode_step_paged")
+           "path_kcache_from_prefill_paged", "path_decode_step_paged",
+           "path_decode_step_noalloc")
 
 
 class PathError(RuntimeError):
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.path_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.path_decode_step.restype = I
     lib.path_decode_step.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P, S, P]
+    lib.path_decode_step_noalloc.restype = I
+    lib.path_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.path_fcache_from_prefill.restype = I
     lib.path_fcache_from_prefill.argtypes = [P, P, I, I, I, I, P]
     lib.path_decode_step_gated.restype = I
@@ -198,6 +201,18 @@ def path_decode_step(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t,
                               float(scale), _dt(k_cache), _p(workspace), ws_bytes,
                               _stream(stream))
     _check(st, "path_decode_step")
+
+
+def path_decode_step_noalloc(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t, t,
+                             scale, stream=None):
+    """path_decode_step with the library's own partials buffer (no workspace)."""
+    lib = load_library()
+    _require_cuda(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, lse_t)
+    B, H, T_max, d = k_cache.shape
+    st = lib.path_decode_step_noalloc(_p(k_cache), _p(v_cache), _p(q_t), _p(k_t), _p(v_t),
+                                      _p(w_t), _p(beta_t), _p(out_t), _p(lse_t), B, H, int(t),
+                                      T_max, d, float(scale), _dt(k_cache), _stream(stream))
+    _check(st, "path_decode_step_noalloc")
 
 
 def path_fcache_from_prefill(log_f, f_cache, stream=None):

@@ -236,30 +236,49 @@ size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype) {
     return align256((size_t)B * H * nsplit_max * (d + 2) * sizeof(float));
 }
 
-static int decode_step(void* k_cache, void* v_cache, float* f_cache, const void* q_t,
-                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
-                       const float* log_f_t, void* out_t, float* lse_t, int B, int H, int t,
-                       int T_max, int d, float scale, int dtype, void* workspace, size_t ws_bytes,
-                       void* stream, const CacheMap& map) {
+static int decode_check(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
+                        const void* v_t, const void* w_t, const float* beta_t, void* out_t,
+                        int B, int H, int t, int T_max, int d, float scale, int dtype) {
     if (B < 1 || H < 1 || T_max < 1 || t < 0 || t >= T_max || !valid_dtype(dtype))
         return PATH_ERR_INVALID;
     if (dtype != PATH_BF16 || (d != 64 && d != 128)) return PATH_ERR_UNSUPPORTED;
     if (!k_cache || !v_cache || !q_t || !k_t || !v_t || !w_t || !beta_t || !out_t)
         return PATH_ERR_INVALID;
     if (!(scale == scale)) return PATH_ERR_INVALID;
-    const size_t need = path_decode_workspace_bytes(B, H, T_max, d, dtype);
-    if (!workspace || ws_bytes < need) return PATH_ERR_WORKSPACE;
+    return PATH_OK;
+}
+
+// The step itself, after the checks; part holds the split partials.
+static int decode_launch(void* k_cache, void* v_cache, float* f_cache, const void* q_t,
+                         const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                         const float* log_f_t, void* out_t, float* lse_t, int B, int H, int t,
+                         int T_max, int d, float scale, void* part, void* stream,
+                         const CacheMap& map) {
     DecodeArgs a{};
     a.k_cache = k_cache; a.v_cache = v_cache;
     a.q = q_t; a.k = k_t; a.v = v_t; a.w = w_t; a.beta = beta_t;
     a.out = out_t; a.lse = lse_t;
-    a.part = static_cast<float*>(workspace);
+    a.part = static_cast<float*>(part);
     a.BH = B * H; a.t = t; a.T_max = T_max;
     a.scale2 = scale * kLog2e;
     a.log_f = log_f_t; a.f_cache = f_cache;
     a.map = map;
     return launch_path_decode(a, d, static_cast<hipStream_t>(stream)) == hipSuccess
                ? PATH_OK : PATH_ERR_HIP;
+}
+
+static int decode_step(void* k_cache, void* v_cache, float* f_cache, const void* q_t,
+                       const void* k_t, const void* v_t, const void* w_t, const float* beta_t,
+                       const float* log_f_t, void* out_t, float* lse_t, int B, int H, int t,
+                       int T_max, int d, float scale, int dtype, void* workspace, size_t ws_bytes,
+                       void* stream, const CacheMap& map) {
+    const int st = decode_check(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, B, H, t,
+                                T_max, d, scale, dtype);
+    if (st != PATH_OK) return st;
+    const size_t need = path_decode_workspace_bytes(B, H, T_max, d, dtype);
+    if (!workspace || ws_bytes < need) return PATH_ERR_WORKSPACE;
+    return decode_launch(k_cache, v_cache, f_cache, q_t, k_t, v_t, w_t, beta_t, log_f_t, out_t,
+                         lse_t, B, H, t, T_max, d, scale, workspace, stream, map);
 }
 
 int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
@@ -269,6 +288,24 @@ int path_decode_step(void* k_cache, void* v_cache, const void* q_t, const void* 
     const CacheMap map{nullptr, 0, 0, 0, H, T_max};
     return decode_step(k_cache, v_cache, nullptr, q_t, k_t, v_t, w_t, beta_t, nullptr, out_t, lse_t,
                        B, H, t, T_max, d, scale, dtype, workspace, ws_bytes, stream, map);
+}
+
+int path_decode_step_noalloc(void* k_cache, void* v_cache, const void* q_t, const void* k_t,
+                             const void* v_t, const void* w_t, const float* beta_t, void* out_t,
+                             float* lse_t, int B, int H, int t, int T_max, int d, float scale,
+                             int dtype, void* stream) {
+    const int st = decode_check(k_cache, v_cache, q_t, k_t, v_t, w_t, beta_t, out_t, B, H, t,
+                                T_max, d, scale, dtype);
+    if (st != PATH_OK) return st;
+    // the step uses at most ceil((t + 1) / 64) splits per head
+    const size_t nsplit_max = ((size_t)t + kDecodeSplitQuantum) / kDecodeSplitQuantum;
+    if ((size_t)B * H * nsplit_max * (d + 2) * sizeof(float) > kDecodeScratchBytes)
+        return PATH_ERR_WORKSPACE;
+    void* part = nullptr;
+    if (decode_scratch(&part) != hipSuccess) return PATH_ERR_HIP;
+    const CacheMap map{nullptr, 0, 0, 0, H, T_max};
+    return decode_launch(k_cache, v_cache, nullptr, q_t, k_t, v_t, w_t, beta_t, nullptr, out_t,
+                         lse_t, B, H, t, T_max, d, scale, part, stream, map);
 }
 
 int path_fcache_from_prefill(const float* log_f, float* f_cache, int B, int H, int L, int T_max,

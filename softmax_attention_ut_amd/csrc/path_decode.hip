@@ -242,6 +242,29 @@ static hipError_t resident_split_blocks(int D, int& n) {
     return hipSuccess;
 }
 
+// Split partials of path_decode_step_noalloc, for callers that cannot
+// allocate: one array per device, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it names a host-side
+// stand-in); it passes the device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {       // first call on this device (concurrent first calls store the same value)
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
+
 hipError_t launch_path_decode(const DecodeArgs& args, int D, hipStream_t s) {
     if (D != 64 && D != 128) return hipErrorInvalidValue;
     // Split the t + 1 keys of each head so that all (split, head) workgroups

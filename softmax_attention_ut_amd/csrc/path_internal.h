@@ -210,6 +210,11 @@ hipError_t launch_path_fwd_f32(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s);
 hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s);
+// The library's own split-partials buffer of path_decode_step_noalloc: its
+// size, and its device address on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_path_fcache(const FcacheArgs& a, hipStream_t s);
 hipError_t launch_path_transition(TransArgs a, hipStream_t s);
 

@@ -89,6 +89,24 @@ def test_decode_argument_errors_before_launch():
     assert lib.path_decode_step(*args(3, 16, 64, pa.PATH_BF16, 8)) == -4
 
 
+def test_noalloc_decode_argument_errors_before_launch():
+    """path_decode_step_noalloc checks its arguments like path_decode_step
+    and rejects calls whose partials exceed its 8 MiB array, all before any
+    HIP call (the fake pointers are never dereferenced)."""
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    args = lambda B, H, t, T, d, dt, q=p: (p, p, q, p, p, p, p, p, None, B, H, t, T, d, 0.1, dt,
+                                           None)
+    assert lib.path_decode_step_noalloc(*args(1, 1, 16, 16, 64, pa.PATH_BF16)) == -1  # t >= T_max
+    assert lib.path_decode_step_noalloc(*args(1, 1, 3, 16, 64, pa.PATH_BF16, None)) == -1
+    assert lib.path_decode_step_noalloc(*args(0, 1, 3, 16, 64, pa.PATH_BF16)) == -1
+    assert lib.path_decode_step_noalloc(*args(1, 1, 3, 16, 96, pa.PATH_BF16)) == -2
+    assert lib.path_decode_step_noalloc(*args(1, 1, 3, 16, 64, pa.PATH_F32)) == -2
+    # 64 heads, d = 128: 64 * ceil((t+1)/64) * 130 * 4 bytes <= 8 MiB holds up to t = 16127
+    assert lib.path_decode_step_noalloc(*args(2, 32, 16128, 20000, 128, pa.PATH_BF16)) == -4
+    assert lib.path_decode_step_noalloc(*args(128, 64, 100, 200, 128, pa.PATH_BF16)) == -4
+
+
 def test_gated_decode_argument_errors_before_launch():
     lib = pa.load_library()
     p = ctypes.c_void_p(4096)
