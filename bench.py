@@ -42,11 +42,14 @@ def flop_model(B, H, L, d, C=64):
             own chunk and the key chunk: 2 d^2 C per (query chunk, chunk) pair
             with the d x d product (d = 64), 4 C^2 d with the rank-C form
             Q - (Q W^T) U (d = 128)
-      diag  the diagonal-chunk extras done by the scan kernel: Q W^T, the
-            carry to the chunk start and the strictUpper(Q W^T) Y correction
-      prep  the per-chunk UT work of the prepare stage (G, R, T^{-1}, U, Y, K~,
-            and M = W^T U for the d x d carry)
-    "scan" is what the scan kernel must compute; "alg" the whole forward."""
+      diag  the own-chunk extras: Q W^T, the carry to the chunk start and the
+            lower(Q W^T) Y correction
+      prep  the per-chunk UT work (G, R, T^{-1}, U, Y, K~, and M = W^T U for
+            the d x d carry), which the survey's count of the prepare stage
+            also takes to cover the own-chunk extras
+    "scan" is what the scan kernel computes: at d = 64 the prepare stage takes
+    the own-chunk step (its extras and the own-chunk Q K^T, C^2 d per chunk),
+    at d = 128 the scan does.  "alg" is the whole forward: eff + carry + prep."""
     N = (L + C - 1) // C
     dense = d == 64
     pairs = (N - 1) * (N - 2) / 2.0
@@ -55,8 +58,8 @@ def flop_model(B, H, L, d, C=64):
     f_diag = N * (4.0 * C * C * d + 2.0 * C ** 3)
     f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3 + (2.0 * C * d * d if dense else 0.0))
     BH = B * H
-    return {"eff": BH * f_eff, "scan": BH * (f_eff + f_carry + f_diag),
-            "alg": BH * (f_eff + f_carry + f_prep)}
+    f_scan = f_eff + f_carry - N * C * C * d if dense else f_eff + f_carry + f_diag
+    return {"eff": BH * f_eff, "scan": BH * f_scan, "alg": BH * (f_eff + f_carry + f_prep)}
 
 
 def _kernel_sha(name):
@@ -145,7 +148,8 @@ def bench_fwd(args, cfg, torch, pa, inputs):
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        pa.path_attn_fwd_prepare(g["k"], g["v"], g["w"], g["beta"], g["log_f"], 0, ws, stream)
+        pa.path_attn_fwd_prepare(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], cfg.scale,
+                                 0, ws, stream)
         if ev:
             ev[1].record(stream)
         pa.path_attn_fwd_scan(g["q"], g["k"], g["v"], g["w"], g["log_f"], out, lse, cfg.scale,

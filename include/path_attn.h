@@ -106,18 +106,21 @@ int path_attn_fwd(const void* q, const void* k, const void* v, const void* w,
  * separately.  Same arguments, layouts and errors as path_attn_fwd.
  *
  * path_attn_fwd_prepare: the per-chunk stage (the pages' boundary-adjusted
- *   keys computed beforehand, Dutch summary section 3): the UT transform of
- *   every chunk and the chunk-local forget-gate sums, written to `workspace`.
- *   Reads k, v, w, beta, log_f.
+ *   keys and queries computed beforehand, Dutch summary section 3): the UT
+ *   transform of every chunk and the chunk-local forget-gate sums, written
+ *   to `workspace`; for bf16 with d = 64 also each query chunk's step with
+ *   its own chunk (queries carried to the chunk start, the probabilities of
+ *   the chunk's own keys), which needs q and scale.  Reads q, k, v, w, beta,
+ *   log_f.
  * path_attn_fwd_scan: the right-to-left scan of each query tile over the key
  *   chunks (Dutch summary section 3), reading q and the workspace written by
- *   a preceding path_attn_fwd_prepare with the same B, H, L, d, dtype, chunk
- *   and the same log_f presence (the workspace must not be modified in
- *   between).  Writes out and lse.
+ *   a preceding path_attn_fwd_prepare with the same q, B, H, L, d, scale,
+ *   dtype, chunk and the same log_f presence (the workspace must not be
+ *   modified in between).  Writes out and lse.
  */
-int path_attn_fwd_prepare(const void* k, const void* v, const void* w,
+int path_attn_fwd_prepare(const void* q, const void* k, const void* v, const void* w,
                           const float* beta, const float* log_f,
-                          int B, int H, int L, int d, int dtype, int chunk,
+                          int B, int H, int L, int d, float scale, int dtype, int chunk,
                           void* workspace, size_t ws_bytes, void* stream);
 
 int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* w,

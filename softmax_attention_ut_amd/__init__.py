@@ -64,7 +64,7 @@ def load_library(path: str = LIB_PATH):
     lib.path_attn_fwd.restype = I
     lib.path_attn_fwd.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
     lib.path_attn_fwd_prepare.restype = I
-    lib.path_attn_fwd_prepare.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, S, P]
+    lib.path_attn_fwd_prepare.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
     lib.path_attn_fwd_scan.restype = I
     lib.path_attn_fwd_scan.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
     lib.path_kcache_workspace_bytes.restype = S
@@ -144,14 +144,15 @@ def path_attn_fwd(q, k, v, w, beta, log_f, out, lse, scale, chunk=0,
     _check(st, "path_attn_fwd")
 
 
-def path_attn_fwd_prepare(k, v, w, beta, log_f, chunk=0, workspace=None, stream=None):
-    """The per-chunk UT-transform stage of path_attn_fwd (fills workspace)."""
+def path_attn_fwd_prepare(q, k, v, w, beta, log_f, scale, chunk=0, workspace=None, stream=None):
+    """The per-chunk stage of path_attn_fwd (fills workspace)."""
     lib = load_library()
-    _require_cuda(k, v, w, beta, log_f, workspace)
+    _require_cuda(q, k, v, w, beta, log_f, workspace)
     B, H, L, d = k.shape
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib.path_attn_fwd_prepare(_p(k), _p(v), _p(w), _p(beta), _p(log_f), B, H, L, d,
-                                   _dt(k), int(chunk), _p(workspace), ws_bytes, _stream(stream))
+    st = lib.path_attn_fwd_prepare(_p(q), _p(k), _p(v), _p(w), _p(beta), _p(log_f), B, H, L, d,
+                                   float(scale), _dt(k), int(chunk), _p(workspace), ws_bytes,
+                                   _stream(stream))
     _check(st, "path_attn_fwd_prepare")
 
 

@@ -86,16 +86,23 @@ int plan_fwd(int B, int H, int L, int d, int dtype, int& chunk, bool gate, const
     return PATH_OK;
 }
 
-UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, const float* beta,
-               const float* log_f, int L, int d, int chunk, void* workspace, bool with_z) {
+// Sections at offset 0 other than kt (which always comes first) are absent.
+UtArgs ut_args(const FwdPlan& p, const void* q, float scale, const void* k, const void* v,
+               const void* w, const float* beta, const float* log_f, int L, int d, int chunk,
+               void* workspace, bool with_z) {
     UtArgs u{};
     u.k = k; u.v = v; u.w = w; u.beta = beta; u.log_f = log_f;
     u.BH = p.BH; u.L = L; u.N = p.N; u.C = chunk; u.D = d;
     u.kt = at(workspace, p.ws.kt);
-    u.ut = at(workspace, p.ws.ut);
+    u.ut = p.ws.ut ? at(workspace, p.ws.ut) : nullptr;
     u.vt = p.ws.vt ? at(workspace, p.ws.vt) : nullptr;
-    u.yt = at(workspace, p.ws.yt);
+    u.yt = p.ws.yt ? at(workspace, p.ws.yt) : nullptr;
     u.zt = with_z ? at(workspace, p.ws.zt) : nullptr;
+    u.q = p.ws.qt ? q : nullptr;
+    u.scale2 = scale * kLog2e;
+    u.qt = p.ws.qt ? at(workspace, p.ws.qt) : nullptr;
+    u.pd = p.ws.pd ? at(workspace, p.ws.pd) : nullptr;
+    u.ml = p.ws.ml ? reinterpret_cast<float*>(at(workspace, p.ws.ml)) : nullptr;
     u.mt = p.ws.mt ? at(workspace, p.ws.mt) : nullptr;
     u.loc = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.loc)) : nullptr;
     u.csum = p.gate ? reinterpret_cast<float*>(at(workspace, p.ws.csum)) : nullptr;
@@ -107,14 +114,16 @@ UtArgs ut_args(const FwdPlan& p, const void* k, const void* v, const void* w, co
 
 extern "C" {
 
-int path_attn_fwd_prepare(const void* k, const void* v, const void* w, const float* beta,
-                          const float* log_f, int B, int H, int L, int d, int dtype, int chunk,
-                          void* workspace, size_t ws_bytes, void* stream) {
+int path_attn_fwd_prepare(const void* q, const void* k, const void* v, const void* w,
+                          const float* beta, const float* log_f, int B, int H, int L, int d,
+                          float scale, int dtype, int chunk, void* workspace, size_t ws_bytes,
+                          void* stream) {
     FwdPlan p;
     int st = plan_fwd(B, H, L, d, dtype, chunk, log_f != nullptr, workspace, ws_bytes, p);
     if (st != PATH_OK) return st;
-    if (!k || !v || !w || !beta) return PATH_ERR_INVALID;
-    const UtArgs u = ut_args(p, k, v, w, beta, log_f, L, d, chunk, workspace, false);
+    if (!q || !k || !v || !w || !beta) return PATH_ERR_INVALID;
+    if (!(scale == scale)) return PATH_ERR_INVALID;
+    const UtArgs u = ut_args(p, q, scale, k, v, w, beta, log_f, L, d, chunk, workspace, false);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = p.bf ? launch_path_ut_bf16(u, s) : launch_path_ut_f32(u, s);
     return e == hipSuccess ? PATH_OK : PATH_ERR_HIP;
@@ -130,11 +139,12 @@ int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* 
     if (st != PATH_OK) return st;
     if (!q || !k || !v || !w || !out) return PATH_ERR_INVALID;
     if (!(scale == scale)) return PATH_ERR_INVALID;
-    const UtArgs u = ut_args(p, k, v, w, nullptr, log_f, L, d, chunk, wsp, false);
+    const UtArgs u = ut_args(p, q, scale, k, v, w, nullptr, log_f, L, d, chunk, wsp, false);
     FwdArgs f{};
     f.q = q; f.k = k; f.v = v; f.w = w;
     f.kt = u.kt; f.ut = u.ut; f.vt = u.vt; f.yt = u.yt; f.mt = u.mt;
     f.loc = u.loc; f.csum = u.csum; f.gb = u.gb;
+    f.qt = u.qt; f.pd = u.pd; f.ml = u.ml;
     f.out = out; f.lse = lse;
     f.BH = p.BH; f.L = L; f.N = p.N; f.C = chunk; f.D = d;
     f.nqb = (p.N + 1) / 2;
@@ -149,8 +159,8 @@ int path_attn_fwd(const void* q, const void* k, const void* v, const void* w,
                   int B, int H, int L, int d, float scale, int dtype, int chunk,
                   void* workspace, size_t ws_bytes, void* stream) {
     if (!q || !out) return PATH_ERR_INVALID;
-    int st = path_attn_fwd_prepare(k, v, w, beta, log_f, B, H, L, d, dtype, chunk, workspace,
-                                   ws_bytes, stream);
+    int st = path_attn_fwd_prepare(q, k, v, w, beta, log_f, B, H, L, d, scale, dtype, chunk,
+                                   workspace, ws_bytes, stream);
     if (st != PATH_OK) return st;
     return path_attn_fwd_scan(q, k, v, w, log_f, out, lse, B, H, L, d, scale, dtype, chunk,
                               workspace, ws_bytes, stream);

@@ -1,37 +1,47 @@
-// path_fwd (bf16 mode): blockwise PaTH attention forward on gfx950 MFMA.
+// path_fwd (bf16 mode): blockwise PaTH attention forward on gfx950 MFMA,
+// the right-to-left scan over key chunks.
 //
 // Algorithm (Dutch summary section 3: boundary-adjusted queries/keys per
 // block, a right-to-left scan over key/value blocks, FlashAttention-style
 // on-chip tiling; Chinese notes, training strategy: UT transform and the
-// full-matrix form).  Chunks hold C = 64 tokens.  A wave owns 32 queries of
-// one chunk a and walks the key chunks b = a, a-1, ..., 0:
+// full-matrix form).  Chunks hold C = 64 tokens.  A query chunk a walks the
+// key chunks b = a, a-1, ..., 0:
 //   b = a:  S = Q K~^T + strictUpper(Q W^T) Y   (causal mask j <= i)
 //           Q <- Q - lower(Q W^T) U             (query carried to chunk start)
-//   b < a:  S = Q K~^T,  X = Q W^T
-//           Q <- Q - X U   (skipped for b = 0)  (query carried through chunk b)
+//   b < a:  S = Q K~^T;  Q carried through chunk b (skipped for b = 0)
 // and accumulates softmax(S) V online.  Every product is a bf16 MFMA with
 // fp32 accumulation; the carried query Q stays in fp32 accumulators and is
 // rounded to bf16 only as an MFMA operand.
 //
-// Orientation.  All products are formed transposed (S^T = K~ Q^T,
-// X^T = W Q^T, O^T += V^T P^T, Q^T -= U^T X^T), so every accumulator that
-// feeds a later product (S^T -> P^T, X^T, Q^T) is already in B-operand
-// position: accumulator registers 8s..8s+7 are the B operand of k-step s
-// under the k-slot permutation perm16 (path_internal.h).  V^T, U^T and Y^T
-// are written by path_ut with their key axis in that slot order and the d
-// rows of V^T, U^T permuted too, so the carried query and the output come
-// out with d in natural order: K~ and W are used as they are, and every LDS
-// operand read is one 16-byte ds_read.
+// d = 64 (path_fwd_bf16_d64pp_kernel): the step b = a is taken by the prepare
+// stage (path_ut_bf16.hip), which leaves the query carried to its chunk
+// start, the pending probabilities of its own keys and their maximum and sum.
+// The scan carries the query through every left chunk with the chunk's d x d
+// product, Q <- Q - Q M (M = W^T U): 2 d^2 flops per query and chunk against
+// 4 C d for the rank-C form.  A workgroup of 8 waves (two per SIMD, in
+// alternating matrix and vector phases) holds four query chunks; workgroups
+// are persistent, one per CU.
 //
-// Pipeline.  A workgroup (4 waves = 128 queries = query chunks 2qb, 2qb+1)
-// stages key chunks in LDS in two alternating buffer sets.  While the waves
-// compute on one set, the next chunk is copied into the other with
-// global_load_lds_dwordx4 (HBM/L2 -> LDS without passing through VGPRs).
-// LDS tiles are unpadded; the 16-byte units of row r are XOR-swizzled by
-// (r & 7), which keeps the 32-row MFMA operand reads free of bank conflicts.
-// Block order: heaviest query blocks first; when BH is a multiple of 8 all
-// blocks of one head land on one XCD (blocks are dealt to the 8 XCDs
-// round-robin), so a head's chunks are reused out of that XCD's L2.
+// d = 128 (path_fwd_bf16_kernel): every step, the own chunk's too, is taken
+// here, with the rank-C carry Q <- Q - (Q W^T) U; a workgroup of 4 waves
+// holds two query chunks (32 queries per wave).
+//
+// Orientation.  All products are formed transposed (S^T = K~ Q^T,
+// O^T += V^T P^T, Q^T += (-M^T) Q^T or Q^T -= U^T X^T), so every accumulator
+// that feeds a later product (S^T -> P^T, X^T, Q^T) is already in B-operand
+// position: accumulator registers 8s..8s+7 are the B operand of k-step s
+// under the k-slot permutation perm16 (path_internal.h).  The transposed
+// tiles the prepare stage writes have their key axis in that slot order and
+// their d rows permuted, so the carried query and the output come out with d
+// in natural order, and every LDS operand read is one 16-byte ds_read (or,
+// for the d = 64 V tile, LDS transpose loads).
+//
+// Staging.  Key chunks are copied HBM/L2 -> LDS with global_load_lds (no
+// VGPRs) into two alternating stage sets while the waves compute on the
+// other.  LDS tiles are unpadded, their 16-byte units XOR-swizzled per row.
+// Dealing: heaviest query blocks first, and when B*H is a multiple of 8 all
+// blocks of one head go to one XCD, so a head's chunks are reused out of that
+// XCD's L2.
 #include <type_traits>
 
 #include "path_internal.h"
@@ -411,123 +421,6 @@ __device__ __forceinline__ void raise_max(WaveState<64, GATE>& st, float shift) 
         for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
 }
 
-// One key chunk strictly left of the wave's query chunk, d = 64.
-//
-// The carried query is held pre-scaled by c2 = scale*log2(e) (the transport
-// is linear, so this is the same as scaling the logits).  One extra k-step of
-// the logit product adds the key's gate term -loc_j and the query's offset
-// a_i - m_run, each as three bf16 terms:
-//     A row j    = (g_h, g_m, g_l, 1, 1, 1, 0, 0 | 0 ... 0),   g = -loc_j
-//     B column i = (1, 1, 1, o_h, o_m, o_l, 0, 0 | 0 ... 0),   o = a_i - m_run
-// so the accumulator holds z_ij - m_run and the probabilities are exp2 of it.
-// The A rows are written per key by path_ut (gate) or constant (no gate).
-// The running maximum is raised only when a row sum exceeds kRescaleTrigger.
-// The query is carried through the whole chunk with the chunk's d x d
-// product, Q^T += (-M^T) Q^T (M = W^T U); the carry, the logits and the
-// softmax only share the query operand.
-//
-// Issue order (a wave issues in program order, and an MFMA occupies the
-// matrix pipe for 8 passes while independent vector instructions issue):
-// logits of keys 0..31, logits of keys 32..63, the carry interleaved with
-// the probabilities of keys 0..31, the PV product of keys 0..31 interleaved
-// with the probabilities of keys 32..63, the PV product of keys 32..63.
-template <bool GATE>
-__device__ __forceinline__ void dense_step(WaveState<64, GATE>& st, const Stage<64>& sg, int l32, int hh) {
-    constexpr int C = 64, D = 64, KS = 4;
-    const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
-    const unsigned lower = hh ? 0u : ~0u;   // bias terms live on the lower lane half
-    bf16x8 opg[2];
-    if (GATE) {
-        opg[0] = lds8(sg.gb + l32 * 16 + 8 * hh);
-        opg[1] = lds8(sg.gb + (32 + l32) * 16 + 8 * hh);
-    } else {
-        opg[0] = opg[1] = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
-    }
-    bf16x8 opk[2 * KS];
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
-    bf16x8 bq;
-    {
-        const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
-        bf16 h, m, l;
-        split3(a_i - st.m_run, h, m, l);
-        bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
-    }
-    f32x16 s[2];
-    bf16x8 opm[2 * KS];
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
-        s[kt2] = mfma32(opg[kt2], bq, s[kt2]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
-        if (kt2 == 0) {
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    opm[KS * dt + ks] = lds8(sg.mt + (32 * dt + l32) * D + st.offD[ks]);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // carry Q^T += (-M^T) Q^T (also formed, unused, for key chunk 0), with the
-    // probabilities of keys 0..31
-    bf16x8 pB[KS];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) st.qacc[dt] = mfma32(opm[KS * dt + ks], st.qB[ks], st.qacc[dt]);
-    float psum = tile_probs(s[0], pB[0], pB[1], 0.f);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (__any(!(psum <= kRescaleTrigger))) {
-        const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
-        raise_max(st, shift);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[1][v] -= shift;
-        psum = tile_probs(s[0], pB[0], pB[1], shift);
-    }
-    st.l_run += psum;
-    bf16x8 opv[2 * KS];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opv[KS * dt + ks] = pv_operand(sg.v, st.voff, dt, ks);
-    // O^T += V^T P^T for keys 0..31, with the probabilities of keys 32..63
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
-    psum = tile_probs(s[1], pB[2], pB[3], 0.f);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (__any(!(psum <= kRescaleTrigger))) {
-        const float shift = fmaxf(pair_max(tile_max(s[1])), 0.f);
-        raise_max(st, shift);
-        psum = tile_probs(s[1], pB[2], pB[3], shift);
-    }
-    st.l_run += psum;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 2; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-    if (GATE) st.dab += static_cast<double>(sg.loc[C]);
-}
-
 // Per-lane setup shared by both kernels: block decode, query load, state.
 template <int D, bool GATE>
 struct ScanSetup {
@@ -716,6 +609,17 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
 // carry's MFMAs are issued in the vector phase, where they fill the matrix
 // pipe while the other wave of the SIMD issues the next logits).
 //
+// The carried query is held pre-scaled by c2 = scale*log2(e) (the transport
+// is linear, so this is the same as scaling the logits).  One extra k-step of
+// the logit product adds the key's gate term -loc_j and the query's offset
+// a_i - m_run, each as three bf16 terms:
+//     A row j    = (g_h, g_m, g_l, 1, 1, 1, 0, 0 | 0 ... 0),   g = -loc_j
+//     B column i = (1, 1, 1, o_h, o_m, o_l, 0, 0 | 0 ... 0),   o = a_i - m_run
+// so the accumulator holds z_ij - m_run and the probabilities are exp2 of it.
+// The A rows are written per key by path_ut (gate) or constant (no gate).
+// The query is carried through the whole chunk with the chunk's d x d
+// product, Q^T += (-M^T) Q^T (M = W^T U).
+//
 // Issue order: the PV operands are read first and the logit operands (K~
 // rows, bias rows) after them, so that the PV MFMAs cover the latency of the
 // latter; the -M^T operands are read in the shadow of the logit MFMAs.
@@ -812,191 +716,6 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
     for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
 }
 
-// The d = 64 diagonal step of one wave (its own chunk), in three parts.
-//
-// Products: the rank-C form of the diagonal step (Chinese notes, training
-// strategy: full-matrix form), in the transposed orientation, with the query
-// not yet scaled by c2:
-//     X^T = W Q^T,  S^T = K~ Q^T + g (g_j = -loc_j / c2, three bf16 terms)
-//     S^T += Y^T strictUpper(X)^T          (keys m > i of the query's row i)
-//     Q^T += (-U^T) lower(X)^T             (the query carried to its chunk start)
-template <bool GATE>
-__device__ __forceinline__ void diag64_products(WaveState<64, GATE>& st, f32x16 s[2], const Stage<64>& sg,
-                                               const bf16* sy, int l32, int hh, int iloc, float c2) {
-    constexpr int D = 64, C = 64, KS = 4;
-    // each operand group is read under the MFMAs of the group before it
-    bf16x8 opw[2 * KS], opk[2 * KS], opy[2 * KS], opu[2 * KS];
-    f32x16 x[2];
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            x[kt2][v] = 0.f;
-            s[kt2][v] = 0.f;
-        }
-    float gl8[2] = {0.f, 0.f};
-    if (GATE) {
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) gl8[kt2] = sg.loc[32 * kt2 + l32];
-    }
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opw[KS * kt2 + ks] = lds8(sg.w + (32 * kt2 + l32) * D + st.offD[ks]);
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opk[KS * kt2 + ks] = lds8(sg.k + (32 * kt2 + l32) * D + st.offD[ks]);
-    // X^T = W Q^T
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) x[kt2] = mfma32(opw[KS * kt2 + ks], st.qB[ks], x[kt2]);
-    __builtin_amdgcn_sched_group_barrier(0x100, GATE ? 10 : 8, 0);   // W reads (+ gate terms)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {                                     // X MFMAs, K~ reads between them
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opy[KS * kt2 + ks] = lds8(sy + (32 * kt2 + l32) * C + st.offD[ks]);
-    // S^T = K~ Q^T + g
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opk[KS * kt2 + ks], st.qB[ks], s[kt2]);
-    if (GATE) {   // the key's gate term -loc_j / c2 as three bf16 terms
-        bf16x8 ones = {};
-        if (hh == 0) {
-            ones[0] = static_cast<bf16>(1.f);
-            ones[1] = static_cast<bf16>(1.f);
-            ones[2] = static_cast<bf16>(1.f);
-        }
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) {
-            bf16 gh, gm, gl;
-            split3(-gl8[kt2] * (1.f / c2), gh, gm, gl);
-            bf16x8 ag = {};
-            if (hh == 0) {
-                ag[0] = gh;
-                ag[1] = gm;
-                ag[2] = gl;
-            }
-            s[kt2] = mfma32(ag, ones, s[kt2]);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {                                     // logit MFMAs, Y reads between them
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // split X^T at the query's row: xu = strictly upper part (m > i), x keeps m <= i
-    bf16x8 xu[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int v = 8 * (ks & 1) + t;
-            const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
-            const float xv = x[ks >> 1][v];
-            xu[ks][t] = static_cast<bf16>(m > iloc ? xv : 0.f);
-            x[ks >> 1][v] = (m <= iloc) ? xv : 0.f;
-        }
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) opu[KS * dt + ks] = lds8(sg.u + (32 * dt + l32) * C + st.offD[ks]);
-    // S^T += Y^T strictUpper(X)^T
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) s[kt2] = mfma32(opy[KS * kt2 + ks], xu[ks], s[kt2]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {                                     // Y MFMAs, -U^T reads between them
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Q^T += (-U^T) lower(X)^T
-    bf16x8 xB[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) xB[ks] = pack8(x[ks >> 1], ks & 1);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) st.qacc[dt] = mfma32(opu[KS * dt + ks], xB[ks], st.qacc[dt]);
-}
-
-// Softmax: the causal mask (keys j <= i), the first running maximum and the
-// probabilities of z = c2 S + a_i; then the query, now at its chunk start, is
-// scaled by c2 and repacked, and the gate offset moves past the chunk (csum:
-// its gate sum).
-template <bool GATE>
-__device__ __forceinline__ void diag64_softmax(WaveState<64, GATE>& st, f32x16 s[2], bf16x8 pB[4],
-                                               int hh, int iloc, float c2, float csum) {
-    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            if ((32 * kt2 + 8 * (v >> 2) + 4 * hh + (v & 3)) > iloc) s[kt2][v] = -INFINITY;
-            mx = fmaxf(mx, s[kt2][v]);
-        }
-    mx = pair_max(mx);
-    const float cand = fmaf(mx, c2, a_i);
-    if (__any(cand > st.m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(st.m_run, cand);
-        const float alpha = fast_exp2(st.m_run - m_new);
-        st.m_run = m_new;
-        st.l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
-    }
-    const float msub = st.m_run - a_i;
-    float psum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
-        }
-    }
-    st.l_run += psum;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st.qacc[dt][v] *= c2;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-    if (GATE) st.dab += static_cast<double>(csum);
-}
-
-// The whole step: products, softmax, then O^T += V^T P^T with the chunk's V.
-template <bool GATE>
-__device__ __forceinline__ void diag_step64(WaveState<64, GATE>& st, const Stage<64>& sg, const bf16* sy,
-                                            int l32, int hh, int iloc, float c2) {
-    f32x16 s[2];
-    bf16x8 pB[4];
-    const float csum = GATE ? sg.loc[64] : 0.f;
-    diag64_products<GATE>(st, s, sg, sy, l32, hh, iloc, c2);
-    diag64_softmax<GATE>(st, s, pB, hh, iloc, c2, csum);
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) st.oacc[dt] = mfma32(pv_operand(sg.v, st.voff, dt, ks), pB[ks], st.oacc[dt]);
-}
-
 // Workgroup barrier without a memory fence: stage copies stay in flight
 // across it (each wave waits for its own copies explicitly); the clobber keeps
 // the compiler from moving LDS accesses across it.
@@ -1030,9 +749,8 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     constexpr int C = 64, D = 64, NT = 512;
     constexpr int TILE = C * D;
     // Two stage sets, each one LDS object for a key chunk's K~, -M^T, V, bias
-    // rows and gate terms and one for an own chunk's W, -U^T, Y^T (the
-    // compiler tells copy targets in flight from tiles being read per object,
-    // and it tracks only a few objects).
+    // rows and gate terms (the compiler tells copy targets in flight from
+    // tiles being read per object, and it tracks only a few objects).
     struct ChunkTiles {
         bf16 k[TILE];
         bf16 m[TILE];
@@ -1040,15 +758,8 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         bf16 gb[GATE ? C * 16 : 8];
         float loc[C + 4];
     };
-    struct OwnTiles {
-        bf16 w[TILE];
-        bf16 u[TILE];
-        bf16 y[TILE];
-    };
     __shared__ __attribute__((aligned(1024))) ChunkTiles km0;
     __shared__ __attribute__((aligned(1024))) ChunkTiles km1;
-    __shared__ __attribute__((aligned(1024))) OwnTiles dg0;
-    __shared__ __attribute__((aligned(1024))) OwnTiles dg1;
 
     const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const bool leader = wave_u >= 4;
@@ -1064,29 +775,53 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const int L = a.L, N = a.N, Lp = N * C;
     const unsigned loff = tile64_lane_offset(wave_u, lane);
     const unsigned vloff = vtile_lane_offset(wave_u, lane);
-    const float c2 = a.scale2;
     // query chunk 4qb + j: waves j (rows 0-31) and 7 - j (rows 32-63), which
-    // run on different SIMDs (wave w runs on SIMD w % 4), so that no SIMD has
-    // two diagonal steps at once in the own-chunk steps below
+    // run on different SIMDs (wave w runs on SIMD w % 4)
     WaveState<D, GATE> st;
-    const ScanSetup<D, GATE> u = scan_setup<D, GATE>(a, st, head, qb, 4 * qb + (leader ? 7 - wave_u : wave_u),
-                                                     (wave_u >> 2) * 32 + l32, l32, hh);
-    const int qc = u.qc, iloc = u.iloc;
-    const bool active = u.active;
+    bf16x8 pB[4];
+    const int qc = 4 * qb + (leader ? 7 - wave_u : wave_u);
+    const int iloc = (wave_u >> 2) * 32 + l32;
+    const bool active = qc < N;
+    ScanSetup<D, GATE> u;
+    u.head = head; u.qb = qb; u.qc = qc; u.iloc = iloc; u.active = active;
+    u.qi = qc * C + iloc;
+    u.qvalid = active && u.qi < L;
+    {
+        // the state after the query's own chunk, from the prepare stage: the
+        // query carried to its chunk start (scaled by scale*log2(e)), the
+        // pending probabilities of its own keys, their maximum and sum
+        const size_t row = (size_t)head * Lp + (active ? u.qi : 0);
+        const bf16* qrow = static_cast<const bf16*>(a.qt) + row * D;
+        const bf16* prow = static_cast<const bf16*>(a.pd) + row * C;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
+            st.qB[ks] = lds8(qrow + 16 * ks + 8 * hh);
+            pB[ks] = lds8(prow + 16 * ks + 8 * hh);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(st.qB[ks][t]);
+        }
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ml + 2 * row);
+        st.m_run = ml[0];
+        st.l_run = hh == 0 ? ml[1] : 0.f;   // the two lane halves' sums are added at the end
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
+        st.loc_i = GATE ? a.loc[row] : 0.f;
+        st.dab = GATE ? static_cast<double>(a.csum[(size_t)head * N + (active ? qc : 0)]) : 0.0;
+    }
     vtr_offsets(st.voff, lane);
 
     const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
-    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
-    const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
     const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
-    const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
     const bf16* mtg = static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D;
     const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
     const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
     const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
 
-    const Stage<D> set0{km0.k, dg0.w, dg0.u, km0.v, km0.m, km0.loc, km0.gb};
-    const Stage<D> set1{km1.k, dg1.w, dg1.u, km1.v, km1.m, km1.loc, km1.gb};
+    const Stage<D> set0{km0.k, nullptr, nullptr, km0.v, km0.m, km0.loc, km0.gb};
+    const Stage<D> set1{km1.k, nullptr, nullptr, km1.v, km1.m, km1.loc, km1.gb};
 
     // every [64][64] tile: wave w copies its 1 KB block w (rows 8w .. 8w+7)
     auto tile = [&](bf16* lds, const bf16* g) {
@@ -1113,51 +848,15 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         else
             copy_guarded<C, D, NT, true>(sg.v, vin + (size_t)kc * TILE, L - kc * C, tid);   // ragged: zero rows
     };
-    // an own chunk's W (rows past L zero-filled), -U^T and Y^T
-    auto issue_own = [&](const Stage<D>& sg, bf16* y, int kcd) {
-        if ((kcd + 1) * C <= L) tile(sg.w, win + (size_t)kcd * TILE);
-        else copy_guarded<C, D, NT>(sg.w, win + (size_t)kcd * TILE, L - kcd * C, tid);
-        tile(sg.u, ut + (size_t)kcd * TILE);
-        tile(y, yt + (size_t)kcd * TILE);
-    };
-    // ---- the block's own chunks ktop .. q0, every wave in step.  Chunk kc
-    // sits in set kc % 2, and the next chunk (with its own-chunk tiles) is
-    // copied while this one is computed; the steps are peeled so that every
-    // set is known at compile time (q0 is a multiple of 4). ----
-    const int q0 = 4 * qb;
-    const int ktop = min(q0 + 3, N - 1);
-    auto own_step = [&](int kc, const Stage<D>& cur, const Stage<D>& nxt, const bf16* ycur, bf16* ynxt) {
-        if (kc == ktop) {
-            issue_km(cur, kc);
-            issue_v(cur, kc);
-            issue_own(cur, const_cast<bf16*>(ycur), kc);
-            wait_vmem();
-            __syncthreads();
-        }
-        if (kc > 0) {
-            issue_km(nxt, kc - 1);
-            issue_v(nxt, kc - 1);
-            if (kc > q0) issue_own(nxt, ynxt, kc - 1);
-        }
-        if (active && kc <= qc) {
-            if (kc == qc) {
-                diag_step64<GATE>(st, cur, ycur, l32, hh, iloc, c2);
-            } else {
-                dense_step<GATE>(st, cur, l32, hh);
-            }
-        }
-        wait_vmem();
-        __syncthreads();
-    };
-    if (ktop >= q0 + 3) own_step(q0 + 3, set1, set0, dg1.y, dg0.y);
-    if (ktop >= q0 + 2) own_step(q0 + 2, set0, set1, dg0.y, dg1.y);
-    if (ktop >= q0 + 1) own_step(q0 + 1, set1, set0, dg1.y, dg0.y);
-    own_step(q0, set0, set1, dg0.y, dg1.y);
 
-    // ---- chunks q0-1 .. 0 in phases.  Chunk k's K~/-M^T/gate terms sit in
-    // set k % 2, its V tile in that set's V tile.  Every wave runs
-    //     for k = q0-1 .. 0:  M(k); barrier; V(k); barrier        then PV(0)
-    // where M(k) = PV(k+1) (k < q0-1), logits and carry of k, and V(k) = the
+    // ---- key chunks ktop-1 .. 0 in phases; ktop = the block's top chunk.
+    // Chunk k's K~/-M^T/gate terms sit in set k % 2, its V tile in that set's
+    // V tile.  A wave works on chunk k only when k < qc (its own chunk was
+    // done by the prepare stage, whose probabilities are pending against
+    // V(qc)); the other waves of the block keep the copies and barriers.
+    // Every wave runs
+    //     for k = ktop-1 .. 0:  M(k); barrier; V(k); barrier        then PV(0)
+    // where M(k) = PV(k+1), logits and carry of k, and V(k) = the
     // probabilities of k.  The followers (waves 0..3) enter one barrier late,
     // so between two barriers one wave of each SIMD is in a matrix phase and
     // the other in a vector phase.  Copies: at the start of its M(k) a leader
@@ -1165,8 +864,25 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     // V(k) a follower issues its blocks of chunk k-2 and V(k-1) -- the same
     // moment, one phase after the buffers' last reads.  Leaders wait for their
     // copies at the end of V(k), followers at the end of M(k): two phases
-    // later, and before the barrier that opens the first phase reading them. ----
-    if (q0 > 0) {
+    // later, and before the barrier that opens the first phase reading them.
+    // The prologue stages V(ktop), and chunk ktop-1 with V(ktop-1), whole. ----
+    const int ktop = min(4 * qb + 3, N - 1);
+    if (ktop & 1) {
+        issue_v(set1, ktop);
+        issue_km(set0, ktop - 1);
+        issue_v(set0, ktop - 1);
+    } else {
+        issue_v(set0, ktop);
+        if (ktop >= 1) {
+            issue_km(set1, ktop - 1);
+            issue_v(set1, ktop - 1);
+        }
+    }
+    wait_vmem();
+    __syncthreads();
+    f32x16 s[2];
+    bf16x8 opm[8];
+    if (ktop > 0) {
         // copies of the phase loop, issued out of the compiler's sight (it
         // would otherwise pair a copy issued on one role's path with a read
         // on the other's and wait for it); each wave waits for its own.
@@ -1183,24 +899,18 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
                 if (lane == 0) dma_lds4(csg + kc, 0, sg.loc + C);
             }
         };
-        // the first matrix phase has no pending probabilities: its PV product
-        // adds zero (P = 0 against the V tile of chunk q0, which is staged)
-        f32x16 s[2];
-        bf16x8 pB[4], opm[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pB[i] = bf16x8{};
-        const bool go = active;
         if (!leader) {
-            if (q0 >= 2) kissue(set0, q0 - 2);
+            if (ktop >= 2) kissue((ktop & 1) ? set1 : set0, ktop - 2);
             phase_barrier();
         }
         auto iter = [&](int k, const Stage<D>& ck, const Stage<D>& cn) {
             // ck: chunk k and V(k); cn: chunk k +- 1 and V(k +- 1).  Chunks
-            // left of q0 are full, so V is copied without a guard.
+            // below ktop are full, so V is copied without a guard.
             if (leader) {
                 if (k >= 1) kissue(cn, k - 1);
-                if (k < q0 - 1) dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
+                if (k < ktop - 1) dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
             }
+            const bool go = active && k < qc;
             if (go) pp_mphase<GATE, true>(st, s, pB, opm, ck, cn.v, l32, hh);
             if (!leader) wait_vmem();
             phase_barrier();
@@ -1212,13 +922,19 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
             if (leader) wait_vmem();
             phase_barrier();
         };
-        for (int k = q0 - 1; k >= 0; k -= 2) {     // k odd, then k - 1 even
+        int k = ktop - 1;
+        if ((k & 1) == 0) {           // k even: one step to reach the odd/even pairs
+            iter(k, set0, set1);
+            --k;
+        }
+        for (; k >= 0; k -= 2) {     // k odd, then k - 1 even
             iter(k, set1, set0);
             iter(k - 1, set0, set1);
         }
-        if (go) pp_mphase<GATE, false>(st, s, pB, opm, set0, set0.v, l32, hh);
-        if (leader) phase_barrier();
     }
+    // PV(0) with the pending probabilities (the own chunk's, for qc = 0)
+    if (active) pp_mphase<GATE, false>(st, s, pB, opm, set0, set0.v, l32, hh);
+    if (ktop > 0 && leader) phase_barrier();
     scan_store<D, GATE>(a, st, u, hh);
     };
 

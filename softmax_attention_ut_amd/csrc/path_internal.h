@@ -14,6 +14,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -51,6 +52,14 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), laid out like ut (cache only)
 //     mt  [BH][N][D][D] bf16  -M^T, M = W^T U: [rho][d'] = -M[d'][permk(rho)]
 //                             (d = 64 forward only: dense d x d transport)
+//   The d = 64 forward has no ut / yt: its prepare stage also takes each
+//   query chunk's own-chunk (diagonal) step and writes instead
+//     qt  [BH][Lp][D]  bf16  the query carried to its chunk start,
+//                            q - lower(q W^T) U, times scale*log2(e)
+//     pd  [BH][Lp][C]  bf16  the query's own-chunk probabilities
+//                            exp2(z_ij - m_i), in the scan's B-operand
+//                            register order (see path_ut_bf16.hip)
+//     ml  [BH][Lp][2]  f32   (m_i, l_i): their maximum (log2 units) and sum
 //   Permuting the d rows of the transposed tiles makes the fp32 accumulators
 //   they multiply into (carried query, output) come out with register 8s+t
 //   holding d = 16s + 8*(lane/32) + t, i.e. in natural B-operand order.
@@ -61,7 +70,7 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     csum [BH][N]  f32  sum over the chunk of log2 f_s
 // ---------------------------------------------------------------------------
 struct Workspace {
-    size_t kt, ut, vt, yt, zt, mt, loc, csum, gb, total;
+    size_t kt, ut, vt, yt, zt, mt, loc, csum, gb, qt, pd, ml, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -79,12 +88,17 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     const size_t es = bf16_mode ? 2 : 4;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    // the d = 64 forward: own-chunk step in the prepare stage (no ut / yt)
+    const bool diag = !with_z && dense_transport(D, bf16_mode);
     w.kt = take(BH * Lp * D * es);
-    w.ut = take(BH * Lp * D * es);
+    w.ut = diag ? 0 : take(BH * Lp * D * es);
     w.vt = (bf16_mode && D != 64) ? take(BH * Lp * D * es) : 0;
-    w.yt = take(BH * N * C * C * es);
+    w.yt = diag ? 0 : take(BH * N * C * C * es);
     w.zt = with_z ? take(BH * Lp * D * es) : 0;
-    w.mt = (!with_z && dense_transport(D, bf16_mode)) ? take(BH * N * D * D * es) : 0;
+    w.mt = diag ? take(BH * N * D * D * es) : 0;
+    w.qt = diag ? take(BH * Lp * D * es) : 0;
+    w.pd = diag ? take(BH * Lp * C * es) : 0;
+    w.ml = diag ? take(BH * Lp * 2 * 4) : 0;
     w.loc = gate ? take(BH * Lp * 4) : 0;
     w.csum = gate ? take(BH * N * 4) : 0;
     // d x d transport with the gate: each key's gate term as the A row of the
@@ -98,6 +112,8 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
 // Kernel argument blocks.
 // ---------------------------------------------------------------------------
 struct UtArgs {
+    const void* q;         // d = 64 forward: queries of the own-chunk step (else null)
+    float scale2;          // scale * log2(e) (own-chunk step)
     const void* k;
     const void* v;
     const void* w;
@@ -113,6 +129,9 @@ struct UtArgs {
     float* loc;            // null without gate
     float* csum;
     void* gb;              // may be null (gate bias rows, d x d transport)
+    void* qt;              // d = 64 forward: own-chunk step outputs (else null)
+    void* pd;
+    float* ml;
 };
 
 struct FwdArgs {
@@ -128,6 +147,9 @@ struct FwdArgs {
     const float* loc;
     const float* csum;
     const void* gb;        // d = 64 with gate: bias rows of the key chunks
+    const void* qt;        // d = 64: own-chunk step results of the prepare stage
+    const void* pd;
+    const float* ml;
     void* out;
     float* lse;
     int BH, L, N, C, D, nqb;

@@ -21,14 +21,20 @@
 //                  (optional; the d = 64 scan carries queries with it)
 // plus the chunk-local forget-gate sums.
 //
+// The d = 64 forward instance (DIAG) also takes each query chunk's step with
+// its own chunk (phase 4 below) and writes the carried query, the pending
+// probabilities and their maximum and sum instead of ut and yt.
+//
 // Arithmetic.  G = W W^T and R = W K^T are bf16 MFMAs with fp32
-// accumulation (exact products of the bf16 inputs).  T^{-1} is formed in
-// fp32 by forward substitution, one lane per column,
-//     T^{-1}[m][n] = beta_m (delta_mn - sum_{p<m} G[m][p] T^{-1}[p][n]),
-// the column held in registers.  Products with the fp32 factors T^{-1}, R
-// and Y use a two-term bf16 split x = hi + lo (hi = bf16(x),
-// lo = bf16(x - hi)), so they carry ~16 significant bits before the final
-// bf16 rounding of the stored result.
+// accumulation (exact products of the bf16 inputs).  T^{-1} =
+// (I + strictLower(D G))^{-1} D is formed in fp32, blocked by 16: the four
+// diagonal 16-blocks by forward substitution (one lane per column,
+//     X[m][n] = beta_m (delta_mn - sum_{p<m} G[m][p] X[p][n]),
+// four blocks at once on one wave), the off-diagonal blocks from 16x16x4
+// fp32 MFMA products of the blocks already known.  Products with the fp32
+// factors T^{-1}, R and Y use a two-term bf16 split x = hi + lo
+// (hi = bf16(x), lo = bf16(x - hi)), so they carry ~16 significant bits
+// before the final bf16 rounding of the stored result.
 #include "path_internal.h"
 
 #include <type_traits>
@@ -71,12 +77,29 @@ __device__ __forceinline__ bf16x8 cvt8(const f32x16& acc, int half, float sign) 
     return r;
 }
 
+// max / sum of a value with the lane 32 positions away (the two lane halves
+// hold the two key halves of one query column)
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace
 
 // Three workgroups per CU where LDS allows it (d = 64 without Z: 46 KB, held
 // to 136 VGPRs by the bound); the other instances need more LDS per workgroup.
-template <int D, bool WITH_Z>
+//
+// DIAG (d = 64 forward): the chunk's own-chunk step of the scan is taken here
+// too, for its 64 queries (phase 4 below): the query carried to the chunk
+// start and the probabilities of the chunk's own keys, with their maximum and
+// sum.  U and Y then stay on chip (they serve no other step).
+template <int D, bool WITH_Z, bool DIAG>
 __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf16_kernel(const UtArgs a) {
+    static_assert(!DIAG || (D == 64 && !WITH_Z), "the own-chunk step is a d = 64 forward stage");
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
     constexpr int PT = C + 8;     // pitch of [x][token-slot] bf16 tiles
@@ -99,6 +122,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     __shared__ __attribute__((aligned(16))) bf16 sZh[WITH_Z ? C * PT : 8];  // T^{-T} rows, m slots
     __shared__ __attribute__((aligned(16))) bf16 sZl[WITH_Z ? C * PT : 8];
     __shared__ float sB[C];
+    __shared__ __attribute__((aligned(16))) float sLoc[DIAG ? C : 4];   // -local log2 gate prefix (0 without gate)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -110,6 +134,19 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     const size_t chunkbase = (size_t)head * N + c;
 
     float lf_in = 0.f;
+    // DIAG: the queries of phase 4 (wave w: rows 32 (w & 1) .. +31, as the
+    // B operand of k-step ks: d = 16 ks + 8 hh .. +7), loaded with the stage
+    // (a load issued later would be waited for behind phase 3's stores)
+    bf16x8 qv[KSD];
+    if (DIAG) {
+        const int iq = 32 * (wave & 1) + l32;
+        const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)head * L + p0 + iq) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+            qv[ks] = bf16x8{};
+            if (iq < nvalid) qv[ks] = ld8(qrow + 16 * ks + 8 * hh);
+        }
+    }
     // ---- phase 0: stage W, K (rows), W^T (token slots), beta.  Every load
     // is issued before the first LDS write, so the stage waits for memory
     // once. ----
@@ -203,6 +240,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             for (int t = 0; t < 8; ++t) col[t] = sV[permk(s0 + t) * PW + e];
             *reinterpret_cast<bf16x8*>(vt + (size_t)rho * C + s0) = col;
         }
+        if (DIAG && wave == 1 && !a.loc) sLoc[lane] = 0.f;
         if (wave == 1 && a.loc) {
             // forget gate: chunk-local suffix sums in log2 units, fp64.  Lane s
             // holds log2 f_s; an inclusive suffix scan over the 64 lanes gives
@@ -216,6 +254,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             }
             const float loc = static_cast<float>(-(x - lf));
             a.loc[rowbase + lane] = loc;
+            if (DIAG) sLoc[lane] = loc;
             if (lane == 0) a.csum[chunkbase] = static_cast<float>(x);
             if (a.gb) {
                 // the key's gate term -loc as the A row of the scan's bias
@@ -322,6 +361,9 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     __syncthreads();
 
     // ---- phase 3 ----
+    // DIAG: the Y^T rows (waves 0, 1) and -U^T rows (waves 2, 3) are kept in
+    // registers for phase 4 instead of being stored.
+    bf16x8 keep[4];
     // R, Y and T^{-1} are triangular: tiles and k-steps that only meet their
     // zero blocks are skipped (key tile jt is wave-uniform, a compile-time
     // case each).
@@ -365,13 +407,15 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
                 yacc[mb] = mfma(al, rh[ks], yacc[mb]);
             }
         }
-        // store Y^T[j][m-slot]
-        bf16* yrow = static_cast<bf16*>(a.yt) + (chunkbase * C + j) * C;
+        // store Y^T[j][m-slot] (DIAG: keep it for phase 4)
+        bf16* yrow = DIAG ? nullptr : static_cast<bf16*>(a.yt) + (chunkbase * C + j) * C;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
+            for (int s2 = 0; s2 < 2; ++s2) {
+                if (DIAG) keep[2 * mb + s2] = cvt8(yacc[mb], s2, -1.f);   // -Y^T
+                else *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
+            }
         // K~^T[d][j] = K^T[d][j] - sum_{m > j} W^T[d][m] Y[m][j]
         bf16x8 yh[4], yl[4];
 #pragma unroll
@@ -422,12 +466,14 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
                     uacc[mt] = mfma(ld8(tl + 16 * ks), w8, uacc[mt]);
                 }
             }
-            bf16* urow = static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
+            bf16* urow = DIAG ? nullptr : static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc[mt], s2, -1.f);
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    if (DIAG) keep[2 * mt + s2] = cvt8(uacc[mt], s2, -1.f);
+                    else *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc[mt], s2, -1.f);
+                }
             if (a.mt) {
                 // M = W^T U (d x d): the whole chunk's transition product is
                 // I - M in row-vector form.  The U accumulator's column is
@@ -475,17 +521,153 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             }
         }
     }
+    if constexpr (DIAG) {
+        // ---- phase 4: the chunk's own-chunk step for its 64 queries ----
+        // (Chinese notes, training strategy: the full-matrix form of a block;
+        // Dutch summary section 3: boundary-adjusted queries.)  For query i and
+        // key j <= i of the chunk, with X = Q W^T:
+        //     S = Q K^T - lower(X) Y          (= Q K~^T + strictUpper(X) Y)
+        //     q~ = q - lower(X) U             (query carried to the chunk start)
+        // in the scan's transposed orientation (S^T = K Q^T - Y^T lower(X)^T,
+        // q~^T = Q^T + (-U^T) lower(X)^T), lower(X)^T coming out of the X^T
+        // accumulator as the B operand over m.  Y^T and -U^T go over the T^{-1}
+        // tiles, which are no longer read.
+        bf16* const sYt = sTh;      // -Y^T rows j, m in slots
+        bf16* const sUt = sTl;      // -U^T rows rho, m in slots
+        __syncthreads();
+        {
+            bf16* dst = (wave < 2 ? sYt : sUt) + (32 * (wave & 1) + l32) * PT;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    *reinterpret_cast<bf16x8*>(dst + 32 * b + 16 * s2 + 8 * hh) = keep[2 * b + s2];
+        }
+        __syncthreads();
+        // wave w: query tile QT = w & 1 (rows 32 QT .. +31), role w >> 1 (0: the
+        // probabilities, 1: the carried query).  Rows m (and keys j) of the
+        // tiles above the query tile meet only the zero part of lower(X) (and
+        // the mask), so those products are skipped: a compile-time case each.
+        auto own = [&](auto qtc, auto rolec) {
+            constexpr int QT = decltype(qtc)::value, ROLE = decltype(rolec)::value;
+            constexpr int KM = 2 * (QT + 1);        // k-steps over m that meet lower(X)
+            const int iloc = 32 * QT + l32;
+            const size_t row = rowbase + iloc;
+            f32x16 x[2];
+#pragma unroll
+            for (int kt2 = 0; kt2 <= QT; ++kt2) {
+                zero(x[kt2]);
+#pragma unroll
+                for (int ks = 0; ks < KSD; ++ks)
+                    x[kt2] = mfma(ld8(sW + (32 * kt2 + l32) * PW + 16 * ks + 8 * hh), qv[ks], x[kt2]);
+            }
+            // lower(X)^T: rows m <= i
+            bf16x8 xl[KM];
+#pragma unroll
+            for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int v = 8 * (ks & 1) + t;
+                    const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
+                    xl[ks][t] = static_cast<bf16>(m <= iloc ? x[ks >> 1][v] : 0.f);
+                }
+            if constexpr (ROLE == 0) {
+                // S^T = K Q^T + (-Y^T) lower(X)^T for key tiles kt2 <= QT
+                f32x16 s[2];
+#pragma unroll
+                for (int kt2 = 0; kt2 <= QT; ++kt2) {
+                    zero(s[kt2]);
+#pragma unroll
+                    for (int ks = 0; ks < KSD; ++ks)
+                        s[kt2] = mfma(ld8(sK + (32 * kt2 + l32) * PW + 16 * ks + 8 * hh), qv[ks], s[kt2]);
+#pragma unroll
+                    for (int ks = 0; ks < KM; ++ks)
+                        s[kt2] = mfma(ld8(sYt + (32 * kt2 + l32) * PT + 16 * ks + 8 * hh), xl[ks], s[kt2]);
+                }
+                // z = scale log2(e) S + log2 prod_{s=j+1}^{i} f_s  (= loc_i - loc_j,
+                // zero without the gate), causal mask j <= i (key tile QT only);
+                // lane: keys j = 32 kt2 + 8 (v/4) + 4 hh + v%4, four consecutive
+                // per group
+                const float li = sLoc[iloc];
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kt2 = 0; kt2 <= QT; ++kt2)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 lj = *reinterpret_cast<const f32x4*>(sLoc + 32 * kt2 + 8 * g + 4 * hh);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const int v = 4 * g + c;
+                            const int j = 32 * kt2 + 8 * g + 4 * hh + c;
+                            float z = fmaf(s[kt2][v], a.scale2, li - lj[c]);
+                            if (kt2 == QT && j > iloc) z = -INFINITY;
+                            s[kt2][v] = z;
+                            mx = fmaxf(mx, z);
+                        }
+                    }
+                mx = pair_max(mx);
+                // probabilities as the scan's PV B operand: register ks holds the
+                // accumulator registers 8 (ks & 1) .. +7 of key tile ks >> 1 (zero
+                // above the query tile); the row sum is taken over the rounded
+                // values the PV product uses
+                const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+                float psum = 0.f;
+                bf16* prow = static_cast<bf16*>(a.pd) + row * C;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 p8 = {};
+                    if ((ks >> 1) <= QT) {
+#pragma unroll
+                        for (int t = 0; t < 8; ++t)
+                            p8[t] = static_cast<bf16>(__builtin_amdgcn_exp2f(s[ks >> 1][8 * (ks & 1) + t] - mx));
+#pragma unroll
+                        for (int t = 0; t < 8; t += 2)
+                            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p8[t], p8[t + 1]}, ones, psum, false);
+                    }
+                    *reinterpret_cast<bf16x8*>(prow + 16 * ks + 8 * hh) = p8;
+                }
+                psum = pair_sum(psum);
+                if (hh == 0) *reinterpret_cast<f32x2*>(a.ml + 2 * row) = f32x2{mx, psum};
+            } else {
+                // q~^T = Q^T + (-U^T) lower(X)^T, then times scale log2(e)
+                f32x16 qacc[2];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(qv[ks][t]);
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                    for (int ks = 0; ks < KM; ++ks)
+                        qacc[dt] = mfma(ld8(sUt + (32 * dt + l32) * PT + 16 * ks + 8 * hh), xl[ks], qacc[dt]);
+                // register 8 s + t of tile dt holds d = 32 dt + 16 s + 8 hh + t
+                bf16* qrow = static_cast<bf16*>(a.qt) + row * D;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks)
+                    *reinterpret_cast<bf16x8*>(qrow + 16 * ks + 8 * hh) = cvt8(qacc[ks >> 1], ks & 1, a.scale2);
+            }
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        switch (__builtin_amdgcn_readfirstlane(wave)) {
+            case 0: own(I0{}, I0{}); break;
+            case 1: own(I1{}, I0{}); break;
+            case 2: own(I0{}, I1{}); break;
+            default: own(I1{}, I1{}); break;
+        }
+    }
 }
 
 hipError_t launch_path_ut_bf16(const UtArgs& a, hipStream_t s) {
     const dim3 grid(a.BH * a.N), block(256);
     const bool z = a.zt != nullptr;
     if (a.D == 64) {
-        if (z) hipLaunchKernelGGL((path_ut_bf16_kernel<64, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_ut_bf16_kernel<64, false>), grid, block, 0, s, a);
+        if (z) hipLaunchKernelGGL((path_ut_bf16_kernel<64, true, false>), grid, block, 0, s, a);
+        else if (a.qt) hipLaunchKernelGGL((path_ut_bf16_kernel<64, false, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((path_ut_bf16_kernel<64, false, false>), grid, block, 0, s, a);
     } else if (a.D == 128) {
-        if (z) hipLaunchKernelGGL((path_ut_bf16_kernel<128, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_ut_bf16_kernel<128, false>), grid, block, 0, s, a);
+        if (z) hipLaunchKernelGGL((path_ut_bf16_kernel<128, true, false>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((path_ut_bf16_kernel<128, false, false>), grid, block, 0, s, a);
     } else {
         return hipErrorInvalidValue;
     }
