@@ -12,7 +12,8 @@ d128_L8k_decode the step is one decode step (in-place key-cache update +
 one-token attention) and the 256 steps after that prefill are timed.  With
 --workload transition_L4k the step is one path_transition_prep launch (w and
 beta of every token from the layer input; B=8, L=4096, width 1536, rank 64,
-H=24, d=64).
+H=24, d=64).  With --workload d128_L8k_kcache the step is one prefill ->
+decode key-cache hand-off (path_kcache_from_prefill) after that prefill.
 
 Prints one JSON line: effective TFLOP/s (2*B*H*L^2*d per forward), tokens/s,
 the roofline of the dominant kernel (HIP events on its launch stream) and the
@@ -324,6 +325,74 @@ def bench_decode(args, cfg, torch, pa, inputs):
     return res, None
 
 
+def kcache_bytes_flops(B, H, L, d, C=64, G=8):
+    """Algorithmic HBM bytes and FLOPs of one prefill -> decode key-cache
+    hand-off: read k, w, v (bf16) and beta, write the key and value caches'
+    L slots; the UT work of every chunk (G, T^{-1}, Z, R, Y, K~: about
+    N (8 C^2 d + 4 C^3)), the carry of every key to its group's end and of
+    the d identity rows through the group (4 C^2 d per chunk passed), the
+    suffix products of the group products (2 d^3 per group) and the product
+    of every key with its group's suffix (2 d^2 per key), per head."""
+    N = (L + C - 1) // C
+    NG = (N + G - 1) // G
+    nbytes = B * H * (5 * L * d * 2 + L * 4)
+    carries = NG * (G * (G - 1) / 2 + G * d / C)     # chunk passes of 64 rows
+    flops = B * H * (N * (8.0 * C * C * d + 4.0 * C ** 3) + carries * 4.0 * C * C * d
+                     + (NG - 1) * 2.0 * d ** 3 + L * 2.0 * d * d)
+    return nbytes, flops
+
+
+def bench_kcache(args, cfg, torch, pa, inputs):
+    """The prefill -> decode hand-off of a prefill + decode workload: the key
+    cache H_{L-1} ... H_{j+1} k_j and the value cache after a prefill of L
+    tokens, one path_kcache_from_prefill per step."""
+    inp = inputs.generate_config(cfg)
+    B, H, L, d, T = cfg.B, cfg.H, cfg.L, cfg.d, cfg.L_total
+    g = {k: (None if t is None else t[:, :, :L].contiguous().cuda()) for k, t in vars(inp).items()}
+    ws = torch.empty(pa.path_kcache_workspace_bytes(B, H, L, d, pa.PATH_BF16), dtype=torch.uint8,
+                     device="cuda")
+    kc = torch.zeros(B, H, T, d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.path_kcache_from_prefill(g["k"], g["v"], g["w"], g["beta"], kc, vc, ws, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    nbytes, flops = kcache_bytes_flops(B, H, L, d)
+    gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    res = {
+        "metric": "PaTH prefill -> decode key-cache hand-off: ms and HBM GB/s",
+        "value": ev_ms, "unit": "ms per hand-off (HIP events)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_kcache: key and value caches after a prefill of "
+                               f"L={L}, B={B} H={H} d={d}, bf16",
+                   "global_batch": B, "seq_len": L, "parallelism": "single GPU"},
+        "tflops": flops / (ev_ms * 1e-3) / 1e12,
+        "roofline": {"kernel": f"path_kcache_from_prefill: path_ut_bf16_kernel<{d}, true, false> "
+                               f"+ path_kcache_group/suffix/apply_kernel<{d}>",
+                     "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "algorithmic_flops_per_launch": flops},
+    }
+    return res, None
+
+
 def transition_bytes_flops(cfg):
     """Algorithmic HBM bytes and FLOPs of one path_transition_prep launch:
     read x (bf16) once and the weights once, write w (bf16) and beta (fp32);
@@ -465,6 +534,11 @@ def main():
         res, inp = bench_transition(args, cfg, torch, pa, inputs)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = transition_cpu_baseline(inp, cfg, args.cpu_threads or default_cpu_threads())
+        print(json.dumps(res), flush=True)
+        return
+    if args.workload.endswith("_kcache"):
+        cfg = inputs.CONFIGS[args.workload[:-len("_kcache")] + "_decode"]
+        res, _ = bench_kcache(args, cfg, torch, pa, inputs)
         print(json.dumps(res), flush=True)
         return
     cfg = inputs.CONFIGS[args.workload]

@@ -194,14 +194,15 @@ static int kcache_from_prefill(const void* k, const void* v, const void* w, cons
     u.k = k; u.v = v; u.w = w; u.beta = beta; u.log_f = nullptr;
     u.BH = BH; u.L = L; u.N = N; u.C = chunk; u.D = d;
     u.kt = at(workspace, ws.kt);
-    u.ut = at(workspace, ws.ut);
-    u.vt = ws.vt ? at(workspace, ws.vt) : nullptr;
-    u.yt = at(workspace, ws.yt); u.zt = at(workspace, ws.zt);
+    u.zt = at(workspace, ws.zt);            // the hand-off needs K~ and Z only
     if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
     KcacheArgs c{};
     c.kt = u.kt; c.w = w; c.zt = u.zt; c.v = v;
     c.k_cache = k_cache; c.v_cache = v_cache;
     c.BH = BH; c.L = L; c.N = N; c.T_max = T_max;
+    c.NG = (N + kKcacheGroup - 1) / kKcacheGroup;
+    c.tg = reinterpret_cast<float*>(at(workspace, ws.tg));
+    c.rg = at(workspace, ws.rg);
     c.map = map;
     return launch_path_kcache(c, d, s) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
 }

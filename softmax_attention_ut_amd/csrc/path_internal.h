@@ -69,8 +69,11 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     loc  [BH][Lp] f32  -sum_{s=j+1}^{chunk end} log2 f_s
 //     csum [BH][N]  f32  sum over the chunk of log2 f_s
 // ---------------------------------------------------------------------------
+// Chunks per group of the key-cache hand-off's suffix products.
+constexpr int kKcacheGroup = 8;
+
 struct Workspace {
-    size_t kt, ut, vt, yt, zt, mt, loc, csum, gb, qt, pd, ml, total;
+    size_t kt, ut, vt, yt, zt, mt, loc, csum, gb, qt, pd, ml, tg, rg, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -89,12 +92,16 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
     // the d = 64 forward: own-chunk step in the prepare stage (no ut / yt)
+    // the key-cache hand-off (with_z): kt, zt and the group products only
     const bool diag = !with_z && dense_transport(D, bf16_mode);
+    const size_t NG = (N + kKcacheGroup - 1) / kKcacheGroup;
     w.kt = take(BH * Lp * D * es);
-    w.ut = diag ? 0 : take(BH * Lp * D * es);
-    w.vt = (bf16_mode && D != 64) ? take(BH * Lp * D * es) : 0;
-    w.yt = diag ? 0 : take(BH * N * C * C * es);
+    w.ut = (diag || with_z) ? 0 : take(BH * Lp * D * es);
+    w.vt = (bf16_mode && D != 64 && !with_z) ? take(BH * Lp * D * es) : 0;
+    w.yt = (diag || with_z) ? 0 : take(BH * N * C * C * es);
     w.zt = with_z ? take(BH * Lp * D * es) : 0;
+    w.tg = with_z ? take(BH * NG * D * D * 4) : 0;
+    w.rg = with_z ? take(BH * NG * 2 * D * D * 2) : 0;
     w.mt = diag ? take(BH * N * D * D * es) : 0;
     w.qt = diag ? take(BH * Lp * D * es) : 0;
     w.pd = diag ? take(BH * Lp * C * es) : 0;
@@ -175,13 +182,15 @@ __device__ __forceinline__ long long cache_row(const CacheMap& c, int bh, int j)
 }
 
 struct KcacheArgs {
-    const void* kt;        // keys carried to their chunk end (bf16, d permuted)
+    void* kt;              // keys carried to their chunk end (bf16), then to their group's end
     const void* w;         // input w [BH][L][D]
     const void* zt;
     const void* v;         // input values [BH][L][D]
     void* k_cache;         // contiguous [BH][T_max][D] or a page pool (see map)
     void* v_cache;
-    int BH, L, N, T_max;
+    int BH, L, N, T_max, NG;   // NG = ceil(N / kKcacheGroup)
+    float* tg;             // [BH][NG][D][D] fp32: each group's product of chunk transforms
+    void* rg;              // [BH][NG][2][D][D] bf16: suffix products, rows permuted, hi and lo
     CacheMap map;
 };
 

@@ -1,17 +1,33 @@
 // path_kcache: transformed key cache after a prefill of L tokens (gfx950).
 //
-// The inference form keeps every cached key already carried to "now":
-// after token L-1 the cache holds H_{L-1} ... H_{j+1} k_j (Dutch summary
-// section 3, "Inferentie"; Chinese notes, inference paragraph).  Per chunk
-// b, path_ut gives k~_j = H_{end(b)} ... H_{j+1} k_j; this kernel carries
-// every key chunk through each later chunk c = b+1 .. N-1 with the chunk's
-// UT form, in row-vector form
-//     k^T <- k^T - (k^T W_c^T) Z_c,    Z_c = T_c^{-T} W_c,
-// which is (H_{end(c)} ... H_{start(c)}) k.  Layout and MFMA orientation are
-// those of the query transport in path_fwd (the key rides in fp32
-// accumulators, K^T -= Z^T X^T with X^T = W K^T; -Z^T comes from path_ut with
-// its token axis in k-slot order and its d rows permuted, so the key's
-// registers hold d in natural order).
+// The inference form keeps every cached key already carried to "now": after
+// token L-1 the cache holds H_{L-1} ... H_{j+1} k_j (Dutch summary section 3,
+// "Inferentie"; Chinese notes, inference paragraph).  Per chunk b, path_ut
+// gives k~_j = H_{end(b)} ... H_{j+1} k_j.  In row-vector form a chunk c
+// acts on a key as
+//     k^T <- k^T P_c,   P_c = I - W_c^T Z_c,   Z_c = T_c^{-T} W_c
+// (the chunk's UT form), so the cached key is k~_j^T P_{b+1} ... P_{N-1}.
+//
+// The product of the later chunks is formed by suffix products over groups of
+// G = 8 chunks, O(L d^2) work in all (instead of carrying every key through
+// every later chunk, O(L^2 d)):
+//   1. path_kcache_group_kernel, per (head, group g): every key chunk b of
+//      the group carried to the group's end, Y_b = K~_b P_{b+1} ... P_{end(g)}
+//      (written over K~), and the group's product T_g = P_{start(g)} ...
+//      P_{end(g)}, whose rows are the d identity rows carried through the
+//      group (fp32);
+//   2. path_kcache_suffix_kernel, per head, right to left over the groups:
+//      R_{last} = I, R_g = T_{g+1} R_{g+1};
+//   3. path_kcache_apply_kernel, per (head, group): K_cache_b = Y_b R_g for
+//      the group's chunks, and V_cache = V.
+// The carry (step 1) uses the query transport's layout and MFMA orientation
+// (the key rides in fp32 accumulators, K^T -= Z^T X^T with X^T = W K^T; -Z^T
+// comes from path_ut with its token axis in k-slot order and its d rows
+// permuted, so the key's registers hold d in natural order).  Steps 2 and 3
+// keep R_g as R_g^T with permuted rows, Rp[rho][c] = R_g[c][permk(rho)], in
+// two bf16 terms (hi, lo): Rp is the A operand of both products, which then
+// carry ~16 significant bits, and the output registers again hold d in
+// natural order.
 #include "path_internal.h"
 
 namespace path {
@@ -29,11 +45,13 @@ __device__ __forceinline__ bf16x8 pack8k(const f32x16& acc, int half) {
     return r;
 }
 
-template <int C, int D, int PITCH>
+__device__ __forceinline__ bf16x8 ld8k(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+template <int C, int D, int PITCH, int NT = 256>
 __device__ __forceinline__ void stage_rows_k(bf16* dst, const bf16* src, int nvalid, int tid) {
     constexpr int UPR = D / 8;
 #pragma unroll
-    for (int u = tid; u < C * UPR; u += 256) {
+    for (int u = tid; u < C * UPR; u += NT) {
         const int r = u / UPR, d0 = (u % UPR) * 8;
         uint4 val = {0u, 0u, 0u, 0u};
         if (r < nvalid) val = *reinterpret_cast<const uint4*>(src + (size_t)r * D + d0);
@@ -41,12 +59,12 @@ __device__ __forceinline__ void stage_rows_k(bf16* dst, const bf16* src, int nva
     }
 }
 
-template <int ROWS, int COLS, int PITCH>
+template <int ROWS, int COLS, int PITCH, int NT = 256>
 __device__ __forceinline__ void stage_tile_k(bf16* dst, const bf16* src, int tid) {
     constexpr int UPR = COLS / 8;
     constexpr int UNITS = ROWS * UPR;
 #pragma unroll
-    for (int u = tid; u < UNITS; u += 256) {
+    for (int u = tid; u < UNITS; u += NT) {
         const int r = u / UPR, c8 = u % UPR;
         *reinterpret_cast<uint4*>(dst + r * PITCH + c8 * 8) =
             *reinterpret_cast<const uint4*>(src + (size_t)u * 8);
@@ -55,56 +73,66 @@ __device__ __forceinline__ void stage_tile_k(bf16* dst, const bf16* src, int tid
 
 }  // namespace
 
+// Step 1.  Workgroup p of group g (8 waves) holds four row chunks of 64
+// rows, two waves each: row chunk rc = -D/64 + 4p + (wave >> 1); rc >= 0 is
+// the key chunk start(g) + rc, rc < 0 a block of 64 identity rows (entering
+// before the group's first chunk).  The workgroup walks the group's chunks
+// from the first one any of its row chunks passes; a row chunk is carried
+// through those after its own chunk.
 template <int D>
-__global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
-    constexpr int C = 64, PK = D + 8, PC = C + 8;
+__global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs a) {
+    constexpr int C = 64, PK = D + 8, PC = C + 8, G = kKcacheGroup, NID = D / 64, NT = 512;
     constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
+    constexpr int NP = (G + NID + 3) / 4;
     __shared__ __attribute__((aligned(16))) bf16 sW[C * PK];
     __shared__ __attribute__((aligned(16))) bf16 sZ[D * PC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int L = a.L, N = a.N, Lp = N * C;
-    const int nkb = (N + 1) / 2;
-    // lightest work last: key block 0 carries its keys through the most chunks
-    int head, kb;
-    {
-        const int bid = blockIdx.x;
-        if ((a.BH & 7) == 0) {
-            const int xcd = bid & 7, j = bid >> 3;
-            head = xcd + 8 * (j / nkb);
-            kb = j % nkb;
-        } else {
-            head = bid / nkb;
-            kb = bid % nkb;
-        }
-    }
-    const int kc_own = 2 * kb + (wave >> 1);
-    const bool active = kc_own < N;
+    const int L = a.L, N = a.N, Lp = N * C, NG = a.NG;
+    const int head = blockIdx.x / (NG * NP);
+    const int g = (blockIdx.x / NP) % NG, p = blockIdx.x % NP;
+    const int c0 = g * G, c1 = min(c0 + G, N) - 1;
+    const int rc = -NID + 4 * p + (wave >> 1);
     const int jloc = (wave & 1) * 32 + l32;
-    const int j = kc_own * C + jloc;
+    const int kc = c0 + rc;                       // key chunk (rc >= 0)
+    const bool active = rc < 0 || kc <= c1;
+    const int start = rc < 0 ? c0 : kc + 1;       // first chunk this row chunk passes
+    const int cfirst = c0 + max(-NID + 4 * p + 1, 0);   // first chunk the workgroup needs
 
-    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
+    bf16* kt = static_cast<bf16*>(a.kt) + (size_t)head * Lp * D;
     const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
     const bf16* zt = static_cast<const bf16*>(a.zt) + (size_t)head * N * D * C;
 
+    // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t
     f32x16 kacc[DT];
     bf16x8 kB[KSD];
-    if (active) {
-        const bf16* krow = kt + (size_t)j * D;
+    if (rc >= 0 && active) {
+        const bf16* krow = kt + ((size_t)kc * C + jloc) * D;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-            kB[ks] = *reinterpret_cast<const bf16x8*>(krow + 16 * ks + 8 * hh);
+            kB[ks] = ld8k(krow + 16 * ks + 8 * hh);
 #pragma unroll
             for (int t = 0; t < 8; ++t) kacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(kB[ks][t]);
         }
+    } else {
+        const int r = (rc + NID) * C + jloc;      // identity row r
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float e = (16 * ks + 8 * hh + t == r) ? 1.f : 0.f;
+                kacc[ks >> 1][8 * (ks & 1) + t] = e;
+                kB[ks][t] = static_cast<bf16>(e);
+            }
+        }
     }
-    for (int c = 2 * kb + 1; c < N; ++c) {
+    for (int c = cfirst; c <= c1; ++c) {
         __syncthreads();
-        stage_rows_k<C, D, PK>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
-        stage_tile_k<D, C, PC>(sZ, zt + (size_t)c * D * C, tid);
+        stage_rows_k<C, D, PK, NT>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
+        stage_tile_k<D, C, PC, NT>(sZ, zt + (size_t)c * D * C, tid);
         __syncthreads();
-        if (!active || c <= kc_own) continue;
+        if (!active || c < start) continue;
         f32x16 x[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
@@ -112,8 +140,7 @@ __global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
             for (int v = 0; v < 16; ++v) x[k2][v] = 0.f;
             const bf16* aw = sW + (32 * k2 + l32) * PK + 8 * hh;
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks)
-                x[k2] = mfma32k(*reinterpret_cast<const bf16x8*>(aw + 16 * ks), kB[ks], x[k2]);
+            for (int ks = 0; ks < KSD; ++ks) x[k2] = mfma32k(ld8k(aw + 16 * ks), kB[ks], x[k2]);
         }
         bf16x8 xB[KSC];
 #pragma unroll
@@ -122,34 +149,208 @@ __global__ __launch_bounds__(256) void path_kcache_kernel(const KcacheArgs a) {
         for (int dt = 0; dt < DT; ++dt) {
             const bf16* az = sZ + (32 * dt + l32) * PC + 8 * hh;
 #pragma unroll
-            for (int ks = 0; ks < KSC; ++ks)
-                kacc[dt] = mfma32k(*reinterpret_cast<const bf16x8*>(az + 16 * ks), xB[ks], kacc[dt]);
+            for (int ks = 0; ks < KSC; ++ks) kacc[dt] = mfma32k(ld8k(az + 16 * ks), xB[ks], kacc[dt]);
         }
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) kB[ks] = pack8k(kacc[ks >> 1], ks & 1);
     }
-    if (!active || j >= L) return;
-    // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t (the d rows
-    // of -Z^T are stored permuted for this)
-    const long long row = cache_row(a.map, head, j);
-    if (row < 0) return;
-    bf16* kout = static_cast<bf16*>(a.k_cache) + row * D;
+    if (!active) return;
+    if (rc >= 0) {
+        // Y_b over K~_b (the key rows are read once, at the start, by their own waves)
+        bf16* yrow = kt + ((size_t)kc * C + jloc) * D;
 #pragma unroll
-    for (int ks = 0; ks < KSD; ++ks)
-        *reinterpret_cast<bf16x8*>(kout + 16 * ks + 8 * hh) = pack8k(kacc[ks >> 1], ks & 1);
-    // values are copied unchanged, 4 bf16 per lane half
-    const bf16* vin = static_cast<const bf16*>(a.v) + ((size_t)head * L + j) * D;
-    bf16* vout = static_cast<bf16*>(a.v_cache) + row * D;
+        for (int ks = 0; ks < KSD; ++ks) *reinterpret_cast<bf16x8*>(yrow + 16 * ks + 8 * hh) = kB[ks];
+    } else {
+        // row r of T_g in fp32
+        float* trow = a.tg + (((size_t)head * NG + g) * D + (rc + NID) * C + jloc) * D;
 #pragma unroll
-    for (int e = 4 * hh; e < D; e += 8)
-        *reinterpret_cast<bf16x4*>(vout + e) = *reinterpret_cast<const bf16x4*>(vin + e);
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int v = 8 * (ks & 1) + 4 * q;
+                *reinterpret_cast<f32x4*>(trow + 16 * ks + 8 * hh + 4 * q) =
+                    f32x4{kacc[ks >> 1][v], kacc[ks >> 1][v + 1], kacc[ks >> 1][v + 2], kacc[ks >> 1][v + 3]};
+            }
+    }
+}
+
+// Step 2.  One workgroup per head.  Rp_g[rho][c] = sum_m Rp_{g+1}[rho][m]
+// T_{g+1}[c][m] is R_g[c][permk(rho)]: the A operand Rp_{g+1} (two bf16
+// terms, LDS) times the B operand T_{g+1} rows (fp32, split into two bf16
+// terms), three MFMAs per k-step (hi hi, hi lo, lo hi).  Wave w: output
+// columns c in tile w % (D/32), row tiles dt = w / (D/32) + i * 4 / (D/32)
+// (all (D/32)^2 tiles over the four waves).
+template <int D>
+__global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArgs a) {
+    constexpr int PR = D + 8, CT = D / 32, DTW = CT * CT / 4, STEP = 4 / CT, KSD = D / 16;
+    __shared__ __attribute__((aligned(16))) bf16 sRh[D * PR];
+    __shared__ __attribute__((aligned(16))) bf16 sRl[D * PR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int head = blockIdx.x, NG = a.NG;
+    const int ct = wave % CT, dt0 = wave / CT;
+    const int c = 32 * ct + l32;
+    bf16* rg = static_cast<bf16*>(a.rg) + (size_t)head * NG * 2 * D * D;   // [g][hi, lo][rho][c]
+
+    // R_{NG-1} = I: Rp[rho][c] = (c == permk(rho))
+    for (int u = tid; u < D * D; u += 256) {
+        const int rho = u / D, cc = u % D;
+        const bf16 e = static_cast<bf16>(cc == permk(rho) ? 1.f : 0.f);
+        sRh[rho * PR + cc] = e;
+        sRl[rho * PR + cc] = static_cast<bf16>(0.f);
+        bf16* out = rg + (size_t)(NG - 1) * 2 * D * D;
+        out[u] = e;
+        out[D * D + u] = static_cast<bf16>(0.f);
+    }
+    // B operand: row c of T_{g+1}, k = m = 16 ks + 8 hh .. +7 (fp32), loaded
+    // one step ahead
+    f32x4 tv[KSD][2];
+    auto load_t = [&](int gg) {
+        const float* trow = a.tg + (((size_t)head * NG + gg) * D + c) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int q = 0; q < 2; ++q) tv[ks][q] = *reinterpret_cast<const f32x4*>(trow + 16 * ks + 8 * hh + 4 * q);
+    };
+    if (NG >= 2) load_t(NG - 1);
+    for (int g = NG - 2; g >= 0; --g) {
+        __syncthreads();
+        bf16x8 bh[KSD], bl[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float x = tv[ks][t >> 2][t & 3];
+                bh[ks][t] = static_cast<bf16>(x);
+                bl[ks][t] = static_cast<bf16>(x - static_cast<float>(bh[ks][t]));
+            }
+        if (g >= 1) load_t(g);
+        f32x16 acc[DTW];
+#pragma unroll
+        for (int i = 0; i < DTW; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+#pragma unroll
+            for (int i = 0; i < DTW; ++i) {
+                const int rho = 32 * (dt0 + STEP * i) + l32;
+                const bf16x8 ah = ld8k(sRh + rho * PR + 16 * ks + 8 * hh);
+                const bf16x8 al = ld8k(sRl + rho * PR + 16 * ks + 8 * hh);
+                acc[i] = mfma32k(ah, bh[ks], acc[i]);
+                acc[i] = mfma32k(ah, bl[ks], acc[i]);
+                acc[i] = mfma32k(al, bh[ks], acc[i]);
+            }
+        }
+        __syncthreads();    // every wave has read Rp_{g+1}
+#pragma unroll
+        for (int i = 0; i < DTW; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rho = 32 * (dt0 + STEP * i) + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const float x = acc[i][v];
+                const bf16 h = static_cast<bf16>(x);
+                sRh[rho * PR + c] = h;
+                sRl[rho * PR + c] = static_cast<bf16>(x - static_cast<float>(h));
+            }
+        __syncthreads();
+        // Rp_g to global memory in 16-byte units
+        bf16* out = rg + (size_t)g * 2 * D * D;
+        for (int u = tid; u < D * D / 8; u += 256) {
+            const int rho = u / (D / 8), c8 = (u % (D / 8)) * 8;
+            *reinterpret_cast<bf16x8*>(out + (size_t)u * 8) = ld8k(sRh + rho * PR + c8);
+            *reinterpret_cast<bf16x8*>(out + D * D + (size_t)u * 8) = ld8k(sRl + rho * PR + c8);
+        }
+    }
+}
+
+// Step 3.  One workgroup per (head, group): K_cache^T = Rp_g Y^T for the
+// group's chunks (A: Rp_g, hi and lo, in LDS; B: Y rows, exact bf16), one key
+// tile of 32 per wave pair and d tiles split between the pair; values copied.
+template <int D>
+__global__ __launch_bounds__(256) void path_kcache_apply_kernel(const KcacheArgs a) {
+    constexpr int C = 64, PR = D + 8, DT = D / 32, KSD = D / 16, DTW = DT / 2;
+    __shared__ __attribute__((aligned(16))) bf16 sRh[D * PR];
+    __shared__ __attribute__((aligned(16))) bf16 sRl[D * PR];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = a.L, N = a.N, Lp = N * C, NG = a.NG;
+    const int head = blockIdx.x / NG, g = blockIdx.x % NG;
+    const int c0 = g * kKcacheGroup, c1 = min(c0 + kKcacheGroup, N) - 1;
+    const bf16* rg = static_cast<const bf16*>(a.rg) + ((size_t)head * NG + g) * 2 * D * D;
+    for (int u = tid; u < D * D / 8; u += 256) {
+        const int rho = u / (D / 8), c8 = (u % (D / 8)) * 8;
+        *reinterpret_cast<bf16x8*>(sRh + rho * PR + c8) = ld8k(rg + (size_t)u * 8);
+        *reinterpret_cast<bf16x8*>(sRl + rho * PR + c8) = ld8k(rg + D * D + (size_t)u * 8);
+    }
+    __syncthreads();
+    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
+    const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
+    const int jloc = (wave & 1) * 32 + l32, dtb = (wave >> 1) * DTW;
+    const int cend = min(c1, (L - 1) / C);        // chunks past it are padding
+    // Y rows as the B operand (k = c = 16 ks + 8 hh .. +7), one chunk ahead
+    bf16x8 ynext[KSD];
+    auto load_y = [&](int b) {
+        const bf16* yrow = kt + ((size_t)b * C + jloc) * D;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) ynext[ks] = ld8k(yrow + 16 * ks + 8 * hh);
+    };
+    if (c0 <= cend) load_y(c0);
+    for (int b = c0; b <= cend; ++b) {            // uniform: every lane runs the MFMAs
+        const int j = b * C + jloc;
+        bf16x8 y8[KSD];
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) y8[ks] = ynext[ks];
+        if (b < cend) load_y(b + 1);
+        f32x16 acc[DTW];
+#pragma unroll
+        for (int i = 0; i < DTW; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks) {
+#pragma unroll
+            for (int i = 0; i < DTW; ++i) {
+                const int rho = 32 * (dtb + i) + l32;
+                acc[i] = mfma32k(ld8k(sRh + rho * PR + 16 * ks + 8 * hh), y8[ks], acc[i]);
+                acc[i] = mfma32k(ld8k(sRl + rho * PR + 16 * ks + 8 * hh), y8[ks], acc[i]);
+            }
+        }
+        if (j >= L) continue;                     // padding rows of the last chunk
+        const long long row = cache_row(a.map, head, j);
+        if (row < 0) continue;
+        // register 8s+t of tile dt holds d = 32 dt + 16 s + 8 hh + t
+        bf16* kout = static_cast<bf16*>(a.k_cache) + row * D;
+#pragma unroll
+        for (int i = 0; i < DTW; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                *reinterpret_cast<bf16x8*>(kout + 32 * (dtb + i) + 16 * s2 + 8 * hh) = pack8k(acc[i], s2);
+        // values copied unchanged: each wave of the pair a quarter of the row per lane half
+        const bf16* vrow = vin + (size_t)j * D;
+        bf16* vout = static_cast<bf16*>(a.v_cache) + row * D;
+        for (int e = 8 * (2 * (wave >> 1) + hh); e < D; e += 32)
+            *reinterpret_cast<bf16x8*>(vout + e) = ld8k(vrow + e);
+    }
 }
 
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s) {
-    const dim3 grid(a.BH * ((a.N + 1) / 2)), block(256);
-    if (D == 64) hipLaunchKernelGGL(path_kcache_kernel<64>, grid, block, 0, s, a);
-    else if (D == 128) hipLaunchKernelGGL(path_kcache_kernel<128>, grid, block, 0, s, a);
-    else return hipErrorInvalidValue;
+    const int NG = a.NG;
+    if (D == 64) {
+        constexpr int NP = (kKcacheGroup + 1 + 3) / 4;
+        hipLaunchKernelGGL(path_kcache_group_kernel<64>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_apply_kernel<64>, dim3(a.BH * NG), dim3(256), 0, s, a);
+    } else if (D == 128) {
+        constexpr int NP = (kKcacheGroup + 2 + 3) / 4;
+        hipLaunchKernelGGL(path_kcache_group_kernel<128>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_apply_kernel<128>, dim3(a.BH * NG), dim3(256), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

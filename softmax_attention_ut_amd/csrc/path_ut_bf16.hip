@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     __shared__ __attribute__((aligned(16))) bf16 sW[C * PW];     // W rows, d natural
     __shared__ __attribute__((aligned(16))) bf16 sK[C * PW];     // K rows
     __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T: [rho][sigma] = W[permk(sigma)][permk(rho)]
-    constexpr bool VT = D != 64;  // V^T tiles are written (d = 128)
+    constexpr bool VT = D != 64 && !WITH_Z;  // V^T tiles are written (d = 128 forward)
     __shared__ __attribute__((aligned(16))) bf16 sV[VT ? C * PW : 8];  // V rows
     // G rows (p < m used), then X^T over its upper triangle (fp32); once X is
     // complete the same space holds T^{-1} rows with n in slots, hi and lo
@@ -408,13 +408,13 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             }
         }
         // store Y^T[j][m-slot] (DIAG: keep it for phase 4)
-        bf16* yrow = DIAG ? nullptr : static_cast<bf16*>(a.yt) + (chunkbase * C + j) * C;
+        bf16* yrow = (DIAG || WITH_Z) ? nullptr : static_cast<bf16*>(a.yt) + (chunkbase * C + j) * C;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 if (DIAG) keep[2 * mb + s2] = cvt8(yacc[mb], s2, -1.f);   // -Y^T
-                else *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
+                else if (!WITH_Z) *reinterpret_cast<bf16x8*>(yrow + 32 * mb + 16 * s2 + 8 * hh) = cvt8(yacc[mb], s2, 1.f);
             }
         // K~^T[d][j] = K^T[d][j] - sum_{m > j} W^T[d][m] Y[m][j]
         bf16x8 yh[4], yl[4];
@@ -452,10 +452,10 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
         for (int et = wave - 2; et < ET; et += 2) {
             const int e = 32 * et + l32;         // sWt row rho: d = permk(rho)
             const bf16* bw = sWt + e * PT + 8 * hh;
-            // U[m][e] = sum_n T^{-1}[m][n] W[n][e]
+            // U[m][e] = sum_n T^{-1}[m][n] W[n][e]  (not needed by the hand-off)
             f32x16 uacc[2];
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
+            for (int mt = 0; mt < 2 && !WITH_Z; ++mt) {
                 zero(uacc[mt]);
                 const bf16* th = sTh + (32 * mt + l32) * PT + 8 * hh;
                 const bf16* tl = sTl + (32 * mt + l32) * PT + 8 * hh;
@@ -466,15 +466,15 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
                     uacc[mt] = mfma(ld8(tl + 16 * ks), w8, uacc[mt]);
                 }
             }
-            bf16* urow = DIAG ? nullptr : static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
+            bf16* urow = (DIAG || WITH_Z) ? nullptr : static_cast<bf16*>(a.ut) + (chunkbase * D + e) * C;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
+            for (int mt = 0; mt < 2 && !WITH_Z; ++mt)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     if (DIAG) keep[2 * mt + s2] = cvt8(uacc[mt], s2, -1.f);
                     else *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc[mt], s2, -1.f);
                 }
-            if (a.mt) {
+            if (!WITH_Z && a.mt) {
                 // M = W^T U (d x d): the whole chunk's transition product is
                 // I - M in row-vector form.  The U accumulator's column is
                 // d = permk(e), which is row e of -M^T in the stored layout
