@@ -14,6 +14,8 @@ one-token attention) and the 256 steps after that prefill are timed.  With
 beta of every token from the layer input; B=8, L=4096, width 1536, rank 64,
 H=24, d=64).  With --workload d128_L8k_kcache the step is one prefill ->
 decode key-cache hand-off (path_kcache_from_prefill) after that prefill.
+With --workload fox_L4k_bwd (or <forward workload>_bwd) the step is one
+backward pass (path_attn_bwd) of that workload.
 
 Prints one JSON line: effective TFLOP/s (2*B*H*L^2*d per forward), tokens/s,
 the roofline of the dominant kernel (HIP events on its launch stream) and the
@@ -325,6 +327,127 @@ def bench_decode(args, cfg, torch, pa, inputs):
     return res, None
 
 
+def bwd_flop_model(B, H, L, d, C=64):
+    """FLOPs of one backward (d = C = 64, chunk C), per the algorithm the
+    library runs:
+      eff   5 L^2 d per head: the five products of attention's backward (S,
+            dP = dO V^T, dV, dK, dQ) over the causal triangle, the count behind
+            "effective TFLOP/s" (2.5 times the forward's 2 L^2 d)
+      pairs per pair of chunks b < a: those five (5 * 2 C^2 d) and, for b >= 1,
+            the query's transport Q P_b, the adjoint's G P_b^T and dM_b (3 * 2 C d^2)
+      own   per chunk: the fourteen C x C x d products of the own-chunk step
+            and of the carry to the chunk start, read backwards
+      prep  the forward's UT work per chunk (recomputed): as in flop_model
+      utb   per chunk: the UT transform's backward, seventeen C^3 products and
+            the triangular substitution (C^3 / 3)
+    "alg" = pairs + own + prep + utb."""
+    N = (L + C - 1) // C
+    pairs = N * (N - 1) / 2.0
+    f_eff = 5.0 * L * L * d
+    f_pairs = pairs * 10.0 * C * C * d + (pairs - (N - 1)) * 6.0 * C * d * d
+    f_own = N * 14 * 2.0 * C * C * d
+    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3 + 2.0 * C * d * d)
+    f_utb = N * (17 * 2.0 * C ** 3 + C ** 3 / 3.0)
+    BH = B * H
+    return {"eff": BH * f_eff, "alg": BH * (f_pairs + f_own + f_prep + f_utb)}
+
+
+def bench_bwd(args, cfg, torch, pa, inputs):
+    """One backward pass (path_attn_bwd: the per-chunk prepare, the query- and
+    key-stationary kernels, the gate's suffix sums) after one forward of the
+    same inputs, with d_out drawn once; everything resident in HBM."""
+    import numpy as np
+    inp = inputs.generate_config(cfg)
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
+    rng = np.random.default_rng(cfg.seed + 1000)
+    d_out = torch.from_numpy(rng.standard_normal((B, H, L, d)).astype(np.float32)).to(
+        torch.bfloat16).cuda()
+    out, lse = pa.attention(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], scale=cfg.scale)
+    ws = torch.empty(pa.path_attn_bwd_workspace_bytes(B, H, L, d, pa.PATH_BF16), dtype=torch.uint8,
+                     device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    dq, dk, dv, dw = (torch.empty(B, H, L, d, **f32) for _ in range(4))
+    dbeta = torch.empty(B, H, L, **f32)
+    dlog_f = torch.empty(B, H, L, **f32) if cfg.gate else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pa.path_attn_bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], out, lse, d_out,
+                         dq, dk, dv, dw, dbeta, dlog_f, cfg.scale, ws, stream)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    f = bwd_flop_model(B, H, L, d)
+    achieved = f["alg"] / (ev_ms * 1e-3) / 1e12
+    res = {
+        "metric": f"PaTH bwd effective TFLOP/s + tokens/s (bf16, L={L}, d={d}) and % MFMA peak",
+        "value": f["eff"] / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: 5*B*H*L^2*d per backward)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}_bwd: PaTH{'-FoX' if cfg.gate else ''} backward "
+                               f"B={B} H={H} L={L} d={d} bf16, chunk 64",
+                   "global_batch": B, "seq_len": L, "heads": H, "head_dim": d,
+                   "forget_gate": cfg.gate, "parallelism": "single GPU"},
+        "tokens_per_s": B * L / (ms * 1e-3),
+        "step_ms_events": ev_ms,
+        "tflops_algorithmic": achieved,
+        "roofline": {"kernel": "path_attn_bwd (path_ut_bf16_kernel<64,false,false>, "
+                               "path_bwd_query_kernel, path_bwd_key_kernel"
+                               + (", path_bwd_gate_kernel)" if cfg.gate else ")"),
+                     "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": f["alg"]},
+    }
+    return res, inp
+
+
+def bwd_cpu_baseline(inp, cfg, L_sample, heads):
+    """The fp64 oracle's backward (reverse-mode differentiation of the
+    recurrent form, torch CPU ops), unmodified, on the first L_sample tokens
+    of the first `heads` heads; its cost is quadratic in the length and linear
+    in the heads, so the whole job's time is extrapolated by
+    (L / L_sample)^2 * BH / heads."""
+    import numpy as np
+    import torch
+    import oracle
+    BH = cfg.B * cfg.H
+    rng = np.random.default_rng(cfg.seed + 2000)
+    flat = lambda t: None if t is None else t.reshape(-1, *t.shape[2:])
+    q, k, v, w, beta, lf = (flat(t) for t in (inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f))
+    t0 = time.perf_counter()
+    for h in range(heads):
+        d_out = rng.standard_normal((L_sample, cfg.d))
+        oracle.backward(q[h, :L_sample], k[h, :L_sample], v[h, :L_sample], w[h, :L_sample],
+                        beta[h, :L_sample], None if lf is None else lf[h, :L_sample], cfg.scale,
+                        d_out)
+    dt = time.perf_counter() - t0
+    factor = (cfg.L / L_sample) ** 2 * BH / heads
+    t_full = dt * factor
+    res = {"value": bwd_flop_model(cfg.B, cfg.H, cfg.L, cfg.d)["eff"] / t_full / 1e12,
+           "unit": "TFLOP/s (effective)", "cores": torch.get_num_threads(), "kind": "oracle",
+           "tokens_per_s": cfg.B * cfg.L / t_full, "extrapolated": True,
+           "extrapolation_factor": factor,
+           "sample": f"{heads} of {BH} heads, first {L_sample} of {cfg.L} tokens, fp64 autograd "
+                     f"of the recurrent oracle, {dt:.2f} s wall; whole-job time extrapolated "
+                     f"x{factor:.0f} (quadratic in length, linear in heads)"}
+    res.update(host_cpu())
+    return res
+
+
 def kcache_bytes_flops(B, H, L, d, C=64, G=8):
     """Algorithmic HBM bytes and FLOPs of one prefill -> decode key-cache
     hand-off: read k, w, v (bf16) and beta, write the key and value caches'
@@ -534,6 +657,13 @@ def main():
         res, inp = bench_transition(args, cfg, torch, pa, inputs)
         if not args.no_cpu_baseline:
             res["cpu_baseline"] = transition_cpu_baseline(inp, cfg, args.cpu_threads or default_cpu_threads())
+        print(json.dumps(res), flush=True)
+        return
+    if args.workload.endswith("_bwd"):
+        cfg = inputs.CONFIGS[args.workload[:-len("_bwd")]]
+        res, inp = bench_bwd(args, cfg, torch, pa, inputs)
+        if not args.no_cpu_baseline:
+            res["cpu_baseline"] = bwd_cpu_baseline(inp, cfg, 1024, 6)
         print(json.dumps(res), flush=True)
         return
     if args.workload.endswith("_kcache"):

@@ -26,9 +26,11 @@
  *   - The caller owns every buffer, including the workspace; the library
  *     allocates nothing and keeps no global state apart from a per-device
  *     cache of one occupancy query (filled on the first decode call on a
- *     device, thread-safe), so calls on different streams with different
- *     workspaces may run concurrently.  Calls that share a workspace or a
- *     cache race unless ordered by the caller.
+ *     device, thread-safe) and the fixed device array that
+ *     path_decode_step_noalloc uses instead of a workspace, so calls on
+ *     different streams with different workspaces may run concurrently.
+ *     Calls that share a workspace, a cache or that array race unless
+ *     ordered by the caller.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream).  Argument checks run on the host before any HIP call;
  *     a negative path_status_t is returned and nothing is launched.  A failed
@@ -128,6 +130,50 @@ int path_attn_fwd_scan(const void* q, const void* k, const void* v, const void* 
                        int B, int H, int L, int d, float scale,
                        int dtype, int chunk,
                        const void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace size in bytes for path_attn_bwd, or 0 if the arguments are
+ * invalid or unsupported (dtype other than PATH_BF16, d other than 64).
+ * Grows as B*H*L^2/64 * 16 bytes: two 64 x 64 bf16 tiles per pair of
+ * chunks (b < a) per head, plus O(B*H*L*d) for the per-chunk quantities.
+ */
+size_t path_attn_bwd_workspace_bytes(int B, int H, int L, int d, int dtype);
+
+/*
+ * Gradients of path_attn_fwd (training; the pages train with the same
+ * blockwise algorithm as the forward: English summary, Dutch summary
+ * section 3).  Given the forward's inputs, its out and lse, and d_out =
+ * dLoss/d out, writes dLoss/d of every input, the exact gradient of the
+ * blockwise computation read back step by step (Chinese notes, training
+ * strategy: the UT transform, a block's full-matrix form, the right-to-left
+ * transport of queries); the softmax part follows the usual
+ * rowsum(d_out o out) form of attention's backward.
+ *
+ *   q, k, v, w     [B][H][L][d] bf16, as given to path_attn_fwd.
+ *   beta           [B][H][L] float32.
+ *   log_f          [B][H][L] float32 or NULL (no forget gate).
+ *   out, lse       the forward's outputs for these inputs (out bf16, lse
+ *                  float32 natural log).
+ *   d_out          [B][H][L][d] bf16.
+ *   dq, dk, dv, dw [B][H][L][d] float32 (written, every element).
+ *   dbeta          [B][H][L] float32 (written).
+ *   dlog_f         [B][H][L] float32 (written), NULL exactly when log_f is
+ *                  NULL; dlog_f[0] of each head is 0 up to rounding (f_0
+ *                  never enters a logit).
+ *   dtype          PATH_BF16 only; d = 64 only (else PATH_ERR_UNSUPPORTED).
+ *   workspace      at least path_attn_bwd_workspace_bytes(...) bytes,
+ *                  256-byte aligned; contents on entry ignored.
+ * Gradients are accumulated in float32 from bf16 MFMA products; the per-pair
+ * states the algorithm stores are bf16.  A null pointer, a bad size or
+ * log_f/dlog_f given without the other is PATH_ERR_INVALID.  Inputs are not
+ * modified.  Asynchronous on `stream`.
+ */
+int path_attn_bwd(const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_f, const void* out,
+                  const float* lse, const void* d_out, float* dq, float* dk,
+                  float* dv, float* dw, float* dbeta, float* dlog_f,
+                  int B, int H, int L, int d, float scale, int dtype,
+                  void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * Workspace size in bytes for path_kcache_from_prefill, or 0 if invalid.

@@ -31,7 +31,7 @@ EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes"
            "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
            "path_decode_step_gated", "path_transition_prep",
            "path_kcache_from_prefill_paged", "path_decode_step_paged",
-           "path_decode_step_noalloc")
+           "path_decode_step_noalloc", "path_attn_bwd_workspace_bytes", "path_attn_bwd")
 
 
 class PathError(RuntimeError):
@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.path_attn_fwd_prepare.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
     lib.path_attn_fwd_scan.restype = I
     lib.path_attn_fwd_scan.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, I, P, S, P]
+    lib.path_attn_bwd_workspace_bytes.restype = S
+    lib.path_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.path_attn_bwd.restype = I
+    lib.path_attn_bwd.argtypes = [P] * 15 + [I, I, I, I, F, I, P, S, P]
     lib.path_kcache_workspace_bytes.restype = S
     lib.path_kcache_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.path_kcache_from_prefill.restype = I
@@ -167,6 +171,26 @@ def path_attn_fwd_scan(q, k, v, w, log_f, out, lse, scale, chunk=0, workspace=No
                                 B, H, L, d, float(scale), _dt(q), int(chunk), _p(workspace),
                                 ws_bytes, _stream(stream))
     _check(st, "path_attn_fwd_scan")
+
+
+def path_attn_bwd_workspace_bytes(B, H, L, d, dtype) -> int:
+    return load_library().path_attn_bwd_workspace_bytes(B, H, L, d, dtype)
+
+
+def path_attn_bwd(q, k, v, w, beta, log_f, out, lse, d_out, dq, dk, dv, dw, dbeta, dlog_f,
+                  scale, workspace=None, stream=None):
+    """Gradients of path_attn_fwd: q,k,v,w,out,d_out bf16 [B,H,L,d]; dq,dk,dv,dw
+    fp32 [B,H,L,d]; beta, log_f (or None), lse, dbeta, dlog_f (or None) fp32 [B,H,L]."""
+    lib = load_library()
+    _require_cuda(q, k, v, w, beta, log_f, out, lse, d_out, dq, dk, dv, dw, dbeta, dlog_f,
+                  workspace)
+    B, H, L, d = q.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_attn_bwd(_p(q), _p(k), _p(v), _p(w), _p(beta), _p(log_f), _p(out), _p(lse),
+                           _p(d_out), _p(dq), _p(dk), _p(dv), _p(dw), _p(dbeta), _p(dlog_f),
+                           B, H, L, d, float(scale), _dt(q), _p(workspace), ws_bytes,
+                           _stream(stream))
+    _check(st, "path_attn_bwd")
 
 
 def path_kcache_workspace_bytes(B, H, L, d, dtype) -> int:
@@ -316,6 +340,25 @@ def attention(q, k, v, w, beta, log_f=None, scale=None, chunk=0, want_lse=True,
     lse = torch.empty(B, H, L, dtype=torch.float32, device=q.device) if want_lse else None
     path_attn_fwd(q, k, v, w, beta, log_f, out, lse, scale, chunk, ws, stream)
     return out, lse
+
+
+def attention_backward(q, k, v, w, beta, log_f, out, lse, d_out, scale=None, stream=None):
+    """Gradients of attention(): returns (dq, dk, dv, dw, dbeta, dlog_f or None),
+    float32, from the forward's out and lse and d_out = dLoss/d out."""
+    B, H, L, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    n = path_attn_bwd_workspace_bytes(B, H, L, d, _dt(q))
+    if n == 0:
+        raise PathError(-2, "path_attn_bwd_workspace_bytes")
+    ws = _workspace(n, q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv, dw = (torch.empty(B, H, L, d, **f32) for _ in range(4))
+    dbeta = torch.empty(B, H, L, **f32)
+    dlog_f = torch.empty(B, H, L, **f32) if log_f is not None else None
+    path_attn_bwd(q, k, v, w, beta, log_f, out, lse, d_out, dq, dk, dv, dw, dbeta, dlog_f,
+                  scale, ws, stream)
+    return dq, dk, dv, dw, dbeta, dlog_f
 
 
 def kcache_from_prefill(k, v, w, beta, T_max, stream=None):

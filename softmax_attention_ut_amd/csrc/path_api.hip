@@ -166,6 +166,58 @@ int path_attn_fwd(const void* q, const void* k, const void* v, const void* w,
                               workspace, ws_bytes, stream);
 }
 
+size_t path_attn_bwd_workspace_bytes(int B, int H, int L, int d, int dtype) {
+    int chunk = kBf16Chunk;
+    if (dtype != PATH_BF16 || d != 64 || check_fwd_shape(B, H, L, d, dtype, chunk) != PATH_OK)
+        return 0;
+    return plan_bwd_workspace((size_t)B * H, (size_t)L).total;
+}
+
+int path_attn_bwd(const void* q, const void* k, const void* v, const void* w,
+                  const float* beta, const float* log_f, const void* out, const float* lse,
+                  const void* d_out, float* dq, float* dk, float* dv, float* dw, float* dbeta,
+                  float* dlog_f, int B, int H, int L, int d, float scale, int dtype,
+                  void* workspace, size_t ws_bytes, void* stream) {
+    int chunk = kBf16Chunk;
+    int st = check_fwd_shape(B, H, L, d, dtype, chunk);
+    if (st != PATH_OK) return st;
+    if (dtype != PATH_BF16 || d != 64) return PATH_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !w || !beta || !out || !lse || !d_out) return PATH_ERR_INVALID;
+    if (!dq || !dk || !dv || !dw || !dbeta) return PATH_ERR_INVALID;
+    if ((log_f == nullptr) != (dlog_f == nullptr)) return PATH_ERR_INVALID;
+    if (!(scale == scale)) return PATH_ERR_INVALID;
+    const BwdWorkspace ws = plan_bwd_workspace((size_t)B * H, (size_t)L);
+    if (!workspace || ws_bytes < ws.total) return PATH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return PATH_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = B * H, N = (L + chunk - 1) / chunk;
+    // the forward's per-chunk quantities (K~, -U^T, Y^T, -M^T, gate sums)
+    UtArgs u{};
+    u.k = k; u.v = v; u.w = w; u.beta = beta; u.log_f = log_f;
+    u.BH = BH; u.L = L; u.N = N; u.C = chunk; u.D = d;
+    u.kt = at(workspace, ws.fwd.kt);
+    u.ut = at(workspace, ws.fwd.ut);
+    u.yt = at(workspace, ws.fwd.yt);
+    u.mt = at(workspace, ws.fwd.mt);
+    u.loc = log_f ? reinterpret_cast<float*>(at(workspace, ws.fwd.loc)) : nullptr;
+    u.csum = log_f ? reinterpret_cast<float*>(at(workspace, ws.fwd.csum)) : nullptr;
+    if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
+    BwdArgs b{};
+    b.q = q; b.k = k; b.v = v; b.w = w; b.beta = beta; b.log_f = log_f;
+    b.out = out; b.lse = lse; b.dout = d_out;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dw = dw; b.dbeta = dbeta; b.dlogf = dlog_f;
+    b.kt = u.kt; b.ut = u.ut; b.yt = u.yt; b.mt = u.mt; b.loc = u.loc; b.csum = u.csum;
+    b.qs = at(workspace, ws.qs);
+    b.gs = at(workspace, ws.gs);
+    b.own = reinterpret_cast<float*>(at(workspace, ws.own));
+    b.dsum = reinterpret_cast<float*>(at(workspace, ws.dsum));
+    b.rsum = reinterpret_cast<float*>(at(workspace, ws.rsum));
+    b.csd = reinterpret_cast<float*>(at(workspace, ws.csd));
+    b.csl = reinterpret_cast<float*>(at(workspace, ws.csl));
+    b.BH = BH; b.L = L; b.N = N; b.scale = scale;
+    return launch_path_bwd(b, s) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
 size_t path_kcache_workspace_bytes(int B, int H, int L, int d, int dtype) {
     int chunk = kBf16Chunk;
     if (dtype != PATH_BF16 || check_fwd_shape(B, H, L, d, dtype, chunk) != PATH_OK) return 0;

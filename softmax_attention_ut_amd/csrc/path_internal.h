@@ -234,6 +234,48 @@ struct TransArgs {
 // ceil(T_max / kDecodeSplitQuantum) splits (the workspace holds that many).
 constexpr int kDecodeSplitQuantum = 64;
 
+// Backward pass (bf16, d = 64): inputs, outputs and its workspace sections
+// (see path_bwd.hip).
+struct BwdArgs {
+    const void* q; const void* k; const void* v; const void* w;
+    const float* beta; const float* log_f;   // log_f null without the gate
+    const void* out; const float* lse; const void* dout;
+    float* dq; float* dk; float* dv; float* dw; float* dbeta; float* dlogf;
+    const void* kt; const void* ut; const void* yt; const void* mt;
+    const float* loc; const float* csum;
+    void* qs; void* gs; float* own; float* dsum; float* rsum; float* csd; float* csl;
+    int BH, L, N;
+    float scale;
+};
+
+struct BwdWorkspace {
+    Workspace fwd;         // kt, ut, yt, mt, loc, csum of the forward's prepare stage
+    size_t qs, gs, own, dsum, rsum, csd, csl, total;
+};
+
+inline BwdWorkspace plan_bwd_workspace(size_t BH, size_t L) {
+    constexpr size_t C = 64, D = 64;
+    BwdWorkspace b{};
+    const size_t N = (L + C - 1) / C, Lp = N * C, pairs = N * (N - 1) / 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+    b.fwd.kt = take(BH * Lp * D * 2);
+    b.fwd.ut = take(BH * Lp * D * 2);
+    b.fwd.yt = take(BH * N * C * C * 2);
+    b.fwd.mt = take(BH * N * D * D * 2);
+    b.fwd.loc = take(BH * Lp * 4);
+    b.fwd.csum = take(BH * N * 4);
+    b.qs = take(BH * pairs * C * D * 2);
+    b.gs = take(BH * pairs * C * D * 2);
+    b.own = take(BH * N * 5 * C * D * 4);
+    b.dsum = take(BH * Lp * 4);
+    b.rsum = take(BH * Lp * 4);
+    b.csd = take(BH * Lp * 4);
+    b.csl = take(BH * Lp * 4);
+    b.total = off;
+    return b;
+}
+
 // Host-side launchers (return hipError_t of the launch).
 hipError_t launch_path_ut_f32(const UtArgs& a, hipStream_t s);
 hipError_t launch_path_ut_bf16(const UtArgs& a, hipStream_t s);
@@ -241,6 +283,7 @@ hipError_t launch_path_fwd_f32(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_fwd_bf16(const FwdArgs& a, bool gate, hipStream_t s);
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s);
 hipError_t launch_path_decode(const DecodeArgs& a, int D, hipStream_t s);
+hipError_t launch_path_bwd(const BwdArgs& a, hipStream_t s);
 // The library's own split-partials buffer of path_decode_step_noalloc: its
 // size, and its device address on the current device (looked up once per
 // device with hipGetSymbolAddress, then cached).

@@ -107,6 +107,35 @@ def test_noalloc_decode_argument_errors_before_launch():
     assert lib.path_decode_step_noalloc(*args(128, 64, 100, 200, 128, pa.PATH_BF16)) == -4
 
 
+def test_bwd_workspace_and_argument_errors_before_launch():
+    """path_attn_bwd: bf16 with d = 64 only; log_f and dlog_f both or
+    neither; the workspace holds two bf16 64 x 64 tiles per pair of chunks
+    per head.  Every call here is rejected on the host (the fake pointers are
+    never dereferenced)."""
+    lib = pa.load_library()
+    f = lib.path_attn_bwd_workspace_bytes
+    assert f(1, 1, 128, 128, pa.PATH_BF16) == 0
+    assert f(1, 1, 128, 64, pa.PATH_F32) == 0
+    assert f(1, 1, 0, 64, pa.PATH_BF16) == 0
+    # 64 -> 128 chunks adds 64 * 127 / 2 - 32 * 31 / 2 pairs, 16 KiB each
+    assert f(1, 1, 8192, 64, pa.PATH_BF16) - f(1, 1, 4096, 64, pa.PATH_BF16) >= 3568 * 16384
+    assert f(1, 1, 1000, 64, pa.PATH_BF16) == f(1, 1, 1024, 64, pa.PATH_BF16)
+    p = ctypes.c_void_p(4096)
+    ws = f(1, 1, 128, 64, pa.PATH_BF16)
+
+    def call(lf=p, dlf=p, d=64, dt=pa.PATH_BF16, wsb=ws, L=128, q=p, w_=p):
+        return lib.path_attn_bwd(q, p, p, p, p, lf, p, p, p, p, p, p, p, p, dlf,
+                                 1, 1, L, d, 0.125, dt, w_, wsb, None)
+    assert call(dlf=None) == -1
+    assert call(lf=None) == -1
+    assert call(q=None) == -1
+    assert call(L=0) == -1
+    assert call(d=128) == -2
+    assert call(dt=pa.PATH_F32) == -2
+    assert call(wsb=ws - 1) == -4
+    assert call(w_=ctypes.c_void_p(4096 + 16)) == -4
+
+
 def test_gated_decode_argument_errors_before_launch():
     lib = pa.load_library()
     p = ctypes.c_void_p(4096)

@@ -1,0 +1,124 @@
+"""GPU parity of the backward pass (path_attn_bwd through the C ABI) against
+the oracle's gradients (reverse-mode differentiation of the fp64 recurrent
+form), every element of every gradient.
+
+The GPU backward reads the GPU forward's bf16 out and its lse, as a training
+step would; the oracle differentiates the exact forward.  Tolerances, per
+gradient g against the oracle's r (both over all heads and tokens):
+    max |g - r| <= 3e-2 * max |r|,   ||g - r||_F <= 1e-2 * ||r||_F.
+Every product runs on bf16 operands (relative rounding 2^-9 = 2e-3 per
+operand) with fp32 sums; the per-pair states (the query carried to each key
+chunk and the query's adjoint at each chunk) are stored in bf16 and each
+step of their chains adds one such rounding, so over the N <= 11 chunks of
+these cases the relative error grows to a few times 2e-3 (about sqrt(N)
+roundings in a random walk, plus rowsum(d_out o out) taken from the bf16
+out).  The Frobenius bound is 5 times 2e-3, the max bound allows an element
+of a small-magnitude gradient (dbeta, dlog_f sum many signed terms) to sit
+at the tail of the error distribution.  dlog_f[0] is 0 up to rounding on
+both sides (f_0 never enters a logit).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_ut_amd as pa
+from softmax_attention_ut_amd.inputs import generate
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, FRO_REL = 3e-2, 1e-2
+
+
+def _d_out(shape, seed):
+    rng = np.random.default_rng(seed)
+    return torch.from_numpy(rng.standard_normal(shape)).to(torch.bfloat16).contiguous()
+
+
+def _gpu_grads(inp, d_out, scale):
+    g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
+    out, lse = pa.attention(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], scale=scale)
+    grads = pa.attention_backward(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], out,
+                                  lse, d_out.cuda(), scale=scale)
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dw", "dbeta", "dlog_f")
+    return {n: t.double().cpu().numpy() for n, t in zip(names, grads) if t is not None}
+
+
+def _oracle_grads(inp, d_out, scale):
+    B, H, L, d = inp.q.shape
+    res = {}
+    for b in range(B):
+        for h in range(H):
+            r = oracle.backward(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.w[b, h],
+                                inp.beta[b, h], None if inp.log_f is None else inp.log_f[b, h],
+                                scale, d_out[b, h])
+            for n, x in r.items():
+                res.setdefault(n, np.zeros((B, H) + x.shape))[b, h] = x
+    return res
+
+
+def _compare(got, ref, what):
+    assert set(got) == set(ref), (what, sorted(got), sorted(ref))
+    failures = []
+    for n in sorted(ref):
+        g, r = got[n], ref[n]
+        assert np.all(np.isfinite(g)), (what, n)
+        e = np.abs(g - r)
+        mx = e.max() / max(np.abs(r).max(), 1e-30)
+        fro = np.linalg.norm(e) / max(np.linalg.norm(r), 1e-30)
+        where = tuple(int(x) for x in np.unravel_index(np.argmax(e), e.shape))
+        print(f"{what} {n}: max-abs/max|ref| {mx:.3e} (at {where}) "
+              f"fro-rel {fro:.3e}", flush=True)
+        if mx > MAX_REL or fro > FRO_REL:
+            failures.append((n, mx, fro))
+    assert not failures, (what, failures)
+
+
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("L", [64, 333, 700])
+def test_backward_matches_oracle(L, gate):
+    """One chunk (no pairs), a ragged last chunk, and eleven chunks."""
+    B, H, d = 1, 2, 64
+    scale = 1 / math.sqrt(d)
+    inp = generate(B, H, L, d, dtype="bf16", gate=gate, seed=200 + L + gate)
+    d_out = _d_out((B, H, L, d), 300 + L)
+    print(f"backward L={L} gate={gate}", flush=True)
+    _compare(_gpu_grads(inp, d_out, scale), _oracle_grads(inp, d_out, scale),
+             f"L={L} gate={gate}")
+
+
+def test_backward_several_heads_and_batches():
+    """B = 2, H = 3: the head index of every workspace section and gradient."""
+    B, H, L, d = 2, 3, 200, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=True, seed=211)
+    d_out = _d_out((B, H, L, d), 311)
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), "B=2 H=3")
+
+
+def test_backward_gate_cut():
+    """log f = -1e4 at two tokens: gradients of keys before a cut vanish for
+    queries after it, and dlog_f at the cut is (almost) 0."""
+    B, H, L, d = 1, 2, 400, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=True, seed=212)
+    for t in (130, 256):
+        inp.log_f[..., t] = -1e4
+    d_out = _d_out((B, H, L, d), 312)
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), "gate cut")
+
+
+def test_backward_beta_zero_is_causal_attention_backward():
+    """beta = 0 everywhere: PaTH is plain causal softmax attention; dw is 0
+    and the gradients are attention's (checked by the oracle's pins); the GPU
+    path must give dw = 0 exactly (every product with dU, dY, dM vanishes)."""
+    B, H, L, d = 1, 2, 300, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=False, seed=213)
+    inp.beta.zero_()
+    d_out = _d_out((B, H, L, d), 313)
+    got = _gpu_grads(inp, d_out, 0.125)
+    ref = _oracle_grads(inp, d_out, 0.125)
+    assert np.all(got["dw"] == 0.0)
+    del got["dw"], ref["dw"]
+    _compare(got, ref, "beta=0")
