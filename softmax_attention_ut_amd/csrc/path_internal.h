@@ -241,7 +241,7 @@ struct BwdArgs {
     const float* beta; const float* log_f;   // log_f null without the gate
     const void* out; const float* lse; const void* dout;
     float* dq; float* dk; float* dv; float* dw; float* dbeta; float* dlogf;
-    const void* kt; const void* ut; const void* yt; const void* mt;
+    const void* kt; void* ut; void* yt; void* mt;   // U, Y, M: made row-major in place
     const float* loc; const float* csum;
     void* qs; void* gs; float* own; float* dsum; float* rsum; float* csd; float* csl;
     int BH, L, N;
@@ -267,7 +267,7 @@ inline BwdWorkspace plan_bwd_workspace(size_t BH, size_t L) {
     b.fwd.csum = take(BH * N * 4);
     b.qs = take(BH * pairs * C * D * 2);
     b.gs = take(BH * pairs * C * D * 2);
-    b.own = take(BH * N * 5 * C * D * 4);
+    b.own = take(BH * N * 9 * C * D * 4);
     b.dsum = take(BH * Lp * 4);
     b.rsum = take(BH * Lp * 4);
     b.csd = take(BH * Lp * 4);
