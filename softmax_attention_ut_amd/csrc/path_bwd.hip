@@ -159,6 +159,22 @@ __device__ __forceinline__ float wave_sum32(float x) {   // over the 32 lanes of
     return x;
 }
 
+// Workgroup -> (head, chunk).  Workgroups are dealt to the 8 XCDs in turn;
+// when B*H is a multiple of 8, head h goes to XCD h % 8 and its chunks run
+// together there, so the per-chunk tiles every chunk of a head reads (K~,
+// V, M, d_out) stay in that XCD's L2.  rev: chunks in decreasing order.
+__device__ __forceinline__ void wg_map(int x, int BH, int N, bool rev, int& head, int& c) {
+    if ((BH & 7) == 0) {
+        const int slot = x >> 3;
+        head = (slot / N) * 8 + (x & 7);
+        c = slot % N;
+    } else {
+        head = x / N;
+        c = x % N;
+    }
+    if (rev) c = N - 1 - c;
+}
+
 // index of the pair (a, b), b < a, in the per-head pair arrays
 __device__ __forceinline__ size_t pair_index(int a, int b) { return (size_t)a * (a - 1) / 2 + b; }
 
@@ -242,7 +258,8 @@ __global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = a.L, N = a.N, Lp = N * BC;
-    const int head = blockIdx.x / N, ca = blockIdx.x % N;
+    int head, ca;
+    wg_map(blockIdx.x, a.BH, N, true, head, ca);
     const int p0 = ca * BC, nva = min(BC, L - p0);
     const size_t hrow = (size_t)head * L;      // input rows of the head
     const size_t wrow = (size_t)head * Lp;     // workspace rows of the head
@@ -485,7 +502,8 @@ __global__ __launch_bounds__(256, 2) void path_bwd_key_kernel(const BwdKArgs a) 
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = a.L, N = a.N, Lp = N * BC;
-    const int head = blockIdx.x / N, cb = blockIdx.x % N;
+    int head, cb;
+    wg_map(blockIdx.x, a.BH, N, false, head, cb);
     const int p0 = cb * BC, nvb = min(BC, L - p0);
     const size_t hrow = (size_t)head * L, wrow = (size_t)head * Lp;
     const size_t chunk0 = (size_t)head * N;
