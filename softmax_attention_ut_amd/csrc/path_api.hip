@@ -207,6 +207,10 @@ int path_attn_bwd(const void* q, const void* k, const void* v, const void* w,
     b.out = out; b.lse = lse; b.dout = d_out;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dw = dw; b.dbeta = dbeta; b.dlogf = dlog_f;
     b.kt = u.kt; b.ut = u.ut; b.yt = u.yt; b.mt = u.mt; b.loc = u.loc; b.csum = u.csum;
+    b.kp = at(workspace, ws.kp);
+    b.kts = at(workspace, ws.kts);
+    b.mn = at(workspace, ws.mn);
+    b.mtn = at(workspace, ws.mtn);
     b.qs = at(workspace, ws.qs);
     b.gs = at(workspace, ws.gs);
     b.own = reinterpret_cast<float*>(at(workspace, ws.own));

@@ -32,23 +32,32 @@
 //     complementary block, where that rounding weighs most.
 //
 // Kernels (after the forward's prepare stage, path_ut_bf16, for K~, U, Y, M
-// and the gate sums):
-//   path_bwd_layout_kernel one workgroup per (head, chunk): U, Y, M from the
-//       prepare stage's operand layouts to row-major tiles, in place;
-//   path_bwd_query_kernel  one workgroup per (head, query chunk a): the own
-//       chunk, then Q_{a,b} right to left (stored per pair), then the adjoint
-//       G left to right (stored per pair), then dQ~_a and dQ_a;
-//   path_bwd_key_kernel    one workgroup per (head, key chunk b): dV, dK~ and
-//       dM summed over the query chunks a > b;
-//   path_bwd_ut_kernel     one workgroup per (head, chunk): the chunk's
-//       UT-transform backward -> dK, dW, dbeta;
-//   path_bwd_gate_kernel   one workgroup per head: dlog f by suffix sums.
-// Every 64 x 64 x 64 product is four bf16 MFMAs per wave (32 x 32 quarter
-// tiles, fp32 accumulation) on LDS tiles; the stored per-pair states
-// (Q_{a,b}, G_{a,b-1}) are bf16.  Global tiles move as 16-byte fragments,
-// fetched for the next step of a loop while the current step computes; the
-// query and key kernels keep eight LDS tiles (74 KB) so that two workgroups
-// share a CU.
+// and the gate sums), each a grid over (head, chunk):
+//   path_bwd_layout_kernel   U, Y as row-major tiles (in place) and the
+//       operand tiles of the chains (K~, scale K~^T, -M, -M^T with the k
+//       axis in the accumulator slot order, see below);
+//   path_bwd_own_kernel      a query chunk's own-chunk step (probabilities,
+//       dV, dK, dY of the chunk itself, the partial dQ and d lower(Q W^T))
+//       and Q~, the query carried to the chunk start;
+//   path_bwd_chain_kernel    two query chunks per workgroup: Q_{a,b} right
+//       to left (stored per pair), then the adjoint G left to right (stored
+//       per pair) -> dQ~ = G_{a-1} and the row sums of dS;
+//   path_bwd_own_end_kernel  dQ~ through Q~ = Q - lower(Q W^T) U: dQ, dU, dW
+//       of the own chunk;
+//   path_bwd_key_kernel      one key chunk per workgroup: dV, dK~, dM summed
+//       over the later query chunks, and the column sums of dS;
+//   path_bwd_ut_kernel       the UT-transform backward -> dK, dW, dbeta;
+//   path_bwd_gate_kernel     dlog f by suffix sums.
+// The own-chunk kernels work on 64 x 64 LDS tiles with four waves, each wave
+// a 32 x 32 quarter of every product.  The chain and key kernels keep their
+// states in MFMA accumulators: in the 32x32x16 bf16 MFMA, accumulator
+// registers 8s .. 8s+7 of a 32 x 32 tile are exactly the B operand of k-step
+// s when the k axis is taken in the slot order permk (path_internal.h), so a
+// product's result feeds the next product with no data movement, and every
+// A operand that meets it is stored with its k axis in that order.  The
+// per-pair states (Q_{a,b}, G_{a,b-1}) are stored as bf16 rows in slot
+// order, which is both the chain kernel's B operand and the key kernel's A
+// operand.
 #include "path_internal.h"
 
 namespace path {
@@ -59,12 +68,14 @@ constexpr int BC = 64;        // chunk = head dim
 constexpr int BP = BC + 8;    // LDS tile pitch (bf16 elements)
 constexpr int BT = BC * BP;   // LDS tile size (elements)
 constexpr int FP = BC + 4;    // fp32 LDS tile pitch (rows 16-byte aligned)
-constexpr int NOWN = 9;       // fp32 64 x 64 partials per chunk (see below)
+constexpr int TT = BC * BC;   // elements of a 64 x 64 workspace tile
+constexpr int NOWN = 11;      // fp32 64 x 64 partials per chunk (see below)
 
 __device__ __forceinline__ f32x16 mfmab(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ bf16x8 l8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ void s8(bf16* p, bf16x8 x) { *reinterpret_cast<bf16x8*>(p) = x; }
 __device__ __forceinline__ f32x16 z16() {
     f32x16 z;
 #pragma unroll
@@ -117,11 +128,12 @@ __device__ __forceinline__ f32x16 ld_qg(const float* G, int wave, int lane) {
     return r;
 }
 
-// A 64 x 64 bf16 tile of row-major [64][64] global rows in flight: thread t
-// holds rows 2 (t & 31) and 2 (t & 31) + 1, columns 8 (t >> 5) .. + 7.  fetch
-// issues the loads (rows >= nvalid read as zero); put / put_t write the
-// fragment to an LDS tile as is or transposed (then each pair of rows is one
-// 4-byte word per column: the 64 lanes of a wave hit 64 distinct banks).
+// A 64 x 64 bf16 tile of row-major [64][64] global rows in flight over 256
+// threads: thread t holds rows 2 (t & 31) and 2 (t & 31) + 1, columns
+// 8 (t >> 5) .. + 7.  fetch issues the loads (rows >= nvalid read as zero);
+// put / put_t write the fragment to an LDS tile as is or transposed (then
+// each pair of rows is one 4-byte word per column: the 64 lanes of a wave
+// hit 64 distinct banks).
 struct Frag { bf16x8 x[2]; };
 __device__ __forceinline__ Frag fetch(const bf16* g, int nvalid, int tid) {
     const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
@@ -133,8 +145,8 @@ __device__ __forceinline__ Frag fetch(const bf16* g, int nvalid, int tid) {
 }
 __device__ __forceinline__ void put(bf16* T, const Frag& f, int tid) {
     const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
-    *reinterpret_cast<bf16x8*>(T + r * BP + c) = f.x[0];
-    *reinterpret_cast<bf16x8*>(T + (r + 1) * BP + c) = f.x[1];
+    s8(T + r * BP + c, f.x[0]);
+    s8(T + (r + 1) * BP + c, f.x[1]);
 }
 __device__ __forceinline__ void put_t(bf16* T, const Frag& f, int tid) {
     const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
@@ -149,7 +161,70 @@ __device__ __forceinline__ void store_tile(bf16* g, const bf16* T, int tid) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int u = tid + 256 * it, r = u >> 3, c = (u & 7) * 8;
-        *reinterpret_cast<bf16x8*>(g + r * BC + c) = l8(T + r * BP + c);
+        s8(g + r * BC + c, l8(T + r * BP + c));
+    }
+}
+
+// The same over 128 threads: thread t holds rows 2 (t & 31), 2 (t & 31) + 1
+// and the column units 8 (t >> 5) and 8 (t >> 5) + 32.
+struct Frag4 { bf16x8 x[2][2]; };   // [unit][row]
+__device__ __forceinline__ Frag4 fetch4(const bf16* g, int nvalid, int tid) {
+    const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
+    const bf16x8 z = {};
+    Frag4 f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+            f.x[u][rr] = r + rr < nvalid ? l8(g + (size_t)(r + rr) * BC + c + 32 * u) : z;
+    return f;
+}
+__device__ __forceinline__ void put4(bf16* T, const Frag4& f, int tid) {
+    const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) s8(T + (r + rr) * BP + c + 32 * u, f.x[u][rr]);
+}
+// Transposed with the old row index taken into slot order: T[col][permk(row)]
+// (a tile whose rows become the k axis of a chained product); with PC also
+// the old column: T[permk(col)][permk(row)].  permk keeps 2i, 2i+1 adjacent.
+template <bool PC>
+__device__ __forceinline__ void put4_tp(bf16* T, const Frag4& f, int tid) {
+    const int r = 2 * (tid & 31), c = 8 * (tid >> 5), pr = permk(r);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int col = c + 32 * u + e;
+            const bf16x2 p = {f.x[u][0][e], f.x[u][1][e]};
+            *reinterpret_cast<bf16x2*>(T + (PC ? permk(col) : col) * BP + pr) = p;
+        }
+}
+
+// Accumulator registers 8 H .. 8 H + 7 as a bf16 B operand (times s).
+template <int H>
+__device__ __forceinline__ bf16x8 cvt8(const f32x16& a, float s = 1.f) {
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = static_cast<bf16>(s * a[8 * H + t]);
+    return r;
+}
+// B operand of k-step ks from a pair of accumulator tiles (rows 0-31, 32-63)
+__device__ __forceinline__ bf16x8 bop(const f32x16* acc, int ks, float s = 1.f) {
+    return (ks & 1) ? cvt8<1>(acc[ks >> 1], s) : cvt8<0>(acc[ks >> 1], s);
+}
+// A operand of block blk (rows 32 blk ..), k-step ks from an LDS tile
+__device__ __forceinline__ bf16x8 aop(const bf16* T, int blk, int ks, int lane) {
+    return l8(T + (32 * blk + (lane & 31)) * BP + 16 * ks + 8 * (lane >> 5));
+}
+// acc[blk] += A(T) B over the 64-long k axis, for both row blocks
+__device__ __forceinline__ void mm2(f32x16* acc, const bf16* T, const bf16x8* b, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a0 = aop(T, 0, ks, lane), a1 = aop(T, 1, ks, lane);
+        acc[0] = mfmab(a0, b[ks], acc[0]);
+        acc[1] = mfmab(a1, b[ks], acc[1]);
     }
 }
 
@@ -159,20 +234,20 @@ __device__ __forceinline__ float wave_sum32(float x) {   // over the 32 lanes of
     return x;
 }
 
-// Workgroup -> (head, chunk).  Workgroups are dealt to the 8 XCDs in turn;
-// when B*H is a multiple of 8, head h goes to XCD h % 8 and its chunks run
-// together there, so the per-chunk tiles every chunk of a head reads (K~,
-// V, M, d_out) stay in that XCD's L2.  rev: chunks in decreasing order.
-__device__ __forceinline__ void wg_map(int x, int BH, int N, bool rev, int& head, int& c) {
+// Workgroup -> (head, unit).  Workgroups are dealt to the 8 XCDs in turn;
+// when B*H is a multiple of 8, head h goes to XCD h % 8 and its units run
+// together there, so the per-chunk tiles every unit of a head reads stay in
+// that XCD's L2.  rev: units in decreasing order.
+__device__ __forceinline__ void wg_map(int x, int BH, int NU, bool rev, int& head, int& u) {
     if ((BH & 7) == 0) {
         const int slot = x >> 3;
-        head = (slot / N) * 8 + (x & 7);
-        c = slot % N;
+        head = (slot / NU) * 8 + (x & 7);
+        u = slot % NU;
     } else {
-        head = x / N;
-        c = x % N;
+        head = x / NU;
+        u = x % NU;
     }
-    if (rev) c = N - 1 - c;
+    if (rev) u = NU - 1 - u;
 }
 
 // index of the pair (a, b), b < a, in the per-head pair arrays
@@ -200,66 +275,96 @@ __device__ __forceinline__ void row_dots(float* sD, const bf16* dO, const bf16* 
 
 // Workspace sections of the backward (set up by the API layer).
 // Per head: pairs = N (N - 1) / 2.
-//   qs, gs   [BH][pairs][64][64] bf16   Q_{a,b} and G_{a,b-1} (b >= 1)
-//   own      [BH][N][9][64][64] fp32     per chunk: dK (own-chunk step),
-//                                        dV (own chunk), dY, dU, dW (own
-//                                        chunk), dK~, dM, and the query
-//                                        kernel's dQ and dX partials, held
-//                                        there across its two loops
+//   qs, gs   [BH][pairs][64][64] bf16  Q_{a,b} and G_{a,b-1} (b >= 1), rows
+//                                      i with the d axis in slot order:
+//                                      qs[i][s] = Q_{a,b}[i][permk(s)]
+//   kp, kts, mn, mtn [BH][N][64][64] bf16, per chunk (slot order s):
+//            kp[j][s] = K~[j][permk(s)]          kts[e][s] = scale K~[permk(s)][e]
+//            mn[x][s] = -M[x][permk(s)]          mtn[y][s] = -M[permk(s)][y]
+//   own      [BH][N][11][64][64] fp32  per chunk: dK (own-chunk step), dV
+//                                      (own chunk), dY, dU, dW (own chunk),
+//                                      dK~, dM, the own-chunk dQ and
+//                                      d lower(Q W^T), Q~ and dQ~
 //   dsum     [BH][Lp] fp32   rowsum(dO o O) per query
 //   rsum     [BH][Lp] fp32   rowsum(dS) per query (all its keys)
 //   csd      [BH][Lp] fp32   colsum(dS) of the own-chunk step per key
 //   csl      [BH][Lp] fp32   colsum(dS) over the later query chunks per key
-// ut, yt, mt hold U, Y, M as row-major tiles once path_bwd_layout_kernel ran.
+// ut, yt hold U, Y as row-major tiles once path_bwd_layout_kernel ran.
 using BwdKArgs = BwdArgs;
 
 // ---------------------------------------------------------------------------
-// U, Y, M of one chunk from the prepare stage's operand layouts (permk = its
-// k-slot permutation) to row-major tiles, in place:
+// Per chunk: U, Y from the prepare stage's operand layouts to row-major
+// tiles, in place, and the chains' operand tiles.  The prepare stage's
+// layouts (permk = its k-slot permutation):
 //   ut[rho][sigma] = -U[permk(sigma)][permk(rho)]   -> U[m][e]
 //   yt[j][sigma]   =  Y[permk(sigma)][j]            -> Y[m][j]
-//   mt[rho][e]     = -M[e][permk(rho)]              -> M[x][y]
+//   mt[rho][e]     = -M[e][permk(rho)], so -M[x][permk(s)] = mt[s][x] and
+//                    -M[permk(s)][y] = mt[permk(y)][permk(s)]
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void path_bwd_layout_kernel(const BwdKArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 tU[BT], tY[BT], tM[BT];
+    __shared__ __attribute__((aligned(16))) bf16 tU[BT], tY[BT], tM[BT], tK[BT];
     const int tid = threadIdx.x;
-    const size_t base = (size_t)blockIdx.x * BC * BC;
+    const size_t base = (size_t)blockIdx.x * TT;
     bf16* ut = static_cast<bf16*>(a.ut) + base;
     bf16* yt = static_cast<bf16*>(a.yt) + base;
-    bf16* mt = static_cast<bf16*>(a.mt) + base;
-    bf16 xu[16], xy[16], xm[16];
+    const bf16* mt = static_cast<const bf16*>(a.mt) + base;
+    const Frag fk = fetch(static_cast<const bf16*>(a.kt) + base, BC, tid);   // K~ rows
+    bf16 xu[16], xy[16];
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
         const int u = tid + 256 * it;
         xu[it] = ut[u];
         xy[it] = yt[u];
-        xm[it] = mt[u];
     }
+    const Frag fm = fetch(mt, BC, tid);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
         const int u = tid + 256 * it, hi = u >> 6, lo = u & 63;
         tU[permk(lo) * BP + permk(hi)] = static_cast<bf16>(-static_cast<float>(xu[it]));
         tY[permk(lo) * BP + hi] = xy[it];
-        tM[lo * BP + permk(hi)] = static_cast<bf16>(-static_cast<float>(xm[it]));
     }
+    put(tM, fm, tid);          // mt as is
+    put(tK, fk, tid);          // K~ as is
     __syncthreads();
     store_tile(ut, tU, tid);
     store_tile(yt, tY, tid);
-    store_tile(mt, tM, tid);
+    bf16* kp = static_cast<bf16*>(a.kp) + base;
+    bf16* kts = static_cast<bf16*>(a.kts) + base;
+    bf16* mn = static_cast<bf16*>(a.mn) + base;
+    bf16* mtn = static_cast<bf16*>(a.mtn) + base;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = tid + 256 * it, r = u >> 3, s0 = (u & 7) * 8;
+        bf16x8 vkp, vkt, vmn, vmt;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int s = s0 + t, ps = permk(s);
+            vkp[t] = tK[r * BP + ps];
+            vkt[t] = static_cast<bf16>(a.scale * static_cast<float>(tK[ps * BP + r]));
+            vmn[t] = tM[s * BP + r];
+            vmt[t] = tM[permk(r) * BP + ps];
+        }
+        s8(kp + r * BC + s0, vkp);
+        s8(kts + r * BC + s0, vkt);
+        s8(mn + r * BC + s0, vmn);
+        s8(mtn + r * BC + s0, vmt);
+    }
 }
 
 // ---------------------------------------------------------------------------
-// Query-stationary: one workgroup (4 waves) per (head, query chunk a).
+// Own chunk of query chunk a (four waves, 64 x 64 LDS tiles): the chunk's
+// probabilities from S_aa, its dV, dK, dY contributions, the partial dQ and
+// d lower(Q W^T), rowsum(dO o O), the own row and column sums of dS, and Q~.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a) {
+__global__ __launch_bounds__(256, 2) void path_bwd_own_kernel(const BwdKArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 tA[BT], tB[BT], tC[BT], tD[BT], tE[BT], tF[BT],
         tX[BT], tXT[BT];
-    __shared__ float sLse[BC], sD[BC], sLoc[BC], sLocK[BC], sRow[BC], sCol[BC];
+    __shared__ float sLse[BC], sD[BC], sLoc[BC], sRow[BC], sCol[BC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = a.L, N = a.N, Lp = N * BC;
     int head, ca;
-    wg_map(blockIdx.x, a.BH, N, true, head, ca);
+    wg_map(blockIdx.x, a.BH, N, false, head, ca);
     const int p0 = ca * BC, nva = min(BC, L - p0);
     const size_t hrow = (size_t)head * L;      // input rows of the head
     const size_t wrow = (size_t)head * Lp;     // workspace rows of the head
@@ -270,21 +375,18 @@ __global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a
 
     const bf16* q = static_cast<const bf16*>(a.q) + (hrow + p0) * BC;
     const bf16* k = static_cast<const bf16*>(a.k) + (hrow + p0) * BC;
-    const bf16* vv = static_cast<const bf16*>(a.v);
+    const bf16* vv = static_cast<const bf16*>(a.v) + (hrow + p0) * BC;
     const bf16* w = static_cast<const bf16*>(a.w) + (hrow + p0) * BC;
     const bf16* o = static_cast<const bf16*>(a.out) + (hrow + p0) * BC;
     const bf16* dO = static_cast<const bf16*>(a.dout) + (hrow + p0) * BC;
-    const bf16* ktw = static_cast<const bf16*>(a.kt) + wrow * BC;
-    const bf16* un = static_cast<const bf16*>(a.ut) + (chunk0 + ca) * BC * BC;
-    const bf16* yn = static_cast<const bf16*>(a.yt) + (chunk0 + ca) * BC * BC;
-    const bf16* mn = static_cast<const bf16*>(a.mt) + chunk0 * BC * BC;
-    float* own = a.own + (chunk0 + ca) * NOWN * BC * BC;
+    const bf16* un = static_cast<const bf16*>(a.ut) + (chunk0 + ca) * TT;
+    const bf16* yn = static_cast<const bf16*>(a.yt) + (chunk0 + ca) * TT;
+    float* own = a.own + (chunk0 + ca) * NOWN * TT;
 
-    // ---- own chunk: S = scale (Q K^T - lower(X) Y) + gate, X = Q W^T ----
-    Frag fq = fetch(q, nva, tid), fw = fetch(w, nva, tid), fk = fetch(k, nva, tid);
+    // S = scale (Q K^T - lower(X) Y) + gate, X = Q W^T
+    const Frag fq = fetch(q, nva, tid), fw = fetch(w, nva, tid), fk = fetch(k, nva, tid);
     const Frag fy = fetch(yn, BC, tid), fo = fetch(dO, nva, tid);
-    const Frag fv = fetch(vv + (hrow + p0) * BC, nva, tid);
-    Frag fu = fetch(un, BC, tid);
+    const Frag fv = fetch(vv, nva, tid), fu = fetch(un, BC, tid);
     row_dots(sD, dO, o, nva, tid);
     if (tid < BC) {
         sLse[tid] = tid < nva ? a.lse[hrow + p0 + tid] * kLog2e : 0.f;
@@ -307,21 +409,26 @@ __global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a
     st_q<false>(tX, x, wave, lane);
     st_q<true>(tXT, x, wave, lane);
     __syncthreads();
-    f32x16 s = mm_nt(tA, tC, z16(), wave, lane);            // Q K^T
-    f32x16 xy = mm_nt(tX, tD, z16(), wave, lane);           // lower(X) Y
-    f32x16 dp = mm_nt(tE, tF, z16(), wave, lane);           // dO V^T
     f32x16 ds, pp;
+    {
+        const f32x16 s = mm_nt(tA, tC, z16(), wave, lane);      // Q K^T
+        const f32x16 xy = mm_nt(tX, tD, z16(), wave, lane);     // lower(X) Y
+        const f32x16 dp = mm_nt(tE, tF, z16(), wave, lane);     // dO V^T
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = qrow(wave, lane, v);
+            const float z = c2 * (s[v] - xy[v]) + (sLoc[i] - sLoc[n]);
+            const float p = (n <= i && i < nva) ? exp2f(z - sLse[i]) : 0.f;
+            pp[v] = p;
+            ds[v] = p * (dp[v] - sD[i]);
+        }
+    }
+    // row and column sums of the own chunk's dS
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        const int i = qrow(wave, lane, v);
-        const float z = c2 * (s[v] - xy[v]) + (sLoc[i] - sLoc[n]);
-        const float p = (n <= i && i < nva) ? exp2f(z - sLse[i]) : 0.f;
-        pp[v] = p;
-        ds[v] = p * (dp[v] - sD[i]);
+        const float r = wave_sum32(ds[v]);
+        if ((lane & 31) == 0) atomicAdd(&sRow[qrow(wave, lane, v)], r);
     }
-    // dS row sums accumulate per lane over every key chunk (one reduction
-    // at the end); column sums of the own chunk's dS
-    f32x16 rs = ds;
     {
         float cs = 0.f;
 #pragma unroll
@@ -337,116 +444,248 @@ __global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a
     put_t(tF, fq, tid);                       // Q^T [d][i]
     __syncthreads();
     // dV_own = P^T dO, dK_own = scale dS^T Q, dY = -scale lower(X)^T dS
-    st_qg(own + 1 * BC * BC, mm_nt(tD, tE, z16(), wave, lane), wave, lane);
-    st_qg(own + 0 * BC * BC, mm_nt(tC, tF, z16(), wave, lane), wave, lane, a.scale);
-    st_qg(own + 2 * BC * BC, mm_nt(tXT, tC, z16(), wave, lane), wave, lane, -a.scale);
+    st_qg(own + 1 * TT, mm_nt(tD, tE, z16(), wave, lane), wave, lane);
+    st_qg(own + 0 * TT, mm_nt(tC, tF, z16(), wave, lane), wave, lane, a.scale);
+    st_qg(own + 2 * TT, mm_nt(tXT, tC, z16(), wave, lane), wave, lane, -a.scale);
     __syncthreads();
     put_t(tD, fk, tid);                       // K^T [d][j]
     put(tE, fy, tid);                         // Y [m][j]
     put_t(tF, fu, tid);                       // U^T [e][m]
     __syncthreads();
     {
-        const f32x16 dq = mm_nt(tB, tD, z16(), wave, lane);      // dS K, unscaled
-        // dXl = -scale dS Y^T (lower)
+        // dQ (own chunk) = scale dS K; dXl = -scale dS Y^T (lower)
+        const f32x16 dq = mm_nt(tB, tD, z16(), wave, lane);
         f32x16 dxl = mm_nt(tB, tE, z16(), wave, lane);
 #pragma unroll
         for (int v = 0; v < 16; ++v) dxl[v] = (n <= qrow(wave, lane, v)) ? -a.scale * dxl[v] : 0.f;
-        st_qg(own + 7 * BC * BC, dq, wave, lane, a.scale);
-        st_qg(own + 8 * BC * BC, dxl, wave, lane);
+        st_qg(own + 7 * TT, dq, wave, lane, a.scale);
+        st_qg(own + 8 * TT, dxl, wave, lane);
     }
-
-    // ---- Q~ = Q - lower(X) U (the query carried to the chunk start) ----
-    f32x16 qc = mm_nt(tX, tF, z16(), wave, lane);           // lower(X) U
+    {
+        // Q~ = Q - lower(X) U, the query carried to the chunk start (fp32)
+        f32x16 qc = mm_nt(tX, tF, z16(), wave, lane);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) qc[v] = static_cast<float>(tA[qrow(wave, lane, v) * BP + n]) - qc[v];
+        for (int v = 0; v < 16; ++v) qc[v] = static_cast<float>(tA[qrow(wave, lane, v) * BP + n]) - qc[v];
+        st_qg(own + 9 * TT, qc, wave, lane);
+    }
+    if (tid < BC) {
+        a.rsum[wrow + p0 + tid] = sRow[tid];
+        a.csd[wrow + p0 + tid] = sCol[tid];
+    }
+}
 
-    // ---- right to left: Q_{a,b}, b = a-1 .. 0, stored ----
+// ---------------------------------------------------------------------------
+// The chains of two query chunks of a head (waves 0, 1: chunk a_hi = N-1-2p,
+// queries 0-31 and 32-63; waves 2, 3: chunk a_hi - 1), which share the
+// per-key-chunk operand tiles.  Each wave holds its 32 queries as columns of
+// 64 x 32 accumulator pairs (rows = the d or key axis).
+//   right to left:  Q^T <- Q^T + (-M_b^T) Q^T,   storing Q_{a,b}, b = a-1 .. 0;
+//   left to right:  S^T = K~_b Q^T, dP^T = V_b dO^T, dS^T,
+//                   G^T <- G^T + (-M_b) G^T + (scale K~_b^T) dS^T,
+//                   storing G_{a,b-1} (b >= 1); dQ~ = G_{a-1}.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16 tK[BT], tKT[BT], tV[BT], tM[BT];
+    __shared__ __attribute__((aligned(16))) float sLocK[BC];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = a.L, N = a.N, Lp = N * BC, NP = N / 2;
+    int head, pr;
+    wg_map(blockIdx.x, a.BH, NP, false, head, pr);
+    const int ahi = N - 1 - 2 * pr;
+    const int ca = ahi - (wave >> 1);              // this wave's query chunk
+    const bool has = ca >= 1;                      // chunk 0 has no chain
+    const int i = 32 * (wave & 1) + l32;           // the lane's query within the chunk
+    const int row = ca * BC + i;
+    const bool valid = row < L;
+    const size_t hrow = (size_t)head * L, wrow = (size_t)head * Lp, chunk0 = (size_t)head * N;
+    const bool gate = a.loc != nullptr;
+    const float c2 = a.scale * kLog2e;
     const size_t pairs = (size_t)N * (N - 1) / 2;
-    bf16* qs = static_cast<bf16*>(a.qs) + (size_t)head * pairs * BC * BC;
-    bf16* gs = static_cast<bf16*>(a.gs) + (size_t)head * pairs * BC * BC;
-    // M_b and M_{b-1} in flight
-    Frag fm = {}, fm1 = {};
-    if (ca - 1 >= 1) fm = fetch(mn + (size_t)(ca - 1) * BC * BC, BC, tid);
-    if (ca - 2 >= 1) fm1 = fetch(mn + (size_t)(ca - 2) * BC * BC, BC, tid);
-    for (int b = ca - 1; b >= 0; --b) {
-        __syncthreads();
-        st_q<false>(tB, qc, wave, lane);                    // Q_{a,b}
-        if (b >= 1) put_t(tC, fm, tid);                     // M_b^T [y][x]
-        __syncthreads();
-        fm = fm1;
-        if (b - 2 >= 1) fm1 = fetch(mn + (size_t)(b - 2) * BC * BC, BC, tid);
-        store_tile(qs + pair_index(ca, b) * BC * BC, tB, tid);
-        if (b >= 1) {
-            const f32x16 qm = mm_nt(tB, tC, z16(), wave, lane);   // Q M_b
+    bf16* qs = static_cast<bf16*>(a.qs) + (size_t)head * pairs * TT;
+    bf16* gs = static_cast<bf16*>(a.gs) + (size_t)head * pairs * TT;
+    const bf16* kp = static_cast<const bf16*>(a.kp) + chunk0 * TT;
+    const bf16* kts = static_cast<const bf16*>(a.kts) + chunk0 * TT;
+    const bf16* mn = static_cast<const bf16*>(a.mn) + chunk0 * TT;
+    const bf16* mtn = static_cast<const bf16*>(a.mtn) + chunk0 * TT;
+    const bf16* vv = static_cast<const bf16*>(a.v) + hrow * BC;
+    float* own = a.own + (chunk0 + ca) * NOWN * TT;
+
+    // ---- right to left ----
+    f32x16 q[2];
+    {
+        // Q~ (fp32 rows) into the accumulator layout: register v of tile blk
+        // holds d = 32 blk + 8 (v >> 2) + 4 hh + (v & 3)
+        const float* qf = own + 9 * TT + i * BC;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) qc[v] -= qm[v];
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                f32x4 x4 = {0.f, 0.f, 0.f, 0.f};
+                if (has) x4 = *reinterpret_cast<const f32x4*>(qf + 32 * blk + 8 * g4 + 4 * hh);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) q[blk][4 * g4 + r] = x4[r];
+            }
+    }
+    Frag fmt = {};
+    if (ahi - 1 >= 1) fmt = fetch(mtn + (size_t)(ahi - 1) * TT, BC, tid);
+    for (int b = ahi - 1; b >= 0; --b) {
+        const bool mine = has && b <= ca - 1;
+        bf16x8 qb[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = bop(q, ks);
+        if (mine) {
+            bf16* dst = qs + pair_index(ca, b) * TT + i * BC + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s8(dst + 16 * ks, qb[ks]);
+        }
+        if (b >= 1) {
+            __syncthreads();
+            put(tM, fmt, tid);                            // -M_b^T, k in slot order
+            __syncthreads();
+            if (b - 1 >= 1) fmt = fetch(mtn + (size_t)(b - 1) * TT, BC, tid);
+            if (mine) mm2(q, tM, qb, lane);
         }
     }
-    // ---- left to right: dS_ab, the adjoint G, dQ_{a,b} ----
-    double fsum = 0.0;                                       // sum of csum over chunks b+1 .. a (log2)
-    if (gate)
-        for (int c = 1; c <= ca; ++c) fsum += static_cast<double>(a.csum[chunk0 + c]);
-    f32x16 g = z16();
-    Frag fQ = {}, fK = {}, fV = {};
-    float locK = 0.f;
-    // csum of chunk b + 1, subtracted at the end of step b (loaded a step ahead)
-    float cs_cur = (gate && ca >= 1) ? a.csum[chunk0 + 1] : 0.f, cs_nxt = 0.f;
-    __syncthreads();                                         // Q_{a,b} stores visible
-    if (ca >= 1) {
-        fQ = fetch(qs + pair_index(ca, 0) * BC * BC, BC, tid);
-        fK = fetch(ktw, BC, tid);
-        fV = fetch(vv + hrow * BC, BC, tid);
-        if (gate && tid < BC) locK = a.loc[wrow + tid];
+
+    // ---- left to right ----
+    const float lse2 = (has && valid) ? a.lse[hrow + row] * kLog2e : 0.f;
+    const float Di = has ? a.dsum[wrow + row] : 0.f;
+    const float locQ = (gate && has) ? a.loc[wrow + row] : 0.f;
+    bf16x8 dob[4];                                        // dO^T as the B operand (d natural)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        dob[ks] = bf16x8{};
+        if (has && valid) dob[ks] = l8(static_cast<const bf16*>(a.dout) + (hrow + row) * BC + 16 * ks + 8 * hh);
     }
-    put(tE, fetch(dO, nva, tid), tid);                       // dO [i][d]
-    for (int b = 0; b < ca; ++b) {
+    double fsum = 0.0;                                    // sum of csum over chunks b+1 .. a (log2)
+    if (gate && has)
+        for (int c = 1; c <= ca; ++c) fsum += static_cast<double>(a.csum[chunk0 + c]);
+    f32x16 g[2] = {z16(), z16()};
+    float rs = 0.f;
+    Frag fK = {}, fKT = {}, fV = {}, fM = {};
+    float locK = 0.f;
+    bf16x8 qn[4] = {};
+    if (ahi >= 1) {
+        fK = fetch(kp, BC, tid);
+        fKT = fetch(kts, BC, tid);
+        fV = fetch(vv, BC, tid);
+        if (gate && tid < BC) locK = a.loc[wrow + tid];
+        if (has) {
+            const bf16* src = qs + pair_index(ca, 0) * TT + i * BC + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) qn[ks] = l8(src + 16 * ks);
+        }
+    }
+    for (int b = 0; b < ahi; ++b) {
+        const bool mine = has && b <= ca - 1;
         __syncthreads();
-        put(tA, fQ, tid);                                    // Q_{a,b}
-        put(tC, fK, tid);                                    // K~_b [j][d]
-        put_t(tD, fK, tid);                                  // K~_b^T [d][j]
-        put(tF, fV, tid);                                    // V_b (chunks left of a are full)
-        if (b >= 1) put(tB, fm, tid);                        // M_b [x][y]
-        st_q<false>(tX, g, wave, lane);                      // G_{b-1}
+        put(tK, fK, tid);                                 // K~_b, d in slot order
+        put(tKT, fKT, tid);                               // scale K~_b^T, keys in slot order
+        put(tV, fV, tid);                                 // V_b (chunks left of a are full)
+        if (b >= 1) put(tM, fM, tid);                     // -M_b, k in slot order
         if (tid < BC) sLocK[tid] = locK;
         __syncthreads();
-        if (b + 1 < ca) {                                    // the next step's tiles
-            fQ = fetch(qs + pair_index(ca, b + 1) * BC * BC, BC, tid);
-            fK = fetch(ktw + (size_t)(b + 1) * BC * BC, BC, tid);
-            fV = fetch(vv + (hrow + (size_t)(b + 1) * BC) * BC, BC, tid);
-            fm = fetch(mn + (size_t)(b + 1) * BC * BC, BC, tid);
+        bf16x8 qc[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qc[ks] = qn[ks];
+        if (b + 1 < ahi) {                                // the next step's operands
+            fK = fetch(kp + (size_t)(b + 1) * TT, BC, tid);
+            fKT = fetch(kts + (size_t)(b + 1) * TT, BC, tid);
+            fV = fetch(vv + (size_t)(b + 1) * TT, BC, tid);
+            fM = fetch(mn + (size_t)(b + 1) * TT, BC, tid);
             if (gate && tid < BC) locK = a.loc[wrow + (size_t)(b + 1) * BC + tid];
+            if (has && b + 1 <= ca - 1) {
+                const bf16* src = qs + pair_index(ca, b + 1) * TT + i * BC + 8 * hh;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) qn[ks] = l8(src + 16 * ks);
+            }
         }
-        if (gate && b + 2 <= ca) cs_nxt = a.csum[chunk0 + b + 2];
-        if (b >= 1) store_tile(gs + pair_index(ca, b) * BC * BC, tX, tid);
-        const float bias_q = static_cast<float>(fsum);
-        const f32x16 sb = mm_nt(tA, tC, z16(), wave, lane);  // Q_{a,b} K~_b^T
-        const f32x16 db = mm_nt(tE, tF, z16(), wave, lane);  // dO V_b^T
-        f32x16 dsb;
+        const float csn = (gate && has && b + 1 <= ca) ? a.csum[chunk0 + b + 1] : 0.f;
+        if (mine) {
+            f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
+            mm2(s, tK, qc, lane);                          // S^T[j][i], unscaled
+            mm2(dp, tV, dob, lane);                        // dP^T[j][i]
+            // row offset of query i: the gate's local term and chunk sums, -lse
+            const float rq = valid ? (locQ + static_cast<float>(fsum) - lse2) : -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = qrow(wave, lane, v);
-            const float z = c2 * sb[v] + (gate ? sLoc[i] + bias_q - sLocK[n] : 0.f);
-            const float p = i < nva ? exp2f(z - sLse[i]) : 0.f;
-            dsb[v] = p * (db[v] - sD[i]);
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const f32x4 lk = *reinterpret_cast<const f32x4*>(sLocK + 32 * blk + 8 * g4 + 4 * hh);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int v = 4 * g4 + r;
+                        const float p = exp2f(c2 * s[blk][v] + rq - lk[r]);
+                        const float d = p * (dp[blk][v] - Di);
+                        rs += d;
+                        s[blk][v] = d;                     // dS^T
+                    }
+                }
+            bf16x8 db[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) db[ks] = bop(s, ks);
+            if (b >= 1) {
+                bf16x8 gb[4];
+                bf16* dst = gs + pair_index(ca, b) * TT + i * BC + 8 * hh;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    gb[ks] = bop(g, ks);
+                    s8(dst + 16 * ks, gb[ks]);             // G_{a,b-1}
+                }
+                mm2(g, tM, gb, lane);                      // G^T - M_b G^T
+            }
+            mm2(g, tKT, db, lane);                         // + scale K~_b^T dS^T
         }
-#pragma unroll
-        for (int v = 0; v < 16; ++v) rs[v] += dsb[v];
-        f32x16 gm = z16();
-        if (b >= 1) gm = mm_nt(tX, tB, z16(), wave, lane);   // G_{b-1} M_b^T
-        __syncthreads();                                     // tB, tX reads done
-        st_q<false>(tB, dsb, wave, lane);                    // dS [i][j]
-        __syncthreads();
-        const f32x16 dqb = mm_nt(tB, tD, z16(), wave, lane); // dS K~_b
-#pragma unroll
-        for (int v = 0; v < 16; ++v) g[v] = a.scale * dqb[v] + (b >= 1 ? g[v] - gm[v] : 0.f);
-        fsum -= static_cast<double>(cs_cur);
-        cs_cur = cs_nxt;
+        fsum -= static_cast<double>(csn);
     }
-    // ---- dQ~ = G_{a-1}: Q~ backward.  dQ += dQ~ ; dXl += -(dQ~ U^T) lower ;
-    // dU = -lower(X)^T dQ~ ; then dQ += dXl W, dW_own = dXl^T Q ----
-    fu = fetch(un, BC, tid);
-    fw = fetch(w, nva, tid);
-    fq = fetch(q, nva, tid);
+    if (has) {
+        rs += __shfl_xor(rs, 32, 64);
+        if (hh == 0 && valid) a.rsum[wrow + row] += rs;
+        float* gf = own + 10 * TT + i * BC;                // dQ~ = G_{a-1}, fp32 rows
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 x4 = {g[blk][4 * g4], g[blk][4 * g4 + 1], g[blk][4 * g4 + 2], g[blk][4 * g4 + 3]};
+                *reinterpret_cast<f32x4*>(gf + 32 * blk + 8 * g4 + 4 * hh) = x4;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ~ through Q~ = Q - lower(X) U, X = Q W^T (four waves, LDS tiles):
+// dQ = dQ_own + dQ~ + dXl W, dXl = dXl_own - lower(dQ~ U^T),
+// dU = -lower(X)^T dQ~, dW_own = dXl^T Q.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void path_bwd_own_end_kernel(const BwdKArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16 tA[BT], tB[BT], tC[BT], tD[BT], tF[BT], tXT[BT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int L = a.L, N = a.N;
+    int head, ca;
+    wg_map(blockIdx.x, a.BH, N, false, head, ca);
+    const int p0 = ca * BC, nva = min(BC, L - p0);
+    const size_t hrow = (size_t)head * L, chunk0 = (size_t)head * N;
+    const int n = qcol(wave, lane);
+    const bf16* q = static_cast<const bf16*>(a.q) + (hrow + p0) * BC;
+    const bf16* w = static_cast<const bf16*>(a.w) + (hrow + p0) * BC;
+    const bf16* un = static_cast<const bf16*>(a.ut) + (chunk0 + ca) * TT;
+    float* own = a.own + (chunk0 + ca) * NOWN * TT;
+
+    const Frag fq = fetch(q, nva, tid), fw = fetch(w, nva, tid), fu = fetch(un, BC, tid);
+    put(tA, fq, tid);                                        // Q [i][d]
+    put(tB, fw, tid);                                        // W [m][d]
+    __syncthreads();
+    {
+        f32x16 x = mm_nt(tA, tB, z16(), wave, lane);         // X[i][m]
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (n > qrow(wave, lane, v)) x[v] = 0.f;
+        st_q<true>(tXT, x, wave, lane);                      // lower(X)^T [m][i]
+    }
+    const f32x16 g = ca >= 1 ? ld_qg(own + 10 * TT, wave, lane) : z16();   // dQ~ [i][e]
     __syncthreads();
     st_q<false>(tA, g, wave, lane);                          // dQ~ [i][e]
     st_q<true>(tB, g, wave, lane);                           // dQ~^T [e][i]
@@ -455,156 +694,166 @@ __global__ __launch_bounds__(256, 2) void path_bwd_query_kernel(const BwdKArgs a
     put_t(tF, fq, tid);                                      // Q^T [d][i]
     __syncthreads();
     const f32x16 du = mm_nt(tA, tC, z16(), wave, lane);      // (dQ~ U^T)[i][m]
-    f32x16 dq = ld_qg(own + 7 * BC * BC, wave, lane);
-    f32x16 dxl = ld_qg(own + 8 * BC * BC, wave, lane);
+    f32x16 dq = ld_qg(own + 7 * TT, wave, lane);
+    f32x16 dxl = ld_qg(own + 8 * TT, wave, lane);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         dq[v] += g[v];
         dxl[v] -= (n <= qrow(wave, lane, v)) ? du[v] : 0.f;
     }
-    // dU = -lower(X)^T dQ~: rows m, cols e
-    st_qg(own + 3 * BC * BC, mm_nt(tXT, tB, z16(), wave, lane), wave, lane, -1.f);
+    st_qg(own + 3 * TT, mm_nt(tXT, tB, z16(), wave, lane), wave, lane, -1.f);   // dU [m][e]
     __syncthreads();
     st_q<false>(tA, dxl, wave, lane);                        // dXl [i][m]
     st_q<true>(tB, dxl, wave, lane);                         // dXl^T [m][i]
     __syncthreads();
     const f32x16 dqw = mm_nt(tA, tD, z16(), wave, lane);     // dXl W
-    st_qg(own + 4 * BC * BC, mm_nt(tB, tF, z16(), wave, lane), wave, lane);   // dW_own = dXl^T Q
-    {
-        float* dqg = a.dq + (hrow + p0) * BC;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = qrow(wave, lane, v);
-            if (i < nva) dqg[(size_t)i * BC + n] = dq[v] + dqw[v];
-        }
-    }
-    __syncthreads();
+    st_qg(own + 4 * TT, mm_nt(tB, tF, z16(), wave, lane), wave, lane);   // dW_own = dXl^T Q
+    float* dqg = a.dq + (hrow + p0) * BC;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-        const float r = wave_sum32(rs[v]);
-        if ((lane & 31) == 0) atomicAdd(&sRow[qrow(wave, lane, v)], r);
-    }
-    __syncthreads();
-    if (tid < BC) {
-        a.rsum[wrow + p0 + tid] = sRow[tid];
-        a.csd[wrow + p0 + tid] = sCol[tid];
+        const int i = qrow(wave, lane, v);
+        if (i < nva) dqg[(size_t)i * BC + n] = dq[v] + dqw[v];
     }
 }
 
 // ---------------------------------------------------------------------------
-// Key-stationary: one workgroup per (head, key chunk b): dV, dK~ and dM
-// summed over the query chunks a > b.
+// Key chunk b (two waves; wave h holds keys 32 h .. 32 h + 31 as the columns
+// of its accumulators), summed over the query chunks a > b:
+//   S = Q_{a,b} K~_b^T, dP = dO_a V_b^T, P, dS (rows = queries);
+//   dV^T += dO_a^T P, dK~^T += Q_{a,b}^T dS, dM += Q_{a,b}^T G_{a,b-1}
+// (dM: wave h forms the columns 32 h .. 32 h + 31).  The k axis of the last
+// three is the query axis, in slot order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void path_bwd_key_kernel(const BwdKArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 tA[BT], tB[BT], tC[BT], tD[BT], tE[BT], tF[BT],
-        tH[BT], tI[BT];
-    __shared__ float sLse[BC], sD[BC], sLocQ[BC], sLocK[BC], sCol[BC];
+__global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
+    __shared__ __attribute__((aligned(16))) bf16 tQ[BT], tQT[BT], tO[BT], tOT[BT], tGT[BT];
+    __shared__ __attribute__((aligned(16))) float sRq[BC], sD[BC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
     const int L = a.L, N = a.N, Lp = N * BC;
     int head, cb;
     wg_map(blockIdx.x, a.BH, N, false, head, cb);
     const int p0 = cb * BC, nvb = min(BC, L - p0);
-    const size_t hrow = (size_t)head * L, wrow = (size_t)head * Lp;
-    const size_t chunk0 = (size_t)head * N;
+    const int j = 32 * wave + l32;                  // the lane's key within the chunk
+    const size_t hrow = (size_t)head * L, wrow = (size_t)head * Lp, chunk0 = (size_t)head * N;
     const bool gate = a.loc != nullptr;
     const float c2 = a.scale * kLog2e;
-    const int n = qcol(wave, lane);
-
-    const bf16* vv = static_cast<const bf16*>(a.v);
-    const bf16* dOg = static_cast<const bf16*>(a.dout);
-    const bf16* ktw = static_cast<const bf16*>(a.kt) + wrow * BC;
     const size_t pairs = (size_t)N * (N - 1) / 2;
-    const bf16* qs = static_cast<const bf16*>(a.qs) + (size_t)head * pairs * BC * BC;
-    const bf16* gs = static_cast<const bf16*>(a.gs) + (size_t)head * pairs * BC * BC;
-    float* own = a.own + (chunk0 + cb) * NOWN * BC * BC;
+    const bf16* qs = static_cast<const bf16*>(a.qs) + (size_t)head * pairs * TT;
+    const bf16* gs = static_cast<const bf16*>(a.gs) + (size_t)head * pairs * TT;
+    const bf16* dOg = static_cast<const bf16*>(a.dout) + hrow * BC;
+    float* own = a.own + (chunk0 + cb) * NOWN * TT;
 
-    // the tiles and per-query scalars of query chunk ca, in flight
-    Frag fQ = {}, fO = {}, fG = {};
-    float lse_n = 0.f, dsum_n = 0.f, loc_n = 0.f, cs_n = 0.f;
-    auto prefetch = [&](int ca) {
-        const int pa = ca * BC, nva = min(BC, L - pa);
-        if (gate) cs_n = a.csum[chunk0 + ca];
-        fQ = fetch(qs + pair_index(ca, cb) * BC * BC, BC, tid);
-        fO = fetch(dOg + (hrow + pa) * BC, nva, tid);
-        if (cb >= 1) fG = fetch(gs + pair_index(ca, cb) * BC * BC, BC, tid);
+    // the key's B operands: K~ (d in slot order, as the stored queries) and V
+    bf16x8 kb[4], vb[4];
+    {
+        const bf16* kr = static_cast<const bf16*>(a.kp) + (chunk0 + cb) * TT + j * BC + 8 * hh;
+        const bf16* vr = static_cast<const bf16*>(a.v) + (hrow + p0 + j) * BC + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            kb[ks] = l8(kr + 16 * ks);
+            vb[ks] = bf16x8{};
+            if (j < nvb) vb[ks] = l8(vr + 16 * ks);
+        }
+    }
+    const float locK = gate ? a.loc[wrow + p0 + j] : 0.f;
+
+    // query chunk ca's tiles and per-query row terms, in flight
+    Frag4 fQ = {}, fO = {}, fG = {};
+    float rq_n = 0.f, d_n = 0.f;
+    double fpre = 0.0;              // sum of csum over chunks b+1 .. ca, for the prefetch
+    auto prefetch = [&](int cn) {
+        const int pa = cn * BC, nva = min(BC, L - pa);
+        fQ = fetch4(qs + pair_index(cn, cb) * TT, BC, tid);
+        fO = fetch4(dOg + (size_t)pa * BC, nva, tid);
+        if (cb >= 1) fG = fetch4(gs + pair_index(cn, cb) * TT, BC, tid);
+        if (gate) fpre += static_cast<double>(a.csum[chunk0 + cn]);
         if (tid < BC) {
-            lse_n = tid < nva ? a.lse[hrow + pa + tid] * kLog2e : 0.f;
-            dsum_n = a.dsum[wrow + pa + tid];
-            loc_n = gate ? a.loc[wrow + pa + tid] : 0.f;
+            rq_n = tid < nva ? (gate ? a.loc[wrow + pa + tid] : 0.f) + static_cast<float>(fpre) -
+                                   a.lse[hrow + pa + tid] * kLog2e
+                             : -INFINITY;
+            d_n = a.dsum[wrow + pa + tid];
         }
     };
     if (cb + 1 < N) prefetch(cb + 1);
-    {
-        const Frag fk = fetch(ktw + (size_t)cb * BC * BC, BC, tid);
-        const Frag fv = fetch(vv + (hrow + p0) * BC, nvb, tid);
-        put(tA, fk, tid);                                            // K~_b [j][d]
-        put(tB, fv, tid);                                            // V_b [j][d]
-    }
-    if (tid < BC) {
-        sLocK[tid] = gate ? a.loc[wrow + p0 + tid] : 0.f;
-        sCol[tid] = 0.f;
-    }
-    f32x16 dv = z16(), dkt = z16(), dm = z16();
-    double fsum = 0.0;     // sum of csum over chunks b+1 .. a
+    f32x16 dv[2] = {z16(), z16()}, dk[2] = {z16(), z16()}, dm[2] = {z16(), z16()};
+    float cs = 0.f;
     for (int ca = cb + 1; ca < N; ++ca) {
-        const int nva = min(BC, L - ca * BC);
-        fsum += static_cast<double>(cs_n);
         __syncthreads();
-        put(tC, fQ, tid);                                            // Q_{a,b} [i][d]
-        put_t(tD, fQ, tid);                                          // Q_{a,b}^T [d][i]
-        put(tE, fO, tid);                                            // dO_a [i][d]
-        put_t(tF, fO, tid);                                          // dO_a^T [d][i]
-        if (cb >= 1) put_t(tH, fG, tid);                             // G^T [y][i]
+        put4(tQ, fQ, tid);                                   // Q_{a,b} [i][slot]
+        put4_tp<true>(tQT, fQ, tid);                         // Q_{a,b}^T [x][slot of i]
+        put4(tO, fO, tid);                                   // dO_a [i][d]
+        put4_tp<false>(tOT, fO, tid);                        // dO_a^T [d][slot of i]
+        if (cb >= 1) put4_tp<true>(tGT, fG, tid);            // G^T [y][slot of i]
         if (tid < BC) {
-            sLse[tid] = lse_n;
-            sD[tid] = dsum_n;
-            sLocQ[tid] = loc_n;
+            sRq[tid] = rq_n;
+            sD[tid] = d_n;
         }
         __syncthreads();
         if (ca + 1 < N) prefetch(ca + 1);
-        const float bias_q = static_cast<float>(fsum);
-        const f32x16 sb = mm_nt(tC, tA, z16(), wave, lane);         // Q K~^T [i][j]
-        const f32x16 db = mm_nt(tE, tB, z16(), wave, lane);         // dO V^T [i][j]
-        f32x16 pq, dsq;
+        f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
+        mm2(s, tQ, kb, lane);                                 // S[i][j], unscaled
+        mm2(dp, tO, vb, lane);                                // dP[i][j]
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int i = qrow(wave, lane, v);
-            const float z = c2 * sb[v] + (gate ? sLocQ[i] + bias_q - sLocK[n] : 0.f);
-            const float p = i < nva ? exp2f(z - sLse[i]) : 0.f;
-            pq[v] = p;
-            dsq[v] = p * (db[v] - sD[i]);
-        }
-        {
-            float cs = 0.f;
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) cs += dsq[v];
-            cs += __shfl_xor(cs, 32, 64);
-            if (lane < 32) atomicAdd(&sCol[n], cs);
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const f32x4 rq = *reinterpret_cast<const f32x4*>(sRq + 32 * blk + 8 * g4 + 4 * hh);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * blk + 8 * g4 + 4 * hh);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int v = 4 * g4 + r;
+                    const float p = exp2f(c2 * s[blk][v] + rq[r] - locK);
+                    const float d = p * (dp[blk][v] - d4[r]);
+                    cs += d;
+                    s[blk][v] = p;
+                    dp[blk][v] = d;
+                }
+            }
+        bf16x8 pb[4], db[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            pb[ks] = bop(s, ks);
+            db[ks] = bop(dp, ks);
         }
-        // P^T, dS^T as [j][i] tiles (over tE: dO rows are no longer needed)
-        __syncthreads();
-        st_q<true>(tE, pq, wave, lane);                              // P^T [j][i]
-        st_q<true>(tI, dsq, wave, lane);                             // dS^T [j][i]
-        __syncthreads();
-        dv = mm_nt(tE, tF, dv, wave, lane);                          // P^T dO   [j][d]
-        dkt = mm_nt(tI, tD, dkt, wave, lane);                        // dS^T Q   [j][d] (unscaled)
-        if (cb >= 1) dm = mm_nt(tD, tH, dm, wave, lane);             // Q^T G    [x][y]
+        mm2(dv, tOT, pb, lane);                               // dV^T[e][j]
+        mm2(dk, tQT, db, lane);                               // dK~^T[e][j], unscaled
+        if (cb >= 1) {
+            bf16x8 gb[4];
+            const bf16* gr = tGT + j * BP + 8 * hh;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) gb[ks] = l8(gr + 16 * ks);
+            mm2(dm, tQT, gb, lane);                           // (Q^T G)[x][y], y = j
+        }
     }
-    // dV = P^T dO (later queries) + own chunk; dK~ and dM for the UT kernel
+    // dV = the later queries' part + the own chunk's; dK~ (scaled) and dM
+    // for the UT kernel; the column sums of dS
     {
-        const f32x16 dvo = ld_qg(own + 1 * BC * BC, wave, lane);
-        float* dvg = a.dv + (hrow + p0) * BC;
+        const float* dvo = own + 1 * TT + j * BC;
+        float* dvg = a.dv + (hrow + p0 + j) * BC;
+        float* dkt = own + 5 * TT + j * BC;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int j = qrow(wave, lane, v);
-            if (j < nvb) dvg[(size_t)j * BC + n] = dv[v] + dvo[v];
-        }
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int e = 32 * blk + 8 * g4 + 4 * hh;
+                const f32x4 o4 = *reinterpret_cast<const f32x4*>(dvo + e);
+                const f32x4 v4 = {dv[blk][4 * g4] + o4[0], dv[blk][4 * g4 + 1] + o4[1],
+                                  dv[blk][4 * g4 + 2] + o4[2], dv[blk][4 * g4 + 3] + o4[3]};
+                if (j < nvb) *reinterpret_cast<f32x4*>(dvg + e) = v4;
+                const f32x4 k4 = {a.scale * dk[blk][4 * g4], a.scale * dk[blk][4 * g4 + 1],
+                                  a.scale * dk[blk][4 * g4 + 2], a.scale * dk[blk][4 * g4 + 3]};
+                *reinterpret_cast<f32x4*>(dkt + e) = k4;
+            }
+        float* dmg = own + 6 * TT;                           // dM[x][y] = -(Q^T G)[x][y]
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                dmg[(32 * blk + 8 * (v >> 2) + 4 * hh + (v & 3)) * BC + j] = -dm[blk][v];
     }
-    st_qg(own + 5 * BC * BC, dkt, wave, lane, a.scale);
-    st_qg(own + 6 * BC * BC, dm, wave, lane, -1.f);
-    __syncthreads();
-    if (tid < BC) a.csl[wrow + p0 + tid] = sCol[tid];
+    cs += __shfl_xor(cs, 32, 64);
+    if (hh == 0) a.csl[wrow + p0 + j] = cs;
 }
 
 // ---------------------------------------------------------------------------
@@ -861,12 +1110,14 @@ __global__ __launch_bounds__(256) void path_bwd_gate_kernel(const BwdKArgs a) {
 }
 
 hipError_t launch_path_bwd(const BwdArgs& a, hipStream_t s) {
-    const dim3 grid(a.BH * a.N), block(256);
-    hipLaunchKernelGGL(path_bwd_layout_kernel, grid, block, 0, s, a);
-    hipLaunchKernelGGL(path_bwd_query_kernel, grid, block, 0, s, a);
-    hipLaunchKernelGGL(path_bwd_key_kernel, grid, block, 0, s, a);
-    hipLaunchKernelGGL(path_bwd_ut_kernel, grid, block, 0, s, a);
-    if (a.log_f) hipLaunchKernelGGL(path_bwd_gate_kernel, dim3(a.BH), block, 0, s, a);
+    const dim3 grid(a.BH * a.N);
+    hipLaunchKernelGGL(path_bwd_layout_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(path_bwd_own_kernel, grid, dim3(256), 0, s, a);
+    if (a.N >= 2) hipLaunchKernelGGL(path_bwd_chain_kernel, dim3(a.BH * (a.N / 2)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(path_bwd_own_end_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(path_bwd_key_kernel, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(path_bwd_ut_kernel, grid, dim3(256), 0, s, a);
+    if (a.log_f) hipLaunchKernelGGL(path_bwd_gate_kernel, dim3(a.BH), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -241,7 +241,8 @@ struct BwdArgs {
     const float* beta; const float* log_f;   // log_f null without the gate
     const void* out; const float* lse; const void* dout;
     float* dq; float* dk; float* dv; float* dw; float* dbeta; float* dlogf;
-    const void* kt; void* ut; void* yt; void* mt;   // U, Y, M: made row-major in place
+    const void* kt; void* ut; void* yt; const void* mt;   // U, Y: made row-major in place
+    void* kp; void* kts; void* mn; void* mtn;             // the chains' operand tiles
     const float* loc; const float* csum;
     void* qs; void* gs; float* own; float* dsum; float* rsum; float* csd; float* csl;
     int BH, L, N;
@@ -250,7 +251,7 @@ struct BwdArgs {
 
 struct BwdWorkspace {
     Workspace fwd;         // kt, ut, yt, mt, loc, csum of the forward's prepare stage
-    size_t qs, gs, own, dsum, rsum, csd, csl, total;
+    size_t kp, kts, mn, mtn, qs, gs, own, dsum, rsum, csd, csl, total;
 };
 
 inline BwdWorkspace plan_bwd_workspace(size_t BH, size_t L) {
@@ -265,9 +266,13 @@ inline BwdWorkspace plan_bwd_workspace(size_t BH, size_t L) {
     b.fwd.mt = take(BH * N * D * D * 2);
     b.fwd.loc = take(BH * Lp * 4);
     b.fwd.csum = take(BH * N * 4);
+    b.kp = take(BH * N * C * D * 2);
+    b.kts = take(BH * N * C * D * 2);
+    b.mn = take(BH * N * D * D * 2);
+    b.mtn = take(BH * N * D * D * 2);
     b.qs = take(BH * pairs * C * D * 2);
     b.gs = take(BH * pairs * C * D * 2);
-    b.own = take(BH * N * 9 * C * D * 4);
+    b.own = take(BH * N * 11 * C * D * 4);
     b.dsum = take(BH * Lp * 4);
     b.rsum = take(BH * Lp * 4);
     b.csd = take(BH * Lp * 4);
