@@ -486,7 +486,8 @@ __global__ __launch_bounds__(256, 2) void path_bwd_own_kernel(const BwdKArgs a) 
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 tK[BT], tKT[BT], tV[BT], tM[BT];
-    __shared__ __attribute__((aligned(16))) float sLocK[BC];
+    // sLocK[0..63]: the key chunk's gate terms; sLocK[64]: csum of chunk b + 1
+    __shared__ __attribute__((aligned(16))) float sLocK[BC + 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -564,14 +565,19 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
         for (int c = 1; c <= ca; ++c) fsum += static_cast<double>(a.csum[chunk0 + c]);
     f32x16 g[2] = {z16(), z16()};
     float rs = 0.f;
+    // the next step's operands in flight; locK: lanes 0-63 the key chunk's
+    // gate terms, thread 64 the csum that step subtracts (loaded as data of
+    // the step, so that no wait for it comes before the step's stage)
     Frag fK = {}, fKT = {}, fV = {}, fM = {};
-    float locK = 0.f;
+    float locK = 0.f, csK = 0.f;     // (separate registers: a load in flight into
+                                     // one is never overwritten, which would wait)
     bf16x8 qn[4] = {};
     if (ahi >= 1) {
         fK = fetch(kp, BC, tid);
         fKT = fetch(kts, BC, tid);
         fV = fetch(vv, BC, tid);
         if (gate && tid < BC) locK = a.loc[wrow + tid];
+        if (gate && tid == BC) csK = a.csum[chunk0 + 1];
         if (has) {
             const bf16* src = qs + pair_index(ca, 0) * TT + i * BC + 8 * hh;
 #pragma unroll
@@ -586,6 +592,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
         put(tV, fV, tid);                                 // V_b (chunks left of a are full)
         if (b >= 1) put(tM, fM, tid);                     // -M_b, k in slot order
         if (tid < BC) sLocK[tid] = locK;
+        if (tid == BC) sLocK[BC] = csK;
         __syncthreads();
         bf16x8 qc[4];
 #pragma unroll
@@ -596,13 +603,13 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
             fV = fetch(vv + (size_t)(b + 1) * TT, BC, tid);
             fM = fetch(mn + (size_t)(b + 1) * TT, BC, tid);
             if (gate && tid < BC) locK = a.loc[wrow + (size_t)(b + 1) * BC + tid];
+            if (gate && tid == BC && b + 2 < N) csK = a.csum[chunk0 + b + 2];
             if (has && b + 1 <= ca - 1) {
                 const bf16* src = qs + pair_index(ca, b + 1) * TT + i * BC + 8 * hh;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) qn[ks] = l8(src + 16 * ks);
             }
         }
-        const float csn = (gate && has && b + 1 <= ca) ? a.csum[chunk0 + b + 1] : 0.f;
         if (mine) {
             f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
             mm2(s, tK, qc, lane);                          // S^T[j][i], unscaled
@@ -638,7 +645,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
             }
             mm2(g, tKT, db, lane);                         // + scale K~_b^T dS^T
         }
-        fsum -= static_cast<double>(csn);
+        if (gate) fsum -= static_cast<double>(sLocK[BC]);
     }
     if (has) {
         rs += __shfl_xor(rs, 32, 64);
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_own_end_kernel(const BwdKArgs
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 tQ[BT], tQT[BT], tO[BT], tOT[BT], tGT[BT];
-    __shared__ __attribute__((aligned(16))) float sRq[BC], sD[BC];
+    __shared__ __attribute__((aligned(16))) float sRq[BC + 4], sD[BC];   // sRq[64]: the pair's gate bias
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -759,22 +766,23 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
     const float locK = gate ? a.loc[wrow + p0 + j] : 0.f;
 
     // query chunk ca's tiles and per-query row terms, in flight
+    // (raw loads only: they are combined at the stage, where the tiles are
+    // waited for anyway)
     Frag4 fQ = {}, fO = {}, fG = {};
-    float rq_n = 0.f, d_n = 0.f;
-    double fpre = 0.0;              // sum of csum over chunks b+1 .. ca, for the prefetch
+    float lse_n = 0.f, loc_n = 0.f, d_n = 0.f, cs_n = 0.f;
     auto prefetch = [&](int cn) {
         const int pa = cn * BC, nva = min(BC, L - pa);
         fQ = fetch4(qs + pair_index(cn, cb) * TT, BC, tid);
         fO = fetch4(dOg + (size_t)pa * BC, nva, tid);
         if (cb >= 1) fG = fetch4(gs + pair_index(cn, cb) * TT, BC, tid);
-        if (gate) fpre += static_cast<double>(a.csum[chunk0 + cn]);
         if (tid < BC) {
-            rq_n = tid < nva ? (gate ? a.loc[wrow + pa + tid] : 0.f) + static_cast<float>(fpre) -
-                                   a.lse[hrow + pa + tid] * kLog2e
-                             : -INFINITY;
+            lse_n = tid < nva ? a.lse[hrow + pa + tid] : INFINITY;
+            loc_n = gate ? a.loc[wrow + pa + tid] : 0.f;
             d_n = a.dsum[wrow + pa + tid];
         }
+        if (gate && tid == BC) cs_n = a.csum[chunk0 + cn];
     };
+    double fpre = 0.0;              // sum of csum over chunks b+1 .. ca (thread 64)
     if (cb + 1 < N) prefetch(cb + 1);
     f32x16 dv[2] = {z16(), z16()}, dk[2] = {z16(), z16()}, dm[2] = {z16(), z16()};
     float cs = 0.f;
@@ -786,14 +794,19 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
         put4_tp<false>(tOT, fO, tid);                        // dO_a^T [d][slot of i]
         if (cb >= 1) put4_tp<true>(tGT, fG, tid);            // G^T [y][slot of i]
         if (tid < BC) {
-            sRq[tid] = rq_n;
+            sRq[tid] = loc_n - lse_n * kLog2e;                   // -inf past L
             sD[tid] = d_n;
+        }
+        if (tid == BC) {
+            fpre += static_cast<double>(cs_n);
+            sRq[BC] = static_cast<float>(fpre);
         }
         __syncthreads();
         if (ca + 1 < N) prefetch(ca + 1);
         f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
         mm2(s, tQ, kb, lane);                                 // S[i][j], unscaled
         mm2(dp, tO, vb, lane);                                // dP[i][j]
+        const float colterm = sRq[BC] - locK;                 // bias - the key's gate term
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -803,7 +816,7 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int v = 4 * g4 + r;
-                    const float p = exp2f(c2 * s[blk][v] + rq[r] - locK);
+                    const float p = exp2f(c2 * s[blk][v] + rq[r] + colterm);
                     const float d = p * (dp[blk][v] - d4[r]);
                     cs += d;
                     s[blk][v] = p;
