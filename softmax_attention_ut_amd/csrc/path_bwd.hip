@@ -919,10 +919,10 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
 #pragma unroll
         for (int m = 0; m < BC; ++m) {
             const float* grow = sG + m * FP;
-            float acc = 0.f;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};          // four independent chains
 #pragma unroll
-            for (int p = 0; p < m; ++p) acc = fmaf(grow[p], t[p], acc);
-            t[m] = (m == lane ? 1.f : 0.f) - sB[m] * acc;
+            for (int p = 0; p < m; ++p) acc[p & 3] = fmaf(grow[p], t[p], acc[p & 3]);
+            t[m] = (m == lane ? 1.f : 0.f) - sB[m] * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
 #pragma unroll
         for (int m = 0; m < BC; ++m) sX[m * FP + lane] = t[m];
