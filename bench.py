@@ -352,6 +352,24 @@ def bwd_flop_model(B, H, L, d, C=64):
     return {"eff": BH * f_eff, "alg": BH * (f_pairs + f_own + f_prep + f_utb)}
 
 
+def bwd_bytes_model(B, H, L, d, gate, C=64):
+    """HBM bytes of one backward as the library runs it: the inputs q, k, v,
+    w, out, d_out (bf16) and beta, lse (and log f) read once; the gradients
+    dq, dk, dv, dw (fp32) and dbeta (and dlog f) written once; and the
+    per-pair states of the blockwise algorithm, the query carried to key
+    chunk b (N(N-1)/2 pairs) and the query's adjoint (pairs with b >= 1),
+    64 x 64 bf16 each, written once, the queries read twice (the adjoint's
+    pass and the key pass), the adjoints once.  The per-chunk tiles (about
+    0.1 % of this at L = 4096) are left out."""
+    N = (L + C - 1) // C
+    BH = B * H
+    io = BH * L * (6 * d * 2 + (3 if gate else 2) * 4) + BH * L * (4 * d * 4 + (2 if gate else 1) * 4)
+    tile = C * d * 2
+    pq, pg = N * (N - 1) // 2, (N - 1) * (N - 2) // 2
+    states = BH * (3 * pq + 2 * pg) * tile
+    return io + states
+
+
 def bench_bwd(args, cfg, torch, pa, inputs):
     """One backward pass (path_attn_bwd: the per-chunk prepare, the query- and
     key-stationary kernels, the gate's suffix sums) after one forward of the
@@ -390,7 +408,11 @@ def bench_bwd(args, cfg, torch, pa, inputs):
     ms = wall * 1e3 / args.steps
     ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     f = bwd_flop_model(B, H, L, d)
-    achieved = f["alg"] / (ev_ms * 1e-3) / 1e12
+    nbytes = bwd_bytes_model(B, H, L, d, cfg.gate)
+    tflops = f["alg"] / (ev_ms * 1e-3) / 1e12
+    gbs = nbytes / (ev_ms * 1e-3) / 1e9
+    # the committed counter summary covers the 4k FoX workload only
+    traffic = _traffic("path_bwd_fox_L4k.md", "path_bwd.hip") if cfg.name == "fox_L4k" else None
     res = {
         "metric": f"PaTH bwd effective TFLOP/s + tokens/s (bf16, L={L}, d={d}) and % MFMA peak",
         "value": f["eff"] / (ms * 1e-3) / 1e12,
@@ -404,13 +426,17 @@ def bench_bwd(args, cfg, torch, pa, inputs):
                    "forget_gate": cfg.gate, "parallelism": "single GPU"},
         "tokens_per_s": B * L / (ms * 1e-3),
         "step_ms_events": ev_ms,
-        "tflops_algorithmic": achieved,
-        "roofline": {"kernel": "path_attn_bwd (path_ut_bf16_kernel<64,false,false>, "
-                               "path_bwd_query_kernel, path_bwd_key_kernel"
-                               + (", path_bwd_gate_kernel)" if cfg.gate else ")"),
-                     "bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_flops_per_launch": f["alg"]},
+        "tflops_algorithmic": tflops,
+        "mfma_peak_frac_algorithmic": tflops / MFMA_BF16_PEAK_TFLOPS,
+        # the pair states make the design HBM-bound: its bytes at 8 TB/s take
+        # longer than its flops at 2.5 PFLOP/s
+        "roofline": {"kernel": "path_attn_bwd (path_ut_bf16_kernel<64,false,false> + "
+                               "path_bwd_layout/own/chain/own_end/key/ut"
+                               + ("/gate" if cfg.gate else "") + " kernels; HIP events around the call)",
+                     "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "algorithmic_flops_per_launch": f["alg"]},
     }
     return res, inp
 
@@ -509,7 +535,9 @@ def bench_kcache(args, cfg, torch, pa, inputs):
         "roofline": {"kernel": f"path_kcache_from_prefill: path_ut_bf16_kernel<{d}, true, false> "
                                f"+ path_kcache_group/suffix/apply_kernel<{d}>",
                      "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": (_traffic("path_kcache_d128_L8k.md", "path_kcache.hip")
+                                 if cfg.name == "d128_L8k_decode" else None),
                      "algorithmic_bytes_per_launch": nbytes,
                      "algorithmic_flops_per_launch": flops},
     }

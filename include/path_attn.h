@@ -297,10 +297,12 @@ int path_decode_step_gated(void* k_cache, void* v_cache, float* f_cache,
  *                   slot j % page of page block_table[b][j / page].
  *   page            a positive multiple of 64; the capacity of a sequence is
  *                   max_blocks * page slots.
- * The caller owns the pool and the table and keeps the table's entries for
- * every slot a call touches within [0, num_blocks).  A page number outside
- * that range is never dereferenced: its slots are left out (no fault, but
- * the result is then not the attention defined above).
+ * The caller owns the pool and the table and must keep the table's entries
+ * for every slot a call touches within [0, num_blocks): an entry outside
+ * that range gives undefined results (no status reports it).  Such a page
+ * number is never dereferenced, so it cannot fault: its slots are left out
+ * of the update and the attention, and a new key or value for one of them
+ * is not stored.
  *
  * path_kcache_from_prefill_paged is path_kcache_from_prefill writing the
  * transformed keys and the values through the table (slots [0, L); L <=

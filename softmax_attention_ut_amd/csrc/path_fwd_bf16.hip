@@ -591,13 +591,14 @@ __global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) 
 // A workgroup of 8 waves holds query chunks 4qb .. 4qb+3 of one head; wave w
 // runs on SIMD w % 4 (the hardware deals a workgroup's waves to the SIMDs in
 // turn).  Query chunk 4qb + j is split between waves j and 7 - j, on two
-// different SIMDs.  The block's own chunks are walked with every wave in step
-// (a barrier per chunk); there each SIMD has at most one wave on a diagonal
-// step.  Every chunk left of them is split per wave into a matrix phase (PV
-// of the previous chunk, logits and carry of this one: 26 MFMAs) and a vector
-// phase (the probabilities: 32 exps).  Waves 4..7 run one phase ahead of
-// waves 0..3 and a workgroup barrier separates the phases, so on every SIMD
-// one wave's MFMAs run while the other wave's vector instructions issue.
+// different SIMDs.  Each wave starts from the prepare stage's state after its
+// own chunk (the query carried to the chunk start, the pending probabilities
+// of the own keys, their maximum and sum).  Every key chunk left of its own is
+// split per wave into a matrix phase (PV of the previous chunk, logits and
+// carry of this one: 26 MFMAs) and a vector phase (the probabilities: 32
+// exps).  Waves 4..7 run one phase ahead of waves 0..3 and a workgroup
+// barrier separates the phases, so on every SIMD one wave's MFMAs run while
+// the other wave's vector instructions issue.
 //
 // Staging: a key chunk's K~, -M^T, V, gate rows and sums sit in stage set
 // k % 2 and are copied two phases before their first use.
