@@ -529,24 +529,41 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
                 for (int r = 0; r < 4; ++r) q[blk][4 * g4 + r] = x4[r];
             }
     }
-    Frag fmt = {};
-    if (ahi - 1 >= 1) fmt = fetch(mtn + (size_t)(ahi - 1) * TT, BC, tid);
-    for (int b = ahi - 1; b >= 0; --b) {
-        const bool mine = has && b <= ca - 1;
-        bf16x8 qb[4];
+    // Steps go in blocks of four: the block's -M_b^T tiles (k in slot order)
+    // are staged together into the four tile buffers, the next block's are
+    // fetched meanwhile, and the four steps run without a barrier.
+    {
+        bf16* const stage[4] = {tK, tKT, tV, tM};
+        Frag fr[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qb[ks] = bop(q, ks);
-        if (mine) {
-            bf16* dst = qs + pair_index(ca, b) * TT + i * BC + 8 * hh;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) s8(dst + 16 * ks, qb[ks]);
+        for (int t = 0; t < 4; ++t) {
+            fr[t] = Frag{};
+            if (ahi - 1 - t >= 1) fr[t] = fetch(mtn + (size_t)(ahi - 1 - t) * TT, BC, tid);
         }
-        if (b >= 1) {
+        for (int b0 = ahi - 1; b0 >= 0; b0 -= 4) {
             __syncthreads();
-            put(tM, fmt, tid);                            // -M_b^T, k in slot order
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (b0 - t >= 1) put(stage[t], fr[t], tid);
             __syncthreads();
-            if (b - 1 >= 1) fmt = fetch(mtn + (size_t)(b - 1) * TT, BC, tid);
-            if (mine) mm2(q, tM, qb, lane);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                if (b0 - 4 - t >= 1) fr[t] = fetch(mtn + (size_t)(b0 - 4 - t) * TT, BC, tid);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int b = b0 - t;
+                if (b < 0) break;
+                const bool mine = has && b <= ca - 1;
+                bf16x8 qb[4];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) qb[ks] = bop(q, ks);
+                if (mine) {
+                    bf16* dst = qs + pair_index(ca, b) * TT + i * BC + 8 * hh;
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) s8(dst + 16 * ks, qb[ks]);
+                    if (b >= 1) mm2(q, stage[t], qb, lane);   // Q^T += (-M_b^T) Q^T
+                }
+            }
         }
     }
 
