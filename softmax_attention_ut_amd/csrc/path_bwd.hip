@@ -156,6 +156,26 @@ __device__ __forceinline__ void put_t(bf16* T, const Frag& f, int tid) {
         *reinterpret_cast<bf16x2*>(T + (c + e) * BP + r) = p;
     }
 }
+// Transposed with the old row index taken into slot order: T[col][permk(row)]
+// (a tile whose rows become the k axis of a chained product); put_tp also
+// takes the old column into slot order: T[permk(col)][permk(row)].  permk
+// keeps the rows 2i, 2i+1 adjacent.
+__device__ __forceinline__ void put_to(bf16* T, const Frag& f, int tid) {
+    const int r = 2 * (tid & 31), c = 8 * (tid >> 5), pr = permk(r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16x2 p = {f.x[0][e], f.x[1][e]};
+        *reinterpret_cast<bf16x2*>(T + (c + e) * BP + pr) = p;
+    }
+}
+__device__ __forceinline__ void put_tp(bf16* T, const Frag& f, int tid) {
+    const int r = 2 * (tid & 31), c = 8 * (tid >> 5), pr = permk(r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const bf16x2 p = {f.x[0][e], f.x[1][e]};
+        *reinterpret_cast<bf16x2*>(T + permk(c + e) * BP + pr) = p;
+    }
+}
 // LDS tile -> row-major [64][64] global rows (16-byte stores)
 __device__ __forceinline__ void store_tile(bf16* g, const bf16* T, int tid) {
 #pragma unroll
@@ -163,43 +183,6 @@ __device__ __forceinline__ void store_tile(bf16* g, const bf16* T, int tid) {
         const int u = tid + 256 * it, r = u >> 3, c = (u & 7) * 8;
         s8(g + r * BC + c, l8(T + r * BP + c));
     }
-}
-
-// The same over 128 threads: thread t holds rows 2 (t & 31), 2 (t & 31) + 1
-// and the column units 8 (t >> 5) and 8 (t >> 5) + 32.
-struct Frag4 { bf16x8 x[2][2]; };   // [unit][row]
-__device__ __forceinline__ Frag4 fetch4(const bf16* g, int nvalid, int tid) {
-    const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
-    const bf16x8 z = {};
-    Frag4 f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-            f.x[u][rr] = r + rr < nvalid ? l8(g + (size_t)(r + rr) * BC + c + 32 * u) : z;
-    return f;
-}
-__device__ __forceinline__ void put4(bf16* T, const Frag4& f, int tid) {
-    const int r = 2 * (tid & 31), c = 8 * (tid >> 5);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) s8(T + (r + rr) * BP + c + 32 * u, f.x[u][rr]);
-}
-// Transposed with the old row index taken into slot order: T[col][permk(row)]
-// (a tile whose rows become the k axis of a chained product); with PC also
-// the old column: T[permk(col)][permk(row)].  permk keeps 2i, 2i+1 adjacent.
-template <bool PC>
-__device__ __forceinline__ void put4_tp(bf16* T, const Frag4& f, int tid) {
-    const int r = 2 * (tid & 31), c = 8 * (tid >> 5), pr = permk(r);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int col = c + 32 * u + e;
-            const bf16x2 p = {f.x[u][0][e], f.x[u][1][e]};
-            *reinterpret_cast<bf16x2*>(T + (PC ? permk(col) : col) * BP + pr) = p;
-        }
 }
 
 // Accumulator registers 8 H .. 8 H + 7 as a bf16 B operand (times s).
@@ -741,24 +724,34 @@ __global__ __launch_bounds__(256, 2) void path_bwd_own_end_kernel(const BwdKArgs
 }
 
 // ---------------------------------------------------------------------------
-// Key chunk b (two waves; wave h holds keys 32 h .. 32 h + 31 as the columns
-// of its accumulators), summed over the query chunks a > b:
-//   S = Q_{a,b} K~_b^T, dP = dO_a V_b^T, P, dS (rows = queries);
+// Key chunk b, summed over the query chunks a > b (four waves; wave w holds
+// the keys 32 kh .. 32 kh + 31, kh = w & 1, as the columns of its
+// accumulators and takes the queries 32 qh .. 32 qh + 31, qh = w >> 1, of
+// every query chunk):
+//   S = Q_{a,b} K~_b^T, dP = dO_a V_b^T, P, dS (rows = the wave's queries);
 //   dV^T += dO_a^T P, dK~^T += Q_{a,b}^T dS, dM += Q_{a,b}^T G_{a,b-1}
-// (dM: wave h forms the columns 32 h .. 32 h + 31).  The k axis of the last
-// three is the query axis, in slot order.
+// (dM: columns y = the wave's key half).  The k axis of the last three is the
+// wave's half of the query axis, in slot order; the two query halves' partial
+// sums are added through LDS at the end.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 tQ[BT], tQT[BT], tO[BT], tOT[BT], tGT[BT];
+__global__ __launch_bounds__(256, 2) void path_bwd_key_kernel(const BwdKArgs a) {
+    // five tiles in one array (the end's reduction reuses it as 16 KB of fp32)
+    __shared__ __attribute__((aligned(16))) bf16 tiles[5 * BT];
     __shared__ __attribute__((aligned(16))) float sRq[BC + 4], sD[BC];   // sRq[64]: the pair's gate bias
+    bf16* const tQ = tiles;
+    bf16* const tQT = tiles + BT;
+    bf16* const tO = tiles + 2 * BT;
+    bf16* const tOT = tiles + 3 * BT;
+    bf16* const tGT = tiles + 4 * BT;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
+    const int kh = wave & 1, qh = wave >> 1;       // key half, query half of the wave
     const int L = a.L, N = a.N, Lp = N * BC;
     int head, cb;
     wg_map(blockIdx.x, a.BH, N, false, head, cb);
     const int p0 = cb * BC, nvb = min(BC, L - p0);
-    const int j = 32 * wave + l32;                  // the lane's key within the chunk
+    const int j = 32 * kh + l32;                    // the lane's key within the chunk
     const size_t hrow = (size_t)head * L, wrow = (size_t)head * Lp, chunk0 = (size_t)head * N;
     const bool gate = a.loc != nullptr;
     const float c2 = a.scale * kLog2e;
@@ -782,16 +775,15 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
     }
     const float locK = gate ? a.loc[wrow + p0 + j] : 0.f;
 
-    // query chunk ca's tiles and per-query row terms, in flight
-    // (raw loads only: they are combined at the stage, where the tiles are
-    // waited for anyway)
-    Frag4 fQ = {}, fO = {}, fG = {};
+    // query chunk ca's tiles and per-query values in flight (raw loads only:
+    // they are combined at the stage, where the tiles are waited for anyway)
+    Frag fQ = {}, fO = {}, fG = {};
     float lse_n = 0.f, loc_n = 0.f, d_n = 0.f, cs_n = 0.f;
     auto prefetch = [&](int cn) {
         const int pa = cn * BC, nva = min(BC, L - pa);
-        fQ = fetch4(qs + pair_index(cn, cb) * TT, BC, tid);
-        fO = fetch4(dOg + (size_t)pa * BC, nva, tid);
-        if (cb >= 1) fG = fetch4(gs + pair_index(cn, cb) * TT, BC, tid);
+        fQ = fetch(qs + pair_index(cn, cb) * TT, BC, tid);
+        fO = fetch(dOg + (size_t)pa * BC, nva, tid);
+        if (cb >= 1) fG = fetch(gs + pair_index(cn, cb) * TT, BC, tid);
         if (tid < BC) {
             lse_n = tid < nva ? a.lse[hrow + pa + tid] : INFINITY;
             loc_n = gate ? a.loc[wrow + pa + tid] : 0.f;
@@ -801,17 +793,19 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
     };
     double fpre = 0.0;              // sum of csum over chunks b+1 .. ca (thread 64)
     if (cb + 1 < N) prefetch(cb + 1);
+    // accumulators over the wave's query half: dV^T, dK~^T (rows e, the
+    // wave's keys) and dM (rows x, columns y = the wave's key half)
     f32x16 dv[2] = {z16(), z16()}, dk[2] = {z16(), z16()}, dm[2] = {z16(), z16()};
     float cs = 0.f;
     for (int ca = cb + 1; ca < N; ++ca) {
         __syncthreads();
-        put4(tQ, fQ, tid);                                   // Q_{a,b} [i][slot]
-        put4_tp<true>(tQT, fQ, tid);                         // Q_{a,b}^T [x][slot of i]
-        put4(tO, fO, tid);                                   // dO_a [i][d]
-        put4_tp<false>(tOT, fO, tid);                        // dO_a^T [d][slot of i]
-        if (cb >= 1) put4_tp<true>(tGT, fG, tid);            // G^T [y][slot of i]
+        put(tQ, fQ, tid);                                    // Q_{a,b} [i][slot]
+        put_tp(tQT, fQ, tid);                                // Q_{a,b}^T [x][slot of i]
+        put(tO, fO, tid);                                    // dO_a [i][d]
+        put_to(tOT, fO, tid);                                // dO_a^T [d][slot of i]
+        if (cb >= 1) put_tp(tGT, fG, tid);                   // G^T [y][slot of i]
         if (tid < BC) {
-            sRq[tid] = loc_n - lse_n * kLog2e;                   // -inf past L
+            sRq[tid] = loc_n - lse_n * kLog2e;               // -inf past L
             sD[tid] = d_n;
         }
         if (tid == BC) {
@@ -820,45 +814,76 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
         }
         __syncthreads();
         if (ca + 1 < N) prefetch(ca + 1);
-        f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
-        mm2(s, tQ, kb, lane);                                 // S[i][j], unscaled
-        mm2(dp, tO, vb, lane);                                // dP[i][j]
-        const float colterm = sRq[BC] - locK;                 // bias - the key's gate term
+        // S, dP for queries 32 qh .. +31 (rows) and the wave's keys (columns)
+        f32x16 s = z16(), dp = z16();
+        {
+            const bf16* qa = tQ + (32 * qh + l32) * BP + 8 * hh;
+            const bf16* oa = tO + (32 * qh + l32) * BP + 8 * hh;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const f32x4 rq = *reinterpret_cast<const f32x4*>(sRq + 32 * blk + 8 * g4 + 4 * hh);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * blk + 8 * g4 + 4 * hh);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int v = 4 * g4 + r;
-                    const float p = exp2f(c2 * s[blk][v] + rq[r] + colterm);
-                    const float d = p * (dp[blk][v] - d4[r]);
-                    cs += d;
-                    s[blk][v] = p;
-                    dp[blk][v] = d;
-                }
+            for (int ks = 0; ks < 4; ++ks) {
+                s = mfmab(l8(qa + 16 * ks), kb[ks], s);
+                dp = mfmab(l8(oa + 16 * ks), vb[ks], dp);
             }
-        bf16x8 pb[4], db[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            pb[ks] = bop(s, ks);
-            db[ks] = bop(dp, ks);
         }
-        mm2(dv, tOT, pb, lane);                               // dV^T[e][j]
-        mm2(dk, tQT, db, lane);                               // dK~^T[e][j], unscaled
-        if (cb >= 1) {
-            bf16x8 gb[4];
-            const bf16* gr = tGT + j * BP + 8 * hh;
+        const float colterm = sRq[BC] - locK;                // bias - the key's gate term
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) gb[ks] = l8(gr + 16 * ks);
-            mm2(dm, tQT, gb, lane);                           // (Q^T G)[x][y], y = j
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 rq = *reinterpret_cast<const f32x4*>(sRq + 32 * qh + 8 * g4 + 4 * hh);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 32 * qh + 8 * g4 + 4 * hh);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = 4 * g4 + r;
+                const float p = exp2f(c2 * s[v] + rq[r] + colterm);
+                const float d = p * (dp[v] - d4[r]);
+                cs += d;
+                s[v] = p;
+                dp[v] = d;
+            }
+        }
+        // the k axis of the next products is the wave's 32 query slots:
+        // k-steps 2 qh and 2 qh + 1 of the 64-slot axis
+        const bf16x8 pb0 = cvt8<0>(s), pb1 = cvt8<1>(s);
+        const bf16x8 db0 = cvt8<0>(dp), db1 = cvt8<1>(dp);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            dv[blk] = mfmab(aop(tOT, blk, 2 * qh, lane), pb0, dv[blk]);
+            dv[blk] = mfmab(aop(tOT, blk, 2 * qh + 1, lane), pb1, dv[blk]);
+            const bf16x8 aq0 = aop(tQT, blk, 2 * qh, lane), aq1 = aop(tQT, blk, 2 * qh + 1, lane);
+            dk[blk] = mfmab(aq0, db0, dk[blk]);
+            dk[blk] = mfmab(aq1, db1, dk[blk]);
+            if (cb >= 1) {
+                const bf16* gr = tGT + j * BP + 32 * qh + 8 * hh;
+                dm[blk] = mfmab(aq0, l8(gr), dm[blk]);
+                dm[blk] = mfmab(aq1, l8(gr + 16), dm[blk]);
+            }
         }
     }
-    // dV = the later queries' part + the own chunk's; dK~ (scaled) and dM
-    // for the UT kernel; the column sums of dS
-    {
+    // Sum the two query halves through LDS (waves 2, 3 hand their partials to
+    // waves 0, 1), then: dV = the later queries' part + the own chunk's; dK~
+    // (scaled) and dM for the UT kernel; the column sums of dS.
+    float* red = reinterpret_cast<float*>(tiles);           // 2 x 2 x 16 x 64 floats per pass
+    auto reduce = [&](f32x16* acc) {
+        __syncthreads();
+        if (qh == 1)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[((kh * 2 + blk) * 16 + v) * 64 + lane] = acc[blk][v];
+        __syncthreads();
+        if (qh == 0)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[blk][v] += red[((kh * 2 + blk) * 16 + v) * 64 + lane];
+    };
+    reduce(dv);
+    reduce(dk);
+    reduce(dm);
+    __syncthreads();
+    if (qh == 1) red[kh * 64 + lane] = cs;
+    __syncthreads();
+    if (qh == 0) {
+        cs += red[kh * 64 + lane];
         const float* dvo = own + 1 * TT + j * BC;
         float* dvg = a.dv + (hrow + p0 + j) * BC;
         float* dkt = own + 5 * TT + j * BC;
@@ -881,9 +906,9 @@ __global__ __launch_bounds__(128) void path_bwd_key_kernel(const BwdKArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 dmg[(32 * blk + 8 * (v >> 2) + 4 * hh + (v & 3)) * BC + j] = -dm[blk][v];
+        cs += __shfl_xor(cs, 32, 64);
+        if (hh == 0) a.csl[wrow + p0 + j] = cs;
     }
-    cs += __shfl_xor(cs, 32, 64);
-    if (hh == 0) a.csl[wrow + p0 + j] = cs;
 }
 
 // ---------------------------------------------------------------------------
@@ -1145,7 +1170,7 @@ hipError_t launch_path_bwd(const BwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(path_bwd_own_kernel, grid, dim3(256), 0, s, a);
     if (a.N >= 2) hipLaunchKernelGGL(path_bwd_chain_kernel, dim3(a.BH * (a.N / 2)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(path_bwd_own_end_kernel, grid, dim3(256), 0, s, a);
-    hipLaunchKernelGGL(path_bwd_key_kernel, grid, dim3(128), 0, s, a);
+    hipLaunchKernelGGL(path_bwd_key_kernel, grid, dim3(256), 0, s, a);
     hipLaunchKernelGGL(path_bwd_ut_kernel, grid, dim3(256), 0, s, a);
     if (a.log_f) hipLaunchKernelGGL(path_bwd_gate_kernel, dim3(a.BH), dim3(256), 0, s, a);
     return hipGetLastError();
