@@ -917,11 +917,24 @@ __global__ __launch_bounds__(256, 2) void path_bwd_key_kernel(const BwdKArgs a) 
 // X = (I + A)^{-1} with A = strictLower(D G), T^{-1} = X D,
 // R = strictLower(W K^T), Y = T^{-1} R, U = T^{-1} W.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 tA[BT], tB[BT], tCt[BT], tD[BT], tE[BT],
-        tF[BT], tH[BT], tI[BT];
-    __shared__ __attribute__((aligned(16))) float sG[BC * FP], sX[BC * FP];   // fp32: G, (I + A)^{-1}
+__global__ __launch_bounds__(256, 2) void path_bwd_ut_kernel(const BwdKArgs a) {
+    // Eight tiles in one array.  Until T^{-1} is formed, the fp32 G and
+    // X = (I + A)^{-1} of the substitution live over tE, tF and tH, tI; each
+    // wave then keeps its 32 x 32 quarters of G and X in registers, which is
+    // all that later steps read of them.  74 KB: two workgroups per CU.
+    __shared__ __attribute__((aligned(16))) bf16 tiles[8 * BT];
     __shared__ float sB[BC], sDb[BC];
+    bf16* const tA = tiles;
+    bf16* const tB = tiles + BT;
+    bf16* const tCt = tiles + 2 * BT;
+    bf16* const tD = tiles + 3 * BT;
+    bf16* const tE = tiles + 4 * BT;
+    bf16* const tF = tiles + 5 * BT;
+    bf16* const tH = tiles + 6 * BT;
+    bf16* const tI = tiles + 7 * BT;
+    float* const sG = reinterpret_cast<float*>(tE);        // [64][FP] over tE, tF
+    float* const sX = reinterpret_cast<float*>(tH);        // [64][FP] over tH, tI
+    static_assert(BC * FP * 4 <= 2 * BT * 2, "fp32 tile over two bf16 tiles");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int L = a.L, N = a.N;
@@ -946,11 +959,9 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
         sDb[tid] = 0.f;
     }
     __syncthreads();
-    {
-        const f32x16 gq = mm_nt(tA, tA, z16(), wave, lane);         // G = W W^T
+    const f32x16 gq = mm_nt(tA, tA, z16(), wave, lane);             // G = W W^T (kept)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sG[qrow(wave, lane, v) * FP + n] = gq[v];
-    }
+    for (int v = 0; v < 16; ++v) sG[qrow(wave, lane, v) * FP + n] = gq[v];
     __syncthreads();
     // X = (I + A)^{-1} (unit lower triangular) by forward substitution on
     // wave 0, lane c holding column c in registers:
@@ -970,7 +981,10 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
         for (int m = 0; m < BC; ++m) sX[m * FP + lane] = t[m];
     }
     __syncthreads();
-    for (int u = tid; u < BC * BC; u += 256) {                      // T^{-1} = X D
+    f32x16 xq;                                                       // the wave's quarter of X
+#pragma unroll
+    for (int v = 0; v < 16; ++v) xq[v] = sX[qrow(wave, lane, v) * FP + n];
+    for (int u = tid; u < BC * BC; u += 256) {                      // T^{-1} = X D (over sG)
         const int m = u >> 6, c = u & 63;
         const bf16 t = static_cast<bf16>(sX[m * FP + c] * sB[c]);
         tE[m * BP + c] = t;
@@ -1070,9 +1084,8 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
         float cs = 0.f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int m = qrow(wave, lane, v);
             dX[v] = dT[v] * sB[n];
-            cs += sX[m * FP + n] * dT[v];
+            cs += xq[v] * dT[v];
         }
         cs += __shfl_xor(cs, 32, 64);
         if (lane < 32) atomicAdd(&sDb[n], cs);
@@ -1080,12 +1093,8 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
     // X = (I + A)^{-1}: dA = -X^T dX X^T via Z = dX X^T, dA = -X^T Z
     __syncthreads();
     st_q<false>(tH, dX, wave, lane);                                 // dX [m][c]
-    for (int u = tid; u < BC * BC; u += 256) {
-        const int m = u >> 6, c = u & 63;
-        const bf16 xv = static_cast<bf16>(sX[m * FP + c]);
-        tI[m * BP + c] = xv;                                         // X [p][c]
-        tCt[c * BP + m] = xv;                                        // X^T [c][m]
-    }
+    st_q<false>(tI, xq, wave, lane);                                 // X [p][c]
+    st_q<true>(tCt, xq, wave, lane);                                 // X^T [c][m]
     __syncthreads();
     const f32x16 zq = mm_nt(tH, tI, z16(), wave, lane);             // Z = dX X^T [m][p]
     __syncthreads();
@@ -1098,7 +1107,7 @@ __global__ __launch_bounds__(256) void path_bwd_ut_kernel(const BwdKArgs a) {
         const int qr = qrow(wave, lane, v);
         const float da = (n < qr) ? -dA[v] : 0.f;
         dA[v] = sB[qr] * da;
-        const float r = wave_sum32(da * sG[qr * FP + n]);
+        const float r = wave_sum32(da * gq[v]);
         if ((lane & 31) == 0) atomicAdd(&sDb[qr], r);
     }
     // G = W W^T: dW += (dG + dG^T) W
