@@ -211,6 +211,10 @@ __device__ __forceinline__ void mm2(f32x16* acc, const bf16* T, const bf16x8* b,
     }
 }
 
+// The probabilities are v_exp_f32 of their log2 argument (no range
+// reduction: results below the smallest normal flush to zero, which is far
+// below the bf16 rounding of any probability that counts).
+
 __device__ __forceinline__ float wave_sum32(float x) {   // over the 32 lanes of a half
 #pragma unroll
     for (int off = 16; off > 0; off >>= 1) x += __shfl_xor(x, off, 32);
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_own_kernel(const BwdKArgs a) 
         for (int v = 0; v < 16; ++v) {
             const int i = qrow(wave, lane, v);
             const float z = c2 * (s[v] - xy[v]) + (sLoc[i] - sLoc[n]);
-            const float p = (n <= i && i < nva) ? exp2f(z - sLse[i]) : 0.f;
+            const float p = (n <= i && i < nva) ? __builtin_amdgcn_exp2f(z - sLse[i]) : 0.f;
             pp[v] = p;
             ds[v] = p * (dp[v] - sD[i]);
         }
@@ -624,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int v = 4 * g4 + r;
-                        const float p = exp2f(c2 * s[blk][v] + rq - lk[r]);
+                        const float p = __builtin_amdgcn_exp2f(c2 * s[blk][v] + rq - lk[r]);
                         const float d = p * (dp[blk][v] - Di);
                         rs += d;
                         s[blk][v] = d;                     // dS^T
@@ -833,7 +837,7 @@ __global__ __launch_bounds__(256, 2) void path_bwd_key_kernel(const BwdKArgs a) 
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int v = 4 * g4 + r;
-                const float p = exp2f(c2 * s[v] + rq[r] + colterm);
+                const float p = __builtin_amdgcn_exp2f(c2 * s[v] + rq[r] + colterm);
                 const float d = p * (dp[v] - d4[r]);
                 cs += d;
                 s[v] = p;
