@@ -114,6 +114,30 @@ __device__ __forceinline__ void st_q(bf16* T, const f32x16& acc, int wave, int l
         else T[m * BP + n] = x;
     }
 }
+// quarter -> two bf16 LDS tiles, x * s = hi + lo to about 16 bits
+// (hi = bf16(x * s), lo = bf16(x * s - hi)), as is or transposed
+template <bool TR>
+__device__ __forceinline__ void st_q2(bf16* Th, bf16* Tl, const f32x16& acc, int wave, int lane,
+                                      float s = 1.f) {
+    const int n = qcol(wave, lane);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int m = qrow(wave, lane, v);
+        const float x = s * acc[v];
+        const bf16 h = static_cast<bf16>(x);
+        const bf16 l = static_cast<bf16>(x - static_cast<float>(h));
+        const int o = TR ? n * BP + m : m * BP + n;
+        Th[o] = h;
+        Tl[o] = l;
+    }
+}
+// acc += (Ah + Al)(Bh + Bl)^T without the lo x lo term: three bf16 products
+__device__ __forceinline__ f32x16 mm_nt3(const bf16* Ah, const bf16* Al, const bf16* Bh,
+                                         const bf16* Bl, f32x16 acc, int wave, int lane) {
+    acc = mm_nt(Ah, Bh, acc, wave, lane);
+    acc = mm_nt(Ah, Bl, acc, wave, lane);
+    return mm_nt(Al, Bh, acc, wave, lane);
+}
 // quarter <-> fp32 global [64][64] (rows of 64 floats)
 __device__ __forceinline__ void st_qg(float* G, const f32x16& acc, int wave, int lane, float s = 1.f) {
     const int n = qcol(wave, lane);
@@ -500,6 +524,26 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
     const bf16* vv = static_cast<const bf16*>(a.v) + hrow * BC;
     float* own = a.own + (chunk0 + ca) * NOWN * TT;
 
+    // The per-query values of the left-to-right pass, loaded here with the
+    // first right-to-left operands (one round trip for all of them).  fsum,
+    // the sum of the chunk sums csum over chunks 1 .. a, is summed across the
+    // wave (lane l takes chunks 1 + l, 65 + l, ...), not one load at a time.
+    const float lse2 = (has && valid) ? a.lse[hrow + row] * kLog2e : 0.f;
+    const float Di = has ? a.dsum[wrow + row] : 0.f;
+    const float locQ = (gate && has) ? a.loc[wrow + row] : 0.f;
+    bf16x8 dob[4];                                        // dO^T as the B operand (d natural)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        dob[ks] = bf16x8{};
+        if (has && valid) dob[ks] = l8(static_cast<const bf16*>(a.dout) + (hrow + row) * BC + 16 * ks + 8 * hh);
+    }
+    double fsum = 0.0;                                    // sum of csum over chunks b+1 .. a (log2)
+    if (gate && has) {
+        for (int c = 1 + lane; c <= ca; c += 64) fsum += static_cast<double>(a.csum[chunk0 + c]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) fsum += __shfl_xor(fsum, off, 64);
+    }
+
     // ---- right to left ----
     f32x16 q[2];
     {
@@ -555,18 +599,6 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
     }
 
     // ---- left to right ----
-    const float lse2 = (has && valid) ? a.lse[hrow + row] * kLog2e : 0.f;
-    const float Di = has ? a.dsum[wrow + row] : 0.f;
-    const float locQ = (gate && has) ? a.loc[wrow + row] : 0.f;
-    bf16x8 dob[4];                                        // dO^T as the B operand (d natural)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        dob[ks] = bf16x8{};
-        if (has && valid) dob[ks] = l8(static_cast<const bf16*>(a.dout) + (hrow + row) * BC + 16 * ks + 8 * hh);
-    }
-    double fsum = 0.0;                                    // sum of csum over chunks b+1 .. a (log2)
-    if (gate && has)
-        for (int c = 1; c <= ca; ++c) fsum += static_cast<double>(a.csum[chunk0 + c]);
     f32x16 g[2] = {z16(), z16()};
     float rs = 0.f;
     // the next step's operands in flight; locK: lanes 0-63 the key chunk's
@@ -1054,17 +1086,22 @@ __global__ __launch_bounds__(256, 2) void path_bwd_ut_kernel(const BwdKArgs a) {
     __syncthreads();
     f32x16 dT = mm_nt(tH, tI, z16(), wave, lane);                   // dY R^T [m][n]
     dT = mm_nt(tCt, tA, dT, wave, lane);                             // + dU W^T
-    // dR = T^{-T} dY (strictly lower), dW += T^{-T} dU
+    // dR = T^{-T} dY (strictly lower), dW += T^{-T} dU.  These products and
+    // those of dA below take their factors as hi + lo bf16 pairs (about 16
+    // bits): with transitions close to one another and beta near 2 (I + A
+    // ill-conditioned) single bf16 roundings of T^{-1}, dY, dU, X, dX and
+    // Z left several per cent of error in dW, dK and dbeta.
     __syncthreads();
-    st_q<true>(tH, dY, wave, lane);                                  // dY^T [j][m]
-    st_q<true>(tI, dU, wave, lane);                                  // dU^T [e][m]
+    st_q2<true>(tH, tA, dY, wave, lane);                             // dY^T [j][m] (W rows no longer read)
+    st_q2<true>(tI, tCt, dU, wave, lane);                            // dU^T [e][m]
+    st_q2<true>(tF, tE, xq, wave, lane, sB[n]);                      // T^{-T} [n][m], hi over the same values
     __syncthreads();
-    f32x16 dR = mm_nt(tF, tH, z16(), wave, lane);                   // [n][j]
+    f32x16 dR = mm_nt3(tF, tE, tH, tA, z16(), wave, lane);          // [n][j]
 #pragma unroll
     for (int v = 0; v < 16; ++v)
         if (qrow(wave, lane, v) <= n) dR[v] = 0.f;
     {
-        const f32x16 t1 = mm_nt(tF, tI, z16(), wave, lane);         // T^{-T} dU [n][e]
+        const f32x16 t1 = mm_nt3(tF, tE, tI, tCt, z16(), wave, lane);   // T^{-T} dU [n][e]
 #pragma unroll
         for (int v = 0; v < 16; ++v) dW[v] += t1[v];
     }
@@ -1095,16 +1132,17 @@ __global__ __launch_bounds__(256, 2) void path_bwd_ut_kernel(const BwdKArgs a) {
         if (lane < 32) atomicAdd(&sDb[n], cs);
     }
     // X = (I + A)^{-1}: dA = -X^T dX X^T via Z = dX X^T, dA = -X^T Z
+    // (hi + lo factors; tA, tD, tE are free again)
     __syncthreads();
-    st_q<false>(tH, dX, wave, lane);                                 // dX [m][c]
-    st_q<false>(tI, xq, wave, lane);                                 // X [p][c]
-    st_q<true>(tCt, xq, wave, lane);                                 // X^T [c][m]
+    st_q2<false>(tH, tA, dX, wave, lane);                            // dX [m][c]
+    st_q2<false>(tI, tD, xq, wave, lane);                            // X [p][c]
+    st_q2<true>(tCt, tE, xq, wave, lane);                            // X^T [c][m]
     __syncthreads();
-    const f32x16 zq = mm_nt(tH, tI, z16(), wave, lane);             // Z = dX X^T [m][p]
+    const f32x16 zq = mm_nt3(tH, tA, tI, tD, z16(), wave, lane);    // Z = dX X^T [m][p]
     __syncthreads();
-    st_q<true>(tH, zq, wave, lane);                                  // Z^T [p][m]
+    st_q2<true>(tH, tA, zq, wave, lane);                             // Z^T [p][m]
     __syncthreads();
-    f32x16 dA = mm_nt(tCt, tH, z16(), wave, lane);                  // X^T Z [q][p]
+    f32x16 dA = mm_nt3(tCt, tE, tH, tA, z16(), wave, lane);         // X^T Z [q][p]
     // A = strictLower(D G): dbeta_q += sum_{p<q} dA[q][p] G[q][p], dG = beta_q dA
 #pragma unroll
     for (int v = 0; v < 16; ++v) {

@@ -9,7 +9,7 @@ gradient g against the oracle's r (both over all heads and tokens):
 Every product runs on bf16 operands (relative rounding 2^-9 = 2e-3 per
 operand) with fp32 sums; the per-pair states (the query carried to each key
 chunk and the query's adjoint at each chunk) are stored in bf16 and each
-step of their chains adds one such rounding, so over the N <= 11 chunks of
+step of their chains adds one such rounding, so over the N <= 16 chunks of
 these cases the relative error grows to a few times 2e-3 (about sqrt(N)
 roundings in a random walk, plus rowsum(d_out o out) taken from the bf16
 out).  The Frobenius bound is 5 times 2e-3, the max bound allows an element
@@ -60,18 +60,23 @@ def _oracle_grads(inp, d_out, scale):
     return res
 
 
-def _compare(got, ref, what):
+def _compare(got, ref, what, extra=None):
+    """extra: per-gradient arrays of an additional per-element allowance
+    (an error bound that some rounding of the inputs alone implies)."""
     assert set(got) == set(ref), (what, sorted(got), sorted(ref))
     failures = []
     for n in sorted(ref):
         g, r = got[n], ref[n]
         assert np.all(np.isfinite(g)), (what, n)
         e = np.abs(g - r)
+        if extra and n in extra:
+            e = np.maximum(e - extra[n], 0.0)
         mx = e.max() / max(np.abs(r).max(), 1e-30)
         fro = np.linalg.norm(e) / max(np.linalg.norm(r), 1e-30)
         where = tuple(int(x) for x in np.unravel_index(np.argmax(e), e.shape))
         print(f"{what} {n}: max-abs/max|ref| {mx:.3e} (at {where}) "
-              f"fro-rel {fro:.3e}", flush=True)
+              f"fro-rel {fro:.3e}" + (" (beyond the allowance)" if extra and n in extra else ""),
+              flush=True)
         if mx > MAX_REL or fro > FRO_REL:
             failures.append((n, mx, fro))
     assert not failures, (what, failures)
@@ -122,3 +127,65 @@ def test_backward_beta_zero_is_causal_attention_backward():
     assert np.all(got["dw"] == 0.0)
     del got["dw"], ref["dw"]
     _compare(got, ref, "beta=0")
+
+
+@pytest.mark.parametrize("mode", ["all_1.98", "alternating"])
+def test_backward_beta_at_clip_bounds(mode):
+    """beta at the clip bounds: every transition a near reflection (1.98), or
+    alternating 0.02 / 1.98 with the gate; the UT backward's substitution
+    then runs through its largest and smallest diagonal factors."""
+    B, H, L, d = 1, 2, 400, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=(mode == "alternating"), seed=214)
+    if mode == "all_1.98":
+        inp.beta.fill_(1.98)
+    else:
+        inp.beta[..., 0::2] = 0.02
+        inp.beta[..., 1::2] = 1.98
+    d_out = _d_out((B, H, L, d), 314)
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), f"beta {mode}")
+
+
+def test_backward_repeated_w_beta_near_two():
+    """The same unit w over runs of 8 tokens with beta = 1.98: inside a chunk
+    the UT transform's G = W W^T has blocks of ones (T^{-1} then carries
+    powers of (1 - 1.98))."""
+    B, H, L, d = 1, 2, 400, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=False, seed=215)
+    idx = (torch.arange(L) // 8) * 8
+    inp.w = inp.w.double()[:, :, idx].to(torch.bfloat16).contiguous()
+    inp.beta.fill_(1.98)
+    d_out = _d_out((B, H, L, d), 315)
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), "repeated w")
+
+
+def test_backward_peaked_softmax():
+    """Queries scaled by 4 (logits 16 times the variance): most rows put
+    nearly all weight on a few keys, so P and dS are far from uniform and
+    exp2 arguments reach far below the row maximum.
+
+    dlog_f is held to the usual bounds beyond one allowance.  The backward
+    takes D_i = rowsum(dO o O) from the forward's bf16 output O (as training
+    does), and a rounding |dO| <= 2^-9 |O| moves D_i by at most
+    e_i = 2^-9 sum_e |dO_ie O_ie|; dlog f_t is the block sum of dS over
+    i >= t, j < t, and dS_ij = P_ij (dP_ij - D_i), so it moves by at most
+    sum_{i >= t} e_i sum_{j < t} P_ij <= sum_{i >= t} e_i.  With a peaked
+    softmax the true dS nearly cancels there, and this bound is of the size
+    of the gradient itself."""
+    B, H, L, d = 1, 2, 400, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=True, seed=216)
+    inp.q = (inp.q.double() * 4).to(torch.bfloat16)
+    d_out = _d_out((B, H, L, d), 316)
+    out = oracle.recurrent(inp.q, inp.k, inp.v, inp.w, inp.beta, inp.log_f, 0.125)[0]
+    e = 2.0 ** -9 * np.abs(d_out.double().numpy() * out.reshape(B, H, L, d)).sum(-1)
+    allow = np.cumsum(e[..., ::-1], axis=-1)[..., ::-1]           # sum over i >= t
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), "peaked",
+             extra={"dlog_f": allow})
+
+
+def test_backward_sixteen_chunks():
+    """L = 1024 (16 chunks, 120 chunk pairs per head): the longest chains of
+    these tests, whose bf16 per-step roundings add up the most."""
+    B, H, L, d = 1, 2, 1024, 64
+    inp = generate(B, H, L, d, dtype="bf16", gate=True, seed=217)
+    d_out = _d_out((B, H, L, d), 317)
+    _compare(_gpu_grads(inp, d_out, 0.125), _oracle_grads(inp, d_out, 0.125), "L=1024")
