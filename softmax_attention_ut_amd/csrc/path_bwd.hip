@@ -235,6 +235,63 @@ __device__ __forceinline__ void mm2(f32x16* acc, const bf16* T, const bf16x8* b,
     }
 }
 
+// Swizzled unpadded tiles for the chain kernel's direct global -> LDS
+// copies: 64 rows of 128 bytes, the 16-byte unit u of row r stored at unit
+// u ^ swz(r), so that the 32 rows one A-operand read touches fall on
+// distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ ((r >> 3) & 3)) & 7; }
+__device__ __forceinline__ bf16x8 aop_s(const bf16* T, int blk, int ks, int lane) {
+    const int r = 32 * blk + (lane & 31);
+    return l8(T + r * BC + 8 * ((2 * ks + (lane >> 5)) ^ swz(r)));
+}
+__device__ __forceinline__ void mm2_s(f32x16* acc, const bf16* T, const bf16x8* b, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a0 = aop_s(T, 0, ks, lane), a1 = aop_s(T, 1, ks, lane);
+        acc[0] = mfmab(a0, b[ks], acc[0]);
+        acc[1] = mfmab(a1, b[ks], acc[1]);
+    }
+}
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+// global -> LDS copy of 16 (or 4) bytes per lane: lane i writes lds + 16 i
+// (4 i) from gbase + voff.  Issued as inline assembly, out of the
+// compiler's sight (it would otherwise wait for such copies at its own
+// points, with all older stores): the caller waits with s_waitcnt vmcnt.
+// The copy takes its LDS base from M0, which is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
+    unsigned keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gbase, unsigned voff, const void* lds) {
+    unsigned keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "v"(voff), "s"(gbase), "s"(lds_addr(lds)) : "memory");
+}
+// Wait until at most n vector memory operations of this wave are in flight
+// (they complete in issue order): n = the stores issued after the copies
+// being waited for.
+__device__ __forceinline__ void wait_vm(int n) {
+    switch (n) {
+        case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+        case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+        case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+        case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which waits
+// for every store of the wave to complete): the chain kernel's LDS tiles come
+// from the copies above, each wave having waited for its own.
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // The probabilities are v_exp_f32 of their log2 argument (no range
 // reduction: results below the smallest normal flush to zero, which is far
 // below the bf16 rounding of any probability that counts).
@@ -496,9 +553,12 @@ __global__ __launch_bounds__(256, 2) void path_bwd_own_kernel(const BwdKArgs a) 
 //                   storing G_{a,b-1} (b >= 1); dQ~ = G_{a-1}.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a) {
-    __shared__ __attribute__((aligned(16))) bf16 tK[BT], tKT[BT], tV[BT], tM[BT];
-    // sLocK[0..63]: the key chunk's gate terms; sLocK[64]: csum of chunk b + 1
-    __shared__ __attribute__((aligned(16))) float sLocK[BC + 4];
+    // Eight swizzled [64][64] tiles in two sets of four: the right-to-left
+    // pass stages blocks of four -M_b^T tiles, the left-to-right pass a step's
+    // K~_b, scale K~_b^T, V_b, -M_b; one set is read while the other fills.
+    __shared__ __attribute__((aligned(1024))) bf16 tb[8 * TT];
+    // sLoc[s][0..63]: the key chunk's gate terms; sLoc[s][64]: csum of chunk b + 1
+    __shared__ __attribute__((aligned(16))) float sLoc[2][BC + 4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -506,7 +566,8 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
     int head, pr;
     wg_map(blockIdx.x, a.BH, NP, false, head, pr);
     const int ahi = N - 1 - 2 * pr;
-    const int ca = ahi - (wave >> 1);              // this wave's query chunk
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int ca = ahi - (wave_u >> 1);            // this wave's query chunk (wave-uniform)
     const bool has = ca >= 1;                      // chunk 0 has no chain
     const int i = 32 * (wave & 1) + l32;           // the lane's query within the chunk
     const int row = ca * BC + i;
@@ -544,8 +605,30 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
         for (int off = 32; off > 0; off >>= 1) fsum += __shfl_xor(fsum, off, 64);
     }
 
+    // This lane's part of a tile copy: 16-byte unit P = 256 j + 64 wave + lane
+    // of the swizzled LDS tile (j = 0, 1) comes from row P / 8, logical unit
+    // (P % 8) ^ swz(row) of the row-major global tile.
+    unsigned goff[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int P = 256 * j + 64 * wave + lane, r = P >> 3;
+        goff[j] = static_cast<unsigned>(r * 128 + 16 * ((P & 7) ^ swz(r)));
+    }
+    auto copy_tile = [&](bf16* T, const bf16* g) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dma16(g, goff[j], T + (256 * j + 64 * wave_u) * 8);
+    };
+
     // ---- right to left ----
     f32x16 q[2];
+    // blocks of four steps: block i (b = b0 .. b0 - 3, b0 = ahi - 1 - 4 i)
+    // reads set i % 2; its -M_b^T tiles were copied during the block before
+    auto copy_block = [&](int b0, int set) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (b0 - t >= 1) copy_tile(tb + (4 * set + t) * TT, mtn + (size_t)(b0 - t) * TT);
+    };
+    copy_block(ahi - 1, 0);
     {
         // Q~ (fp32 rows) into the accumulator layout: register v of tile blk
         // holds d = 32 blk + 8 (v >> 2) + 4 hh + (v & 3)
@@ -560,26 +643,14 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
                 for (int r = 0; r < 4; ++r) q[blk][4 * g4 + r] = x4[r];
             }
     }
-    // Steps go in blocks of four: the block's -M_b^T tiles (k in slot order)
-    // are staged together into the four tile buffers, the next block's are
-    // fetched meanwhile, and the four steps run without a barrier.
     {
-        bf16* const stage[4] = {tK, tKT, tV, tM};
-        Frag fr[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            fr[t] = Frag{};
-            if (ahi - 1 - t >= 1) fr[t] = fetch(mtn + (size_t)(ahi - 1 - t) * TT, BC, tid);
-        }
-        for (int b0 = ahi - 1; b0 >= 0; b0 -= 4) {
-            __syncthreads();
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (b0 - t >= 1) put(stage[t], fr[t], tid);
-            __syncthreads();
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                if (b0 - 4 - t >= 1) fr[t] = fetch(mtn + (size_t)(b0 - 4 - t) * TT, BC, tid);
+        int stores = -1;                  // stores issued after the last copies (-1: wait for all)
+        int set = 0;
+        for (int b0 = ahi - 1; b0 >= 0; b0 -= 4, set ^= 1) {
+            wait_vm(stores < 0 ? -1 : 4 * stores);
+            bar();
+            if (b0 - 4 >= 1) copy_block(b0 - 4, set ^ 1);
+            stores = 0;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int b = b0 - t;
@@ -592,7 +663,8 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
                     bf16* dst = qs + pair_index(ca, b) * TT + i * BC + 8 * hh;
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks) s8(dst + 16 * ks, qb[ks]);
-                    if (b >= 1) mm2(q, stage[t], qb, lane);   // Q^T += (-M_b^T) Q^T
+                    ++stores;
+                    if (b >= 1) mm2_s(q, tb + (4 * set + t) * TT, qb, lane);   // Q^T += (-M_b^T) Q^T
                 }
             }
         }
@@ -601,66 +673,80 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
     // ---- left to right ----
     f32x16 g[2] = {z16(), z16()};
     float rs = 0.f;
-    // the next step's operands in flight; locK: lanes 0-63 the key chunk's
-    // gate terms, thread 64 the csum that step subtracts (loaded as data of
-    // the step, so that no wait for it comes before the step's stage)
-    Frag fK = {}, fKT = {}, fV = {}, fM = {};
-    float locK = 0.f, csK = 0.f;     // (separate registers: a load in flight into
-                                     // one is never overwritten, which would wait)
+    // step b reads set b % 2: K~_b (d in slot order), scale K~_b^T (keys in
+    // slot order), V_b (chunks left of a are full), -M_b (k in slot order),
+    // the gate terms; the next step's copies and queries are issued at its
+    // start.
+    auto copy_step = [&](int b, int set) {
+        bf16* T = tb + 4 * set * TT;
+        copy_tile(T, kp + (size_t)b * TT);
+        copy_tile(T + TT, kts + (size_t)b * TT);
+        copy_tile(T + 2 * TT, vv + (size_t)b * TT);
+        copy_tile(T + 3 * TT, mn + (size_t)b * TT);
+        if (gate && wave_u == 0) {
+            dma4(a.loc + wrow + (size_t)b * BC, lane * 4, sLoc[set]);
+            if (lane == 0) dma4(a.csum + chunk0 + b + 1, 0, sLoc[set] + BC);
+        }
+    };
     bf16x8 qn[4] = {};
-    if (ahi >= 1) {
-        fK = fetch(kp, BC, tid);
-        fKT = fetch(kts, BC, tid);
-        fV = fetch(vv, BC, tid);
-        if (gate && tid < BC) locK = a.loc[wrow + tid];
-        if (gate && tid == BC) csK = a.csum[chunk0 + 1];
-        if (has) {
-            const bf16* src = qs + pair_index(ca, 0) * TT + i * BC + 8 * hh;
+    auto load_q = [&](int b) {
+        if (has && b <= ca - 1) {
+            const bf16* src = qs + pair_index(ca, b) * TT + i * BC + 8 * hh;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) qn[ks] = l8(src + 16 * ks);
         }
+    };
+    bar();                      // the last right-to-left block's tiles are read
+    if (ahi >= 1) {
+        copy_step(0, 0);
+        load_q(0);
     }
+    int stored = -1;                      // G stores issued after the last copies (-1: wait for all)
     for (int b = 0; b < ahi; ++b) {
+        const int set = b & 1;
         const bool mine = has && b <= ca - 1;
-        __syncthreads();
-        put(tK, fK, tid);                                 // K~_b, d in slot order
-        put(tKT, fKT, tid);                               // scale K~_b^T, keys in slot order
-        put(tV, fV, tid);                                 // V_b (chunks left of a are full)
-        if (b >= 1) put(tM, fM, tid);                     // -M_b, k in slot order
-        if (tid < BC) sLocK[tid] = locK;
-        if (tid == BC) sLocK[BC] = csK;
-        __syncthreads();
+        wait_vm(stored < 0 ? -1 : 4 * stored);
+        bar();
         bf16x8 qc[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qc[ks] = qn[ks];
         if (b + 1 < ahi) {                                // the next step's operands
-            fK = fetch(kp + (size_t)(b + 1) * TT, BC, tid);
-            fKT = fetch(kts + (size_t)(b + 1) * TT, BC, tid);
-            fV = fetch(vv + (size_t)(b + 1) * TT, BC, tid);
-            fM = fetch(mn + (size_t)(b + 1) * TT, BC, tid);
-            if (gate && tid < BC) locK = a.loc[wrow + (size_t)(b + 1) * BC + tid];
-            if (gate && tid == BC && b + 2 < N) csK = a.csum[chunk0 + b + 2];
-            if (has && b + 1 <= ca - 1) {
-                const bf16* src = qs + pair_index(ca, b + 1) * TT + i * BC + 8 * hh;
+            copy_step(b + 1, set ^ 1);
+            load_q(b + 1);
+        }
+        const bf16* tK = tb + 4 * set * TT;
+        const float* lk = sLoc[set];
+        // G_{a,b-1}, stored by every wave at every step (four stores each, so
+        // that the waits above and the compiler's own waits for the queries
+        // can count them): steps without such a state write to the slot of
+        // the pair (a, 0), which nothing reads.
+        bf16x8 gb[4];
+        {
+            const size_t slot = (mine && b >= 1) ? pair_index(ca, b) : pair_index(ca > 0 ? ca : 1, 0);
+            bf16* dst = gs + slot * TT + i * BC + 8 * hh;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) qn[ks] = l8(src + 16 * ks);
+            for (int ks = 0; ks < 4; ++ks) {
+                gb[ks] = bop(g, ks);
+                s8(dst + 16 * ks, gb[ks]);
             }
         }
+        stored = 1;
         if (mine) {
             f32x16 s[2] = {z16(), z16()}, dp[2] = {z16(), z16()};
-            mm2(s, tK, qc, lane);                          // S^T[j][i], unscaled
-            mm2(dp, tV, dob, lane);                        // dP^T[j][i]
+            mm2_s(s, tK, qc, lane);                        // S^T[j][i], unscaled
+            mm2_s(dp, tK + 2 * TT, dob, lane);             // dP^T[j][i]
             // row offset of query i: the gate's local term and chunk sums, -lse
             const float rq = valid ? (locQ + static_cast<float>(fsum) - lse2) : -INFINITY;
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    const f32x4 lk = *reinterpret_cast<const f32x4*>(sLocK + 32 * blk + 8 * g4 + 4 * hh);
+                    const f32x4 l4 = gate ? *reinterpret_cast<const f32x4*>(lk + 32 * blk + 8 * g4 + 4 * hh)
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int v = 4 * g4 + r;
-                        const float p = __builtin_amdgcn_exp2f(c2 * s[blk][v] + rq - lk[r]);
+                        const float p = __builtin_amdgcn_exp2f(c2 * s[blk][v] + rq - l4[r]);
                         const float d = p * (dp[blk][v] - Di);
                         rs += d;
                         s[blk][v] = d;                     // dS^T
@@ -669,19 +755,10 @@ __global__ __launch_bounds__(256, 2) void path_bwd_chain_kernel(const BwdKArgs a
             bf16x8 db[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) db[ks] = bop(s, ks);
-            if (b >= 1) {
-                bf16x8 gb[4];
-                bf16* dst = gs + pair_index(ca, b) * TT + i * BC + 8 * hh;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    gb[ks] = bop(g, ks);
-                    s8(dst + 16 * ks, gb[ks]);             // G_{a,b-1}
-                }
-                mm2(g, tM, gb, lane);                      // G^T - M_b G^T
-            }
-            mm2(g, tKT, db, lane);                         // + scale K~_b^T dS^T
+            if (b >= 1) mm2_s(g, tK + 3 * TT, gb, lane);   // G^T - M_b G^T
+            mm2_s(g, tK + TT, db, lane);                   // + scale K~_b^T dS^T
         }
-        if (gate) fsum -= static_cast<double>(sLocK[BC]);
+        if (gate) fsum -= static_cast<double>(lk[BC]);
     }
     if (has) {
         rs += __shfl_xor(rs, 32, 64);
