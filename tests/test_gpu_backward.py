@@ -83,9 +83,10 @@ def _compare(got, ref, what, extra=None):
 
 
 @pytest.mark.parametrize("gate", [False, True])
-@pytest.mark.parametrize("L", [64, 333, 700])
+@pytest.mark.parametrize("L", [64, 100, 333, 700])
 def test_backward_matches_oracle(L, gate):
-    """One chunk (no pairs), a ragged last chunk, and eleven chunks."""
+    """One chunk (no pairs), two chunks (one pair of query chunks, the lower
+    one with no chain), a ragged last chunk, and eleven chunks."""
     B, H, d = 1, 2, 64
     scale = 1 / math.sqrt(d)
     inp = generate(B, H, L, d, dtype="bf16", gate=gate, seed=200 + L + gate)
