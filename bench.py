@@ -43,25 +43,23 @@ def flop_model(B, H, L, d, C=64):
             behind "effective TFLOP/s" (independent of the carry form)
       carry the query carried through every full chunk strictly between its
             own chunk and the key chunk: 2 d^2 C per (query chunk, chunk) pair
-            with the d x d product (d = 64), 4 C^2 d with the rank-C form
-            Q - (Q W^T) U (d = 128)
+            with the d x d product (the rank-C form Q - (Q W^T) U would take
+            4 C^2 d: twice as much at d = 64, the same at d = 128)
       diag  the own-chunk extras: Q W^T, the carry to the chunk start and the
             lower(Q W^T) Y correction
       prep  the per-chunk UT work (G, R, T^{-1}, U, Y, K~, and M = W^T U for
             the d x d carry), which the survey's count of the prepare stage
             also takes to cover the own-chunk extras
-    "scan" is what the scan kernel computes: at d = 64 the prepare stage takes
-    the own-chunk step (its extras and the own-chunk Q K^T, C^2 d per chunk),
-    at d = 128 the scan does.  "alg" is the whole forward: eff + carry + prep."""
+    "scan" is what the scan kernel computes: the prepare stage takes the
+    own-chunk step (its extras and the own-chunk Q K^T, C^2 d per chunk).
+    "alg" is the whole forward: eff + carry + prep."""
     N = (L + C - 1) // C
-    dense = d == 64
     pairs = (N - 1) * (N - 2) / 2.0
     f_eff = 2.0 * L * L * d
-    f_carry = pairs * (2.0 * d * d * C if dense else 4.0 * C * C * d)
-    f_diag = N * (4.0 * C * C * d + 2.0 * C ** 3)
-    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3 + (2.0 * C * d * d if dense else 0.0))
+    f_carry = pairs * 2.0 * d * d * C
+    f_prep = N * (12.0 * C * C * d + 4.0 * C ** 3 + 2.0 * C * d * d)
     BH = B * H
-    f_scan = f_eff + f_carry - N * C * C * d if dense else f_eff + f_carry + f_diag
+    f_scan = f_eff + f_carry - N * C * C * d
     return {"eff": BH * f_eff, "scan": BH * f_scan, "alg": BH * (f_eff + f_carry + f_prep)}
 
 
@@ -199,7 +197,7 @@ def bench_fwd(args, cfg, torch, pa, inputs):
                            "mean": sum(step_ev) / len(step_ev)},
         "l2_flushed": False,
         "roofline": {"kernel": (f"path_fwd_bf16_d64pp_kernel<{'true' if cfg.gate else 'false'}>" if d == 64
-                                else f"path_fwd_bf16_kernel<{d},{'true' if cfg.gate else 'false'}>"),
+                                else f"path_fwd_bf16_d128pp_kernel<{'true' if cfg.gate else 'false'}>"),
                      "bound": "mfma",
                      "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,

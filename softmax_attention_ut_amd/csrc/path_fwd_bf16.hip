@@ -8,27 +8,25 @@
 // key chunks b = a, a-1, ..., 0:
 //   b = a:  S = Q K~^T + strictUpper(Q W^T) Y   (causal mask j <= i)
 //           Q <- Q - lower(Q W^T) U             (query carried to chunk start)
-//   b < a:  S = Q K~^T;  Q carried through chunk b (skipped for b = 0)
-// and accumulates softmax(S) V online.  Every product is a bf16 MFMA with
-// fp32 accumulation; the carried query Q stays in fp32 accumulators and is
-// rounded to bf16 only as an MFMA operand.
+//   b < a:  S = Q K~^T;  Q carried through chunk b
+// and accumulates softmax(S) V online.  The step b = a is taken by the
+// prepare stage (path_ut_bf16.hip), which leaves the query carried to its
+// chunk start, the pending probabilities of its own keys and their maximum
+// and sum.  This scan carries the query through every left chunk with the
+// chunk's d x d product, Q <- Q - Q M (M = W^T U): 2 d^2 flops per query and
+// chunk, against 4 C d for the rank-C form Q - (Q W^T) U (half at d = 64,
+// the same at d = 128, with one operand tile per chunk instead of two).
+// Every product is a bf16 MFMA with fp32 accumulation; the carried query Q
+// stays in fp32 accumulators and is rounded to bf16 only as an MFMA operand.
 //
-// d = 64 (path_fwd_bf16_d64pp_kernel): the step b = a is taken by the prepare
-// stage (path_ut_bf16.hip), which leaves the query carried to its chunk
-// start, the pending probabilities of its own keys and their maximum and sum.
-// The scan carries the query through every left chunk with the chunk's d x d
-// product, Q <- Q - Q M (M = W^T U): 2 d^2 flops per query and chunk against
-// 4 C d for the rank-C form.  A workgroup of 8 waves (two per SIMD, in
-// alternating matrix and vector phases) holds four query chunks; workgroups
-// are persistent, one per CU.
-//
-// d = 128 (path_fwd_bf16_kernel): every step, the own chunk's too, is taken
-// here, with the rank-C carry Q <- Q - (Q W^T) U; a workgroup of 4 waves
-// holds two query chunks (32 queries per wave).
+// Kernels: path_fwd_bf16_d64pp_kernel (d = 64) and
+// path_fwd_bf16_d128pp_kernel (d = 128).  A workgroup of 8 waves (two per
+// SIMD, in alternating matrix and vector phases) holds four query chunks;
+// workgroups are persistent, one per CU.
 //
 // Orientation.  All products are formed transposed (S^T = K~ Q^T,
-// O^T += V^T P^T, Q^T += (-M^T) Q^T or Q^T -= U^T X^T), so every accumulator
-// that feeds a later product (S^T -> P^T, X^T, Q^T) is already in B-operand
+// O^T += V^T P^T, Q^T += (-M^T) Q^T), so every accumulator
+// that feeds a later product (S^T -> P^T, Q^T) is already in B-operand
 // position: accumulator registers 8s..8s+7 are the B operand of k-step s
 // under the k-slot permutation perm16 (path_internal.h).  The transposed
 // tiles the prepare stage writes have their key axis in that slot order and
@@ -39,9 +37,9 @@
 // Staging.  Key chunks are copied HBM/L2 -> LDS with global_load_lds (no
 // VGPRs) into two alternating stage sets while the waves compute on the
 // other.  LDS tiles are unpadded, their 16-byte units XOR-swizzled per row.
-// Dealing: heaviest query blocks first, and when B*H is a multiple of 8 all
-// blocks of one head go to one XCD, so a head's chunks are reused out of that
-// XCD's L2.
+// Dealing: pairs of query blocks of equal total work, and when B*H is a
+// multiple of 8 all blocks of one head go to one XCD, so a head's chunks are
+// reused out of that XCD's L2.
 #include <type_traits>
 
 #include "path_internal.h"
@@ -126,24 +124,6 @@ __device__ __forceinline__ int swz_g(int r) {
     return COLS == 64 ? ((r ^ ((r >> 3) & 3)) & 7) : (r & 15);
 }
 
-// Asynchronous copy of a [ROWS][COLS] bf16 tile, contiguous in global memory,
-// into a swizzled LDS tile.  Each wave instruction fills one contiguous 1 KB
-// block of LDS (lane i -> bytes 16i..16i+15); the lane picks the global unit
-// that belongs there.
-template <int ROWS, int COLS>
-__device__ __forceinline__ void copy_async(bf16* lds, const bf16* g, int wave, int lane) {
-    constexpr int UPR = COLS / 8;
-    constexpr int RPB = 64 / UPR;             // rows per 1 KB block
-    constexpr int NBLK = ROWS / RPB;
-#pragma unroll
-    for (int b = wave; b < NBLK; b += 4) {
-        const int r = b * RPB + lane / UPR;
-        const int u = (lane % UPR) ^ swz_g<COLS>(r);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(g + (size_t)r * COLS + u * 8),
-                                         (lds_void*)(lds + b * 512), 16, 0, 0);
-    }
-}
-
 // Synchronous guarded copy (rows >= nvalid are zero) into a swizzled tile by
 // NT threads; VTILE: the V tile's swizzle.
 template <int ROWS, int COLS, int NT = 256, bool VTILE = false>
@@ -179,17 +159,6 @@ __device__ __forceinline__ void wait_vmem() {
     __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
 }
 
-__device__ __forceinline__ void decode_block(int bid, int BH, int nqb, int& head, int& qb) {
-    if ((BH & 7) == 0) {
-        const int xcd = bid & 7, j = bid >> 3;
-        head = xcd + 8 * (j / nqb);
-        qb = nqb - 1 - (j % nqb);
-    } else {
-        head = bid / nqb;
-        qb = nqb - 1 - (bid % nqb);
-    }
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // max / sum of a value with the lane 32 positions away (the two lane halves
@@ -203,21 +172,16 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// The running maximum is raised (and O, l rescaled) only when some lane's
-// candidate exceeds it by more than this many log2 units, so probabilities
-// stay <= 2^kRescaleSlack before the final normalisation.
-constexpr float kRescaleSlack = 8.f;
-
 template <int D, bool GATE>
 struct WaveState {
     static constexpr int DT = D / 32, KSD = D / 16;
     f32x16 qacc[DT];   // carried query Q^T (fp32); register 8s+t = d 32dt+16s+8hh+t
-    bf16x8 qB[KSD];    // its bf16 B operand
+    bf16x8 qB[KSD];    // its bf16 B operand (d = 64; at d = 128 it is packed where used)
     f32x16 oacc[DT];   // O^T (unnormalised), same d mapping
     float m_run, l_run, loc_i;
     double dab;        // gate: sum of chunk sums between the query chunk and the key chunk
     int offD[KSD];     // swizzled offsets of unit 2ks+hh in a D-wide row  (row = 32x + lane%32)
-    int offC_[D == 64 ? 1 : 4];   // same in a 64-wide row (d = 64: equal to offD)
+    int offC_[D == 64 ? 1 : 4];   // same in a 64-wide row, k-steps 0..3 (d = 64: equal to offD)
     unsigned voff[D == 64 ? 8 : 1]; // d = 64: transpose-load offsets of the PV operands
     __device__ __forceinline__ int offC(int ks) const { return D == 64 ? offD[ks] : offC_[ks]; }
 };
@@ -225,12 +189,10 @@ struct WaveState {
 template <int D>
 struct Stage {
     bf16* k;           // K~  [C][D]
-    bf16* w;           // W   [C][D]      (d = 64: the diagonal chunk's, shared)
-    bf16* u;           // -U^T [D][C]     (d = 64: the diagonal chunk's, shared)
-    bf16* v;           // V^T  [D][C]
-    bf16* mt;          // -M^T [D][D]     (d = 64 only)
+    bf16* v;           // V   [C][D] (d = 64: read with transpose loads)
+    bf16* mt;          // -M^T [D][D]
     float* loc;        // -local log2 gate prefix [C], then the chunk's gate sum
-    bf16* gb;          // d = 64 with gate: bias k-step A rows [C][16]
+    bf16* gb;          // with gate: bias k-step A rows [C][16]
 };
 
 // Three-term bf16 split, x = h + m + l to about 24 bits.
@@ -239,139 +201,6 @@ __device__ __forceinline__ void split3(float x, bf16& h, bf16& m, bf16& l) {
     const float r = x - static_cast<float>(h);
     m = static_cast<bf16>(r);
     l = static_cast<bf16>(r - static_cast<float>(m));
-}
-
-// One key chunk for one wave.  DIAG: the key chunk is the query's own chunk.
-template <int D, bool GATE, bool DIAG>
-__device__ __forceinline__ void scan_step(WaveState<D, GATE>& st, const Stage<D>& sg,
-                                          const bf16* sY, int l32, int hh, int iloc,
-                                          bool carry, float c2) {
-    constexpr int C = 64;
-    constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
-
-    // S^T = K~ Q^T and X^T = W Q^T  (2 tiles of 32 keys).  With the forget
-    // gate, one more k-step adds -loc_j / c2 to every logit of key j (the key
-    // part of the bias, split into three bf16 terms: a gate that cuts the past
-    // makes loc_j of order 1e4, and the cancellation against the query's part
-    // must keep fp32 precision), so that c2 * S holds
-    // scale*log2(e)*(k~_j . q) + log2 prod f over the key's chunk tail.
-    f32x16 s[2], x[2];
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) { s[kt2][v] = 0.f; x[kt2][v] = 0.f; }
-        const bf16* ak = sg.k + (32 * kt2 + l32) * D;
-        const bf16* aw = sg.w + (32 * kt2 + l32) * D;
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) x[kt2] = mfma32(lds8(aw + st.offD[ks]), st.qB[ks], x[kt2]);
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) s[kt2] = mfma32(lds8(ak + st.offD[ks]), st.qB[ks], s[kt2]);
-        if (GATE) {
-            bf16 gh, gm, gl;
-            split3(-sg.loc[32 * kt2 + l32] * (1.f / c2), gh, gm, gl);
-            bf16x8 ag = {};
-            bf16x8 ones = {};
-            if (hh == 0) {
-                ag[0] = gh;
-                ag[1] = gm;
-                ag[2] = gl;
-                ones[0] = static_cast<bf16>(1.f);
-                ones[1] = static_cast<bf16>(1.f);
-                ones[2] = static_cast<bf16>(1.f);
-            }
-            s[kt2] = mfma32(ag, ones, s[kt2]);
-        }
-    }
-    if (DIAG) {
-        // S^T += Y^T strictUpper(X)^T ;  X^T <- lower part (m <= i)
-        bf16x8 xu[KSC];
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks)
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int v = 8 * (ks & 1) + t;
-                const int m = 32 * (ks >> 1) + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const float xv = x[ks >> 1][v];
-                xu[ks][t] = static_cast<bf16>(m > iloc ? xv : 0.f);
-                x[ks >> 1][v] = (m <= iloc) ? xv : 0.f;
-            }
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2) {
-            const bf16* ay = sY + (32 * kt2 + l32) * C;
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) s[kt2] = mfma32(lds8(ay + st.offC(ks)), xu[ks], s[kt2]);
-        }
-    }
-    // carry the query through this chunk:  Q^T += (-U^T) X^T   (independent of
-    // the softmax below, so its MFMAs overlap with the vector work)
-    if (carry) {
-        bf16x8 xB[KSC];
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) xB[ks] = pack8(x[ks >> 1], ks & 1);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const bf16* au = sg.u + (32 * dt + l32) * C;
-#pragma unroll
-            for (int ks = 0; ks < KSC; ++ks) st.qacc[dt] = mfma32(lds8(au + st.offC(ks)), xB[ks], st.qacc[dt]);
-        }
-    }
-
-    // online softmax in log2 units: z = c2 * S + a_i.  Lane holds keys
-    // j = 32*kt2 + 8*(v/4) + 4*hh + v%4 of query iloc; lane^32 holds the rest.
-    const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            if (DIAG && (32 * kt2 + 8 * (v >> 2) + 4 * hh + (v & 3)) > iloc) s[kt2][v] = -INFINITY;
-            mx = fmaxf(mx, s[kt2][v]);
-        }
-    mx = pair_max(mx);
-    const float cand = fmaf(mx, c2, a_i);
-    if (__any(cand > st.m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(st.m_run, cand);
-        const float alpha = fast_exp2(st.m_run - m_new);
-        st.m_run = m_new;
-        st.l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
-    }
-    const float msub = st.m_run - a_i;
-    bf16x8 pB[KSC];
-    float psum = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KSC; ++ks) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-            pB[ks][t] = static_cast<bf16>(fast_exp2(fmaf(s[ks >> 1][8 * (ks & 1) + t], c2, -msub)));
-        // row sum of the rounded probabilities (the values the PV product uses)
-#pragma unroll
-        for (int t = 0; t < 8; t += 2) {
-            const bf16x2 pr = {pB[ks][t], pB[ks][t + 1]};
-            psum = __builtin_amdgcn_fdot2_f32_bf16(pr, bf16x2{bf16(1.f), bf16(1.f)}, psum, false);
-        }
-    }
-    st.l_run += psum;
-
-    // O^T += V^T P^T (d = 64: V as it is, through transpose loads)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-        const bf16* av = sg.v + (32 * dt + l32) * C;
-#pragma unroll
-        for (int ks = 0; ks < KSC; ++ks) {
-            bf16x8 a8;
-            if constexpr (D == 64) a8 = pv_operand(sg.v, st.voff, dt, ks);
-            else a8 = lds8(av + st.offC(ks));
-            st.oacc[dt] = mfma32(a8, pB[ks], st.oacc[dt]);
-        }
-    }
-    if (carry) {
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-    }
 }
 
 // x with every 32-bit lane word ANDed with msk (0 or ~0)
@@ -410,62 +239,23 @@ __device__ __forceinline__ float tile_max(const f32x16& s) {
 }
 
 // Raise the running maximum by shift >= 0: rescale O and l.
-template <bool GATE>
-__device__ __forceinline__ void raise_max(WaveState<64, GATE>& st, float shift) {
+template <int D, bool GATE>
+__device__ __forceinline__ void raise_max(WaveState<D, GATE>& st, float shift) {
     const float alpha = fast_exp2(-shift);
     st.m_run += shift;
     st.l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) st.oacc[dt][v] *= alpha;
 }
 
-// Per-lane setup shared by both kernels: block decode, query load, state.
+// A wave's query block, query chunk and row within it.
 template <int D, bool GATE>
 struct ScanSetup {
     int head, qb, qc, iloc, qi;
     bool active, qvalid;
 };
-
-// The wave's query chunk is qc, its query row within that chunk iloc.
-template <int D, bool GATE>
-__device__ __forceinline__ ScanSetup<D, GATE> scan_setup(const FwdArgs& a, WaveState<D, GATE>& st, int head,
-                                                          int qb, int qc, int iloc, int l32, int hh) {
-    constexpr int C = 64, DT = D / 32, KSD = D / 16;
-    ScanSetup<D, GATE> u;
-    u.head = head;
-    u.qb = qb;
-    u.qc = qc;
-    u.active = u.qc < a.N;
-    u.iloc = iloc;
-    u.qi = u.qc * C + u.iloc;
-    u.qvalid = u.active && u.qi < a.L;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
-    if (D != 64) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) st.offC_[ks & (D == 64 ? 0 : 3)] = ((2 * ks + hh) ^ swz_g<C>(l32)) << 3;
-    }
-    const bf16* qrow = static_cast<const bf16*>(a.q) + ((size_t)u.head * a.L + (u.qvalid ? u.qi : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-        bf16x8 q8 = {};
-        if (u.qvalid) q8 = lds8(qrow + 16 * ks + 8 * hh);
-        st.qB[ks] = q8;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
-    st.loc_i = (GATE && u.qvalid) ? a.loc[(size_t)u.head * a.N * C + u.qi] : 0.f;
-    st.dab = 0.0;
-    return u;
-}
 
 // Normalised output row and log-sum-exp (natural log).
 template <int D, bool GATE>
@@ -485,104 +275,6 @@ __device__ __forceinline__ void scan_store(const FwdArgs& a, const WaveState<D, 
         *reinterpret_cast<bf16x8*>(orow + 16 * ks + 8 * hh) = o8;
     }
     if (a.lse && hh == 0) a.lse[(size_t)u.head * a.L + u.qi] = (st.m_run + log2f(l_tot)) * kLn2;
-}
-
-// d = 128: every key chunk carries the query with the rank-C form
-// Q <- Q - (Q W^T) U.
-template <int D, bool GATE>
-__global__ __launch_bounds__(256, 1) void path_fwd_bf16_kernel(const FwdArgs a) {
-    constexpr int C = 64;
-    constexpr int TILE = C * D;   // elements of every staged tile
-
-    // two stage sets (distinct objects so the DMA target and the tiles being
-    // read are known not to alias), the diagonal-chunk Y^T tile, gate terms
-    __shared__ __attribute__((aligned(1024))) bf16 sK0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sU0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sV0[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sK1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sW1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sU1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sV1[TILE];
-    __shared__ __attribute__((aligned(1024))) bf16 sY[C * C];
-    __shared__ __attribute__((aligned(256))) float sLoc0[C];
-    __shared__ __attribute__((aligned(256))) float sLoc1[C];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int L = a.L, N = a.N, Lp = N * C;
-    WaveState<D, GATE> st;
-    int head0, qb0;
-    decode_block(blockIdx.x, a.BH, a.nqb, head0, qb0);
-    const ScanSetup<D, GATE> u =
-        scan_setup<D, GATE>(a, st, head0, qb0, 2 * qb0 + (wave >> 1), (wave & 1) * 32 + l32, l32, hh);
-    const int head = u.head, qb = u.qb, qc = u.qc, iloc = u.iloc;
-    const bool active = u.active;
-
-    const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
-    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
-    const bf16* ut = static_cast<const bf16*>(a.ut) + (size_t)head * N * D * C;
-    const bf16* vt = static_cast<const bf16*>(a.vt) + (size_t)head * N * D * C;
-    const bf16* yt = static_cast<const bf16*>(a.yt) + (size_t)head * N * C * C;
-    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
-
-    const Stage<D> stage0{sK0, sW0, sU0, sV0, nullptr, sLoc0, nullptr};
-    const Stage<D> stage1{sK1, sW1, sU1, sV1, nullptr, sLoc1, nullptr};
-
-    auto issue = [&](const Stage<D>& sg, int kc) {     // full chunk, asynchronous
-        copy_async<C, D>(sg.k, kt + (size_t)kc * C * D, wave, lane);
-        copy_async<C, D>(sg.w, win + (size_t)kc * C * D, wave, lane);
-        copy_async<D, C>(sg.u, ut + (size_t)kc * D * C, wave, lane);
-        copy_async<D, C>(sg.v, vt + (size_t)kc * D * C, wave, lane);
-        if (GATE && wave == 0)
-            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane),
-                                             (lds_void*)sg.loc, 4, 0, 0);
-    };
-    const float c2 = a.scale2;
-
-    // prologue: the top chunk (possibly the ragged last one: its W rows past
-    // L are zero-filled) and its Y^T
-    int kc = min(2 * qb + 1, N - 1);
-    copy_async<C, D>(sK0, kt + (size_t)kc * C * D, wave, lane);
-    copy_guarded<C, D>(sW0, win + (size_t)kc * C * D, min(C, L - kc * C), tid);
-    copy_async<D, C>(sU0, ut + (size_t)kc * D * C, wave, lane);
-    copy_async<D, C>(sV0, vt + (size_t)kc * D * C, wave, lane);
-    if (GATE && wave == 0)
-        __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sLoc0, 4, 0, 0);
-    copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
-    wait_vmem();
-    __syncthreads();
-
-    auto compute = [&](const Stage<D>& sg, int kcur) {
-        if (!active || kcur > qc) return;
-        const bool carry = kcur > 0;
-        if (kcur == qc)
-            scan_step<D, GATE, true>(st, sg, sY, l32, hh, iloc, carry, c2);
-        else
-            scan_step<D, GATE, false>(st, sg, sY, l32, hh, iloc, carry, c2);
-        if (GATE && carry) st.dab += static_cast<double>(a.csum[(size_t)head * N + kcur]);
-    };
-
-    for (;;) {
-        if (kc > 0) issue(stage1, kc - 1);
-        compute(stage0, kc);
-        wait_vmem();
-        __syncthreads();
-        if (kc == 0) break;
-        --kc;
-        if (kc >= 2 * qb) {           // second diagonal chunk of this block
-            copy_async<C, C>(sY, yt + (size_t)kc * C * C, wave, lane);
-            wait_vmem();
-            __syncthreads();
-        }
-        if (kc > 0) issue(stage0, kc - 1);
-        compute(stage1, kc);
-        wait_vmem();
-        __syncthreads();
-        if (kc == 0) break;
-        --kc;
-    }
-    scan_store<D, GATE>(a, st, u, hh);
 }
 
 // ---------------------------------------------------------------------------
@@ -709,7 +401,7 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
     float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
     if (__any(!(psum <= kRescaleTrigger))) {
         const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
-        raise_max(st, shift);
+        raise_max<64, GATE>(st, shift);
         psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
     }
     st.l_run += psum;
@@ -821,8 +513,8 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
     const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
 
-    const Stage<D> set0{km0.k, nullptr, nullptr, km0.v, km0.m, km0.loc, km0.gb};
-    const Stage<D> set1{km1.k, nullptr, nullptr, km1.v, km1.m, km1.loc, km1.gb};
+    const Stage<D> set0{km0.k, km0.v, km0.m, km0.loc, km0.gb};
+    const Stage<D> set1{km1.k, km1.v, km1.m, km1.loc, km1.gb};
 
     // every [64][64] tile: wave w copies its 1 KB block w (rows 8w .. 8w+7)
     auto tile = [&](bf16* lds, const bf16* g) {
@@ -981,10 +673,311 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// d = 128, two waves per SIMD in alternating phases.
+//
+// The workgroup layout, the start from the prepare stage's own-chunk state and
+// the persistent dealing are those of the d = 64 kernel; the carry is the
+// chunk's d x d product (Q^T += (-M^T) Q^T, 32 MFMAs per wave and chunk, the
+// same count as the rank-C form at d = 2C).  A wave's chunk is split as
+//     M(k): PV of chunk k+1 (16 MFMAs) and the logits of chunk k (16 + the
+//           bias k-step);
+//     V(k): the probabilities of chunk k (32 exps), then the carry through
+//           chunk k (32 MFMAs, -M^T operands read here),
+// so both waves of a SIMD issue MFMAs in every phase.  The staged tiles of
+// chunk c sit in set c % 2: K~ (and gate rows) read in M(c), -M^T in V(c),
+// V^T of c in M(c-1).  With P(c) the phase of the leaders' M(c), every
+// wave issues its share of K~(c-1), the gate rows of c-1 and V^T(c) at the
+// start of phase P(c) and of -M^T(c-1) at the start of phase P(c)+1, and
+// waits for a phase's copies at the end of the phase after it: each tile's
+// slot was last read two phases before its copy must be complete.
+// ---------------------------------------------------------------------------
+
+// The byte offset of lane `lane` of wave `wave` in the copy of a tile with
+// 256-byte rows (rows of 128 bf16, 16-byte units swizzled by row & 15): one
+// wave instruction fills 1 KB of LDS (lane i -> bytes 16i .. 16i+15), i.e.
+// rows 4w .. 4w+3 of each 32-row slab; the next slab is 8 KB further in
+// both memories and needs the same offset.
+__device__ __forceinline__ unsigned tile128_lane_offset(int wave, int lane) {
+    const int r = 4 * wave + (lane >> 4);
+    const int u = (lane & 15) ^ swz_g<128>(r);
+    return static_cast<unsigned>((r * 128 + u * 8) * 2);
+}
+
+// vmcnt(n) for the copy counts of the d = 128 phase loop
+__device__ __forceinline__ void wait_copies(int n) {
+    switch (n) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0f76); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    }
+}
+
+template <bool GATE>
+struct Tiles128 {
+    bf16 k[64 * 128];          // K~ [C][D], natural rows
+    bf16 m[128 * 128];         // -M^T [D][D]
+    bf16 v[128 * 64];          // V^T [D][C] (128-byte rows, swz_g<64>)
+    bf16 gb[GATE ? 64 * 16 : 8];
+    float loc[64 + 4];         // [64]: the chunk's gate sum
+};
+
+// Matrix phase: O^T += V^T P^T for the pending probabilities pB (V^T tile
+// sv), then (QK) the logits of chunk ck in s as z - m_run, with the bias
+// k-step of the d = 64 kernel.
+template <bool GATE, bool QK>
+__device__ __forceinline__ void pp128_mphase(WaveState<128, GATE>& st, f32x16 s[2], const bf16x8 pB[4],
+                                             const Tiles128<GATE>& ck, const bf16* sv, int l32, int hh) {
+    const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
+    const unsigned lower = hh ? 0u : ~0u;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            st.oacc[dt] = mfma32(lds8(sv + (32 * dt + l32) * 64 + st.offC(ks)), pB[ks], st.oacc[dt]);
+    if (!QK) return;
+    bf16x8 opg[2];
+    const float csum = GATE ? ck.loc[64] : 0.f;
+    if (GATE) {
+        opg[0] = lds8(ck.gb + l32 * 16 + 8 * hh);
+        opg[1] = lds8(ck.gb + (32 + l32) * 16 + 8 * hh);
+    } else {
+        opg[0] = opg[1] = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
+    }
+    bf16x8 bq;
+    {
+        const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
+        bf16 h, m, l;
+        split3(a_i - st.m_run, h, m, l);
+        bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
+    }
+#pragma unroll
+    for (int kt2 = 0; kt2 < 2; ++kt2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
+        s[kt2] = mfma32(opg[kt2], bq, s[kt2]);
+    }
+    // the carried query's bf16 operand is packed from its fp32 accumulator
+    // per k-step (it is not kept between phases: registers)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 qb = pack8(st.qacc[ks >> 1], ks & 1);
+#pragma unroll
+        for (int kt2 = 0; kt2 < 2; ++kt2)
+            s[kt2] = mfma32(lds8(ck.k + (32 * kt2 + l32) * 128 + st.offD[ks]), qb, s[kt2]);
+    }
+    if (GATE) st.dab += static_cast<double>(csum);
+}
+
+// Vector phase: the probabilities pB of the logits s (raising the running
+// maximum when a row sum passes kRescaleTrigger), then the carry through the
+// chunk, Q^T += (-M^T) Q^T.
+template <bool GATE>
+__device__ __forceinline__ void pp128_vphase(WaveState<128, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
+                                             const bf16* smt, int l32) {
+    float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
+    if (__any(!(psum <= kRescaleTrigger))) {
+        const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
+        raise_max<128, GATE>(st, shift);
+        psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
+    }
+    st.l_run += psum;
+    bf16x8 qb[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+            st.qacc[dt] = mfma32(lds8(smt + (32 * dt + l32) * 128 + st.offD[ks]), qb[ks], st.qacc[dt]);
+}
+
+template <bool GATE>
+__global__ __launch_bounds__(512, 1) void path_fwd_bf16_d128pp_kernel(const FwdArgs a) {
+    constexpr int C = 64, D = 128, NT = 512;
+    constexpr int KT = C * D;          // K~ and V^T tile elements
+    constexpr int MT = D * D;          // -M^T tile elements
+    __shared__ __attribute__((aligned(1024))) Tiles128<GATE> km0;
+    __shared__ __attribute__((aligned(1024))) Tiles128<GATE> km1;
+
+    const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const bool leader = wave_u >= 4;
+    const int nqb = (a.N + 3) / 4;
+
+    auto item = [&](const int head, const int qb, const FwdArgs& a, const int lane_in) {
+    const int lane = lane_in & 63;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int L = a.L, N = a.N, Lp = N * C;
+    const unsigned koff = tile128_lane_offset(wave_u, lane);
+    const unsigned voff = tile64_lane_offset(wave_u, lane);
+    WaveState<D, GATE> st;
+    bf16x8 pB[4];
+    const int qc = 4 * qb + (leader ? 7 - wave_u : wave_u);
+    const int iloc = (wave_u >> 2) * 32 + l32;
+    const bool active = qc < N;
+    ScanSetup<D, GATE> u;
+    u.head = head; u.qb = qb; u.qc = qc; u.iloc = iloc; u.active = active;
+    u.qi = qc * C + iloc;
+    u.qvalid = active && u.qi < L;
+    {
+        // the state after the query's own chunk, from the prepare stage
+        const size_t row = (size_t)head * Lp + (active ? u.qi : 0);
+        const bf16* qrow = static_cast<const bf16*>(a.qt) + row * D;
+        const bf16* prow = static_cast<const bf16*>(a.pd) + row * C;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
+            const bf16x8 q8 = lds8(qrow + 16 * ks + 8 * hh);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            st.offC_[ks] = ((2 * ks + hh) ^ swz_g<C>(l32)) << 3;
+            pB[ks] = lds8(prow + 16 * ks + 8 * hh);
+        }
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ml + 2 * row);
+        st.m_run = ml[0];
+        st.l_run = hh == 0 ? ml[1] : 0.f;   // the two lane halves' sums are added at the end
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
+        st.loc_i = GATE ? a.loc[row] : 0.f;
+        st.dab = GATE ? static_cast<double>(a.csum[(size_t)head * N + (active ? qc : 0)]) : 0.0;
+    }
+
+    const char* ktg = static_cast<const char*>(a.kt) + (size_t)head * Lp * D * 2;
+    const char* vtg = static_cast<const char*>(a.vt) + (size_t)head * Lp * D * 2;
+    const char* mtg = static_cast<const char*>(a.mt) + (size_t)head * N * MT * 2;
+    const float* locg = GATE ? a.loc + (size_t)head * Lp : nullptr;
+    const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
+    const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
+
+    // Copies (every wave its share; the number of copy instructions this wave
+    // issued is returned for the wait that follows the next phase).  A(c):
+    // K~ and gate rows of chunk c - 1, V^T of chunk c; B(c): -M^T of chunk
+    // c - 1.  Chunk c goes to set c % 2.
+    auto set_of = [&](int c) -> Tiles128<GATE>& { return (c & 1) ? km1 : km0; };
+    auto issue_a = [&](int c) {
+        int n = 0;
+        if (c >= 1) {
+            Tiles128<GATE>& t = set_of(c - 1);
+            const char* g = ktg + (size_t)(c - 1) * KT * 2;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma_lds16(g + 8192 * j, koff, reinterpret_cast<char*>(t.k) + 8192 * j + 1024 * wave_u);
+            n += 2;
+            if (GATE && wave_u < 2) {
+                dma_lds16(gbg + (size_t)(c - 1) * C * 16 + wave_u * 512, lane * 16, t.gb + wave_u * 512);
+                n += 1;
+            }
+            if (GATE && wave_u == 2) {
+                dma_lds4(locg + (c - 1) * C, lane * 4, t.loc);
+                if (lane == 0) dma_lds4(csg + (c - 1), 0, t.loc + C);
+                n += 2;
+            }
+        }
+        if (c >= 0) {
+            Tiles128<GATE>& t = set_of(c);
+            const char* g = vtg + (size_t)c * KT * 2;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dma_lds16(g + 8192 * j, voff, reinterpret_cast<char*>(t.v) + 8192 * j + 1024 * wave_u);
+            n += 2;
+        }
+        return n;
+    };
+    auto issue_b = [&](int c) {
+        if (c < 1) return 0;
+        Tiles128<GATE>& t = set_of(c - 1);
+        const char* g = mtg + (size_t)(c - 1) * MT * 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma_lds16(g + 8192 * j, koff, reinterpret_cast<char*>(t.m) + 8192 * j + 1024 * wave_u);
+        return 4;
+    };
+
+    // ---- key chunks ktop-1 .. 0 in phases, ktop = the block's top chunk.
+    // Every wave runs  for k = ktop-1 .. 0:  M(k); barrier; V(k); barrier,
+    // then PV(0); the followers (waves 0..3) enter one barrier late.  A
+    // leader issues A(k) in M(k) and B(k) in V(k); a follower B(k) in M(k)
+    // and A(k-1) in V(k).  The prologue stages A(ktop) and B(ktop). ----
+    const int ktop = min(4 * qb + 3, N - 1);
+    issue_a(ktop);
+    issue_b(ktop);
+    wait_vmem();
+    __syncthreads();
+    f32x16 s[2];
+    if (ktop > 0) {
+        if (!leader) {
+            wait_copies(issue_a(ktop - 1));
+            phase_barrier();
+        }
+        auto iter = [&](int k, const Tiles128<GATE>& ck, const Tiles128<GATE>& cn) {
+            // ck: chunk k (K~, -M^T) and V^T(k); cn: V^T(k + 1)
+            const bool go = active && k < qc;
+            int n = leader ? issue_a(k) : issue_b(k);
+            if (go) pp128_mphase<GATE, true>(st, s, pB, ck, cn.v, l32, hh);
+            wait_copies(n);
+            phase_barrier();
+            n = leader ? issue_b(k) : issue_a(k - 1);
+            if (go) pp128_vphase<GATE>(st, s, pB, ck.m, l32);
+            wait_copies(n);
+            phase_barrier();
+        };
+        int k = ktop - 1;
+        if ((k & 1) == 0) {
+            iter(k, km0, km1);
+            --k;
+        }
+        for (; k >= 0; k -= 2) {
+            iter(k, km1, km0);
+            iter(k - 1, km0, km1);
+        }
+    }
+    // PV(0) with the pending probabilities (the own chunk's, for qc = 0)
+    if (active) pp128_mphase<GATE, false>(st, s, pB, km0, km0.v, l32, hh);
+    if (ktop > 0 && leader) phase_barrier();
+    scan_store<D, GATE>(a, st, u, hh);
+    };
+
+    // Persistent workgroups: the dealing of the d = 64 kernel.
+    const int G = gridDim.x;
+    const int P = (nqb + 1) / 2;
+    const bool by_xcd = (a.BH % 8) == 0 && (G % 8) == 0;
+    const int R = by_xcd ? G / 8 : G;
+    const int r = by_xcd ? blockIdx.x / 8 : blockIdx.x;
+    const int xcd = by_xcd ? blockIdx.x % 8 : 0;
+    const int npairs = (by_xcd ? a.BH / 8 : a.BH) * P;
+    const bool single = a.single != 0;
+    for (int t = 0;; ++t) {
+        int i, qb;
+        if (single) {
+            if (t > 0) break;
+            i = r / nqb;
+            qb = nqb - 1 - r % nqb;
+        } else {
+            const int j = r + R * (t >> 1);
+            if (j >= npairs) break;
+            const int pr = j % P;
+            i = j / P;
+            qb = (t & 1) ? pr : nqb - 1 - pr;
+            if ((t & 1) && qb == nqb - 1 - pr) continue;
+        }
+        __syncthreads();
+        typedef const __attribute__((address_space(4))) FwdArgs* ArgPtr;
+        ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
+        int ln = static_cast<int>(threadIdx.x & 63);
+        asm volatile("" : "+s"(ap), "+v"(ln));
+        item(by_xcd ? xcd + 8 * i : i, qb, *(const FwdArgs*)ap, ln);
+    }
+}
+
 hipError_t launch_path_fwd_bf16(const FwdArgs& args, bool gate, hipStream_t s) {
     FwdArgs a = args;
-    const dim3 grid(a.BH * a.nqb), block(256);
-    if (a.D == 64) {
+    if (a.D == 64 || a.D == 128) {
         // persistent: one workgroup per CU (at most one per pair of query
         // blocks), or one per query block when all of them fit at once
         int dev = 0, ncu = 0;
@@ -998,11 +991,13 @@ hipError_t launch_path_fwd_bf16(const FwdArgs& args, bool gate, hipStream_t s) {
         long g = a.single ? blocks : (ncu < pairs ? ncu : pairs);
         if (!a.single && g >= 8 && a.BH % 8 == 0) g -= g % 8;
         const dim3 gridp(static_cast<unsigned>(g)), block8(512);
-        if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<true>), gridp, block8, 0, s, a);
-        else hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<false>), gridp, block8, 0, s, a);
-    } else if (a.D == 128) {
-        if (gate) hipLaunchKernelGGL((path_fwd_bf16_kernel<128, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((path_fwd_bf16_kernel<128, false>), grid, block, 0, s, a);
+        if (a.D == 64) {
+            if (gate) hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<true>), gridp, block8, 0, s, a);
+            else hipLaunchKernelGGL((path_fwd_bf16_d64pp_kernel<false>), gridp, block8, 0, s, a);
+        } else {
+            if (gate) hipLaunchKernelGGL((path_fwd_bf16_d128pp_kernel<true>), gridp, block8, 0, s, a);
+            else hipLaunchKernelGGL((path_fwd_bf16_d128pp_kernel<false>), gridp, block8, 0, s, a);
+        }
     } else {
         return hipErrorInvalidValue;
     }

@@ -51,8 +51,8 @@ __host__ __device__ constexpr int permk(int s) {  // applied inside each group o
 //     yt  [BH][N][C][C] bf16  Y^T (Y = T^{-1} strictLower(W K^T)): [j][sigma] = Y[permk(sigma)][j]
 //     zt  [BH][N][D][C] bf16  -Z^T (Z = T^{-T} W), laid out like ut (cache only)
 //     mt  [BH][N][D][D] bf16  -M^T, M = W^T U: [rho][d'] = -M[d'][permk(rho)]
-//                             (d = 64 forward only: dense d x d transport)
-//   The d = 64 forward has no ut / yt: its prepare stage also takes each
+//                             (forward: dense d x d transport)
+//   The bf16 forward has no ut / yt: its prepare stage also takes each
 //   query chunk's own-chunk (diagonal) step and writes instead
 //     qt  [BH][Lp][D]  bf16  the query carried to its chunk start,
 //                            q - lower(q W^T) U, times scale*log2(e)
@@ -78,11 +78,11 @@ struct Workspace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// The d = 64 bf16 forward carries queries through whole chunks with the
-// d x d product (2 d^2 flops per query and chunk, against 4 C d for the
-// rank-C form); at d = 128 (= 2C) both cost the same and the rank-C form,
-// which needs no extra tile, is kept.
-inline bool dense_transport(size_t D, bool bf16_mode) { return bf16_mode && D == 64; }
+// The bf16 forward carries queries through whole chunks with the d x d
+// product (2 d^2 flops per query and chunk, against 4 C d for the rank-C
+// form: half at d = 64, the same at d = 128 = 2C, where it needs one operand
+// tile per chunk instead of two and no intermediate Q W^T).
+inline bool dense_transport(size_t D, bool bf16_mode) { return bf16_mode && (D == 64 || D == 128); }
 
 inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
                                 bool bf16_mode, bool gate, bool with_z) {
@@ -91,7 +91,7 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
     const size_t es = bf16_mode ? 2 : 4;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
-    // the d = 64 forward: own-chunk step in the prepare stage (no ut / yt)
+    // the bf16 forward: own-chunk step in the prepare stage (no ut / yt)
     // the key-cache hand-off (with_z): kt, zt and the group products only
     const bool diag = !with_z && dense_transport(D, bf16_mode);
     const size_t NG = (N + kKcacheGroup - 1) / kKcacheGroup;
@@ -119,7 +119,7 @@ inline Workspace plan_workspace(size_t BH, size_t L, size_t D, size_t C,
 // Kernel argument blocks.
 // ---------------------------------------------------------------------------
 struct UtArgs {
-    const void* q;         // d = 64 forward: queries of the own-chunk step (else null)
+    const void* q;         // bf16 forward: queries of the own-chunk step (else null)
     float scale2;          // scale * log2(e) (own-chunk step)
     const void* k;
     const void* v;
@@ -136,7 +136,7 @@ struct UtArgs {
     float* loc;            // null without gate
     float* csum;
     void* gb;              // may be null (gate bias rows, d x d transport)
-    void* qt;              // d = 64 forward: own-chunk step outputs (else null)
+    void* qt;              // bf16 forward: own-chunk step outputs (else null)
     void* pd;
     float* ml;
 };
@@ -150,11 +150,11 @@ struct FwdArgs {
     const void* ut;
     const void* vt;        // bf16 d = 128: V^T tiles (otherwise v is read)
     const void* yt;
-    const void* mt;        // d = 64: -M^T tiles
+    const void* mt;        // bf16: -M^T tiles
     const float* loc;
     const float* csum;
-    const void* gb;        // d = 64 with gate: bias rows of the key chunks
-    const void* qt;        // d = 64: own-chunk step results of the prepare stage
+    const void* gb;        // bf16 with gate: bias rows of the key chunks
+    const void* qt;        // bf16: own-chunk step results of the prepare stage
     const void* pd;
     const float* ml;
     void* out;

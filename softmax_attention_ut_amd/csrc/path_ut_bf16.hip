@@ -13,16 +13,17 @@
 //     kt [Lp][D]   K~ rows, natural
 //     ut [N][D][C] -U^T:  ut[rho][sigma] = -U[permk(sigma)][permk(rho)]
 //     vt [N][D][C]  V^T:  vt[rho][sigma] =  V[permk(sigma)][permk(rho)]
-//                  (d = 128 only: the d = 64 scan reads V as it is)
+//                  (d = 128 only: the d = 64 scan reads V as it is with
+//                  transpose loads)
 //     yt [N][C][C]  Y^T:  yt[j][sigma]   =  Y[permk(sigma)][j]
 //     zt [N][D][C] -Z^T, laid out like ut (key-cache hand-off only)
 //     mt [N][D][D] -M^T with M = W^T U (the chunk's product is I - M in
 //                  row-vector form): mt[rho][d'] = -M[d'][permk(rho)]
-//                  (optional; the d = 64 scan carries queries with it)
+//                  (optional; the forward scan carries queries with it)
 // plus the chunk-local forget-gate sums.
 //
-// The d = 64 forward instance (DIAG) also takes each query chunk's step with
-// its own chunk (phase 4 below) and writes the carried query, the pending
+// The forward instances (DIAG) also take each query chunk's step with its own
+// chunk (phase 4 below) and write the carried query, the pending
 // probabilities and their maximum and sum instead of ut and yt.
 //
 // Arithmetic.  G = W W^T and R = W K^T are bf16 MFMAs with fp32
@@ -93,13 +94,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // Three workgroups per CU where LDS allows it (d = 64 without Z: 46 KB, held
 // to 136 VGPRs by the bound); the other instances need more LDS per workgroup.
 //
-// DIAG (d = 64 forward): the chunk's own-chunk step of the scan is taken here
-// too, for its 64 queries (phase 4 below): the query carried to the chunk
-// start and the probabilities of the chunk's own keys, with their maximum and
-// sum.  U and Y then stay on chip (they serve no other step).
+// DIAG (forward): the chunk's own-chunk step of the scan is taken here too,
+// for its 64 queries (phase 4 below): the query carried to the chunk start and
+// the probabilities of the chunk's own keys, with their maximum and sum.  U
+// and Y then stay on chip (they serve no other step).
 template <int D, bool WITH_Z, bool DIAG>
 __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf16_kernel(const UtArgs a) {
-    static_assert(!DIAG || (D == 64 && !WITH_Z), "the own-chunk step is a d = 64 forward stage");
+    static_assert(!DIAG || !WITH_Z, "the own-chunk step is a forward stage");
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
     constexpr int PT = C + 8;     // pitch of [x][token-slot] bf16 tiles
@@ -361,9 +362,9 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     __syncthreads();
 
     // ---- phase 3 ----
-    // DIAG: the Y^T rows (waves 0, 1) and -U^T rows (waves 2, 3) are kept in
-    // registers for phase 4 instead of being stored.
-    bf16x8 keep[4];
+    // DIAG: the Y^T rows (waves 0, 1) and -U^T rows (waves 2, 3: d / 64 row
+    // tiles each) are kept in registers for phase 4 instead of being stored.
+    bf16x8 keep[D / 16];
     // R, Y and T^{-1} are triangular: tiles and k-steps that only meet their
     // zero blocks are skipped (key tile jt is wave-uniform, a compile-time
     // case each).
@@ -449,7 +450,9 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
         else keys(std::integral_constant<int, 1>{});
     } else {
         // waves 2, 3: U (and Z) for every token, a subset of the d columns
-        for (int et = wave - 2; et < ET; et += 2) {
+#pragma unroll
+        for (int ei = 0; ei < ET / 2; ++ei) {
+            const int et = wave - 2 + 2 * ei;
             const int e = 32 * et + l32;         // sWt row rho: d = permk(rho)
             const bf16* bw = sWt + e * PT + 8 * hh;
             // U[m][e] = sum_n T^{-1}[m][n] W[n][e]  (not needed by the hand-off)
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
             for (int mt = 0; mt < 2 && !WITH_Z; ++mt)
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
-                    if (DIAG) keep[2 * mt + s2] = cvt8(uacc[mt], s2, -1.f);
+                    if (DIAG) keep[4 * ei + 2 * mt + s2] = cvt8(uacc[mt], s2, -1.f);
                     else *reinterpret_cast<bf16x8*>(urow + 32 * mt + 16 * s2 + 8 * hh) = cvt8(uacc[mt], s2, -1.f);
                 }
             if (!WITH_Z && a.mt) {
@@ -531,17 +534,25 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
         // in the scan's transposed orientation (S^T = K Q^T - Y^T lower(X)^T,
         // q~^T = Q^T + (-U^T) lower(X)^T), lower(X)^T coming out of the X^T
         // accumulator as the B operand over m.  Y^T and -U^T go over the T^{-1}
-        // tiles, which are no longer read.
-        bf16* const sYt = sTh;      // -Y^T rows j, m in slots
-        bf16* const sUt = sTl;      // -U^T rows rho, m in slots
+        // tiles (d = 128: -U^T fills both, Y^T goes over the W^T tile), which
+        // are no longer read.
+        bf16* const sUt = sTh;                     // -U^T rows rho, m in slots
+        bf16* const sYt = D == 64 ? sTl : sWt;     // -Y^T rows j, m in slots
         __syncthreads();
         {
-            bf16* dst = (wave < 2 ? sYt : sUt) + (32 * (wave & 1) + l32) * PT;
+            auto put = [&](bf16* dst, int i) {
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-                    *reinterpret_cast<bf16x8*>(dst + 32 * b + 16 * s2 + 8 * hh) = keep[2 * b + s2];
+                    for (int s2 = 0; s2 < 2; ++s2)
+                        *reinterpret_cast<bf16x8*>(dst + 32 * b + 16 * s2 + 8 * hh) = keep[4 * i + 2 * b + s2];
+            };
+            if (wave < 2) {
+                put(sYt + (32 * wave + l32) * PT, 0);
+            } else {
+#pragma unroll
+                for (int ei = 0; ei < ET / 2; ++ei) put(sUt + (32 * (wave - 2 + 2 * ei) + l32) * PT, ei);
+            }
         }
         __syncthreads();
         // wave w: query tile QT = w & 1 (rows 32 QT .. +31), role w >> 1 (0: the
@@ -630,20 +641,20 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
                 if (hh == 0) *reinterpret_cast<f32x2*>(a.ml + 2 * row) = f32x2{mx, psum};
             } else {
                 // q~^T = Q^T + (-U^T) lower(X)^T, then times scale log2(e)
-                f32x16 qacc[2];
+                f32x16 qacc[ET];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
                     for (int t = 0; t < 8; ++t) qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(qv[ks][t]);
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt)
+                for (int dt = 0; dt < ET; ++dt)
 #pragma unroll
                     for (int ks = 0; ks < KM; ++ks)
                         qacc[dt] = mfma(ld8(sUt + (32 * dt + l32) * PT + 16 * ks + 8 * hh), xl[ks], qacc[dt]);
                 // register 8 s + t of tile dt holds d = 32 dt + 16 s + 8 hh + t
                 bf16* qrow = static_cast<bf16*>(a.qt) + row * D;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
+                for (int ks = 0; ks < KSD; ++ks)
                     *reinterpret_cast<bf16x8*>(qrow + 16 * ks + 8 * hh) = cvt8(qacc[ks >> 1], ks & 1, a.scale2);
             }
         };
@@ -667,6 +678,7 @@ hipError_t launch_path_ut_bf16(const UtArgs& a, hipStream_t s) {
         else hipLaunchKernelGGL((path_ut_bf16_kernel<64, false, false>), grid, block, 0, s, a);
     } else if (a.D == 128) {
         if (z) hipLaunchKernelGGL((path_ut_bf16_kernel<128, true, false>), grid, block, 0, s, a);
+        else if (a.qt) hipLaunchKernelGGL((path_ut_bf16_kernel<128, false, true>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((path_ut_bf16_kernel<128, false, false>), grid, block, 0, s, a);
     } else {
         return hipErrorInvalidValue;

@@ -8,13 +8,15 @@ and the k-slot permutation permk of the transposed tiles.  Checked, per head
 and chunk, on the bf16-rounded inputs the GPU receives:
   K~   every key carried to its chunk end, H_end ... H_{j+1} k_j
        (oracle.transported_keys);
-  U^T, Y^T (d = 128) and M^T (d = 64), from T^{-1} = (I + strictLower(D W
-       W^T))^{-1} D (oracle.ut_tinv): U = T^{-1} W, Y = T^{-1} strictLower(W
-       K^T), I - M = I - W^T U = oracle.ut_product;
+  M^T (forward, d = 64 and 128), from T^{-1} = (I + strictLower(D W
+       W^T))^{-1} D (oracle.ut_tinv): I - M = I - W^T U = oracle.ut_product;
+  U = T^{-1} W and Y = T^{-1} strictLower(W K^T) (the backward's prepare
+       stage, read back from its workspace after path_attn_bwd, where they
+       are row-major tiles);
   V^T  (d = 128) an exact copy;
   the chunk-local gate sums loc_j = -sum_{s>j}^{end} log2 f_s and the chunk
        totals csum;
-  (d = 64) the own-chunk step: the query carried to the chunk start times
+  (forward) the own-chunk step: the query carried to the chunk start times
        scale log2(e), the row maximum m_i and sum l_i of exp2(z_ij - m_i) over
        the own keys, and those probabilities, z_ij the logits in log2 units
        from the full-matrix form (oracle.full_matrix_logits) plus the gate.
@@ -67,8 +69,9 @@ def _sections(BH, L, D, diag):
     take("kt", BH * Lp * D * 2)
     if not diag:
         take("ut", BH * Lp * D * 2)
-        if D != 64:
-            take("vt", BH * Lp * D * 2)
+    if D != 64:
+        take("vt", BH * Lp * D * 2)
+    if not diag:
         take("yt", BH * N * C * C * 2)
     if diag:
         take("mt", BH * N * D * D * 2)
@@ -144,37 +147,65 @@ def _common(inp, ws, sec, D, L):
     assert worst <= 2.0 ** -7
 
 
-def test_prepare_d128_ut_quantities():
-    """d = 128 (rank-C carry): K~, -U^T, Y^T, V^T, gate sums; L = 200 leaves
-    a ragged last chunk (w = 0, beta = 0 padding: H = I there)."""
-    B, H, L, D = 1, 2, 200, 128
+def _bwd_sections(BH, L):
+    """Byte offsets of the backward workspace's prepare-stage sections (d =
+    64), in the library's order."""
+    D = 64
+    N = (L + C - 1) // C
+    Lp = N * C
+    off = 0
+    sec = {}
+    for name, nbytes in (("kt", BH * Lp * D * 2), ("ut", BH * Lp * D * 2), ("yt", BH * N * C * C * 2),
+                         ("mt", BH * N * D * D * 2), ("loc", BH * Lp * 4), ("csum", BH * N * 4)):
+        sec[name] = (off, nbytes)
+        off += _a256(nbytes)
+    return sec, off
+
+
+def test_prepare_backward_u_and_y():
+    """d = 64, the backward's prepare stage: K~, U, Y, -M^T, gate sums; L =
+    200 leaves a ragged last chunk (w = 0, beta = 0 padding: H = I there).
+    After path_attn_bwd the U and Y sections hold row-major U[m][e] and
+    Y[m][j] (the backward's layout pass rewrites them in place)."""
+    B, H, L, D = 1, 2, 200, 64
+    scale = 0.125
     inp = generate(B, H, L, D, dtype="bf16", gate=True, seed=401)
-    ws, sec = _prepare(inp, 1 / math.sqrt(D), diag=False)
+    g = {k: (None if t is None else t.cuda()) for k, t in vars(inp).items()}
+    n = pa.path_attn_bwd_workspace_bytes(B, H, L, D, pa.PATH_BF16)
+    sec, total = _bwd_sections(B * H, L)
+    assert total <= n, (total, n)
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    out = torch.zeros_like(g["q"])
+    lse = torch.zeros(B, H, L, dtype=torch.float32, device="cuda")
+    dout = torch.zeros_like(g["q"])
+    grads = [torch.zeros(B, H, L, D, dtype=torch.float32, device="cuda") for _ in range(4)]
+    dbeta = torch.zeros(B, H, L, dtype=torch.float32, device="cuda")
+    dlogf = torch.zeros(B, H, L, dtype=torch.float32, device="cuda")
+    pa.path_attn_bwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], out, lse, dout,
+                     *grads, dbeta, dlogf, scale, workspace=ws)
+    torch.cuda.synchronize()
     _common(inp, ws, sec, D, L)
     N = (L + C - 1) // C
-    ut = _view(ws, sec, "ut", torch.bfloat16, (H, N, D, C))
-    vt = _view(ws, sec, "vt", torch.bfloat16, (H, N, D, C))
-    yt = _view(ws, sec, "yt", torch.bfloat16, (H, N, C, C))
+    U_ = _view(ws, sec, "ut", torch.bfloat16, (H, N, C, D))
+    Y_ = _view(ws, sec, "yt", torch.bfloat16, (H, N, C, C))
+    mt = _view(ws, sec, "mt", torch.bfloat16, (H, N, D, D))
     for h in range(H):
         for c in range(N):
             q, k, v, w, beta, lf = (_pad(x, C) for x in _chunk(inp, h, c, L))
             tinv = oracle.ut_tinv(w, beta)
-            U = tinv @ w                                        # [m][e]
-            Y = tinv @ np.tril(w @ k.T, -1)                     # [m][j]
-            # ut[rho][sigma] = -U[permk(sigma)][permk(rho)]; yt[j][sigma] = Y[permk(sigma)][j];
-            # vt[rho][sigma] = V[permk(sigma)][permk(rho)]
-            pk_d = np.array([permk(r) for r in range(D)])
-            _tile_close(ut[h, c], -U[PK][:, pk_d].T, f"-U^T h={h} c={c}")
-            _tile_close(yt[h, c], Y[PK].T, f"Y^T h={h} c={c}")
-            np.testing.assert_array_equal(vt[h, c], v[PK][:, pk_d].T)
+            _tile_close(U_[h, c], tinv @ w, f"U h={h} c={c}")
+            _tile_close(Y_[h, c], tinv @ np.tril(w @ k.T, -1), f"Y h={h} c={c}")
+            M = np.eye(D) - oracle.ut_product(w, beta)
+            _tile_close(mt[h, c], -M[:, PK].T, f"-M^T h={h} c={c}")
 
 
-def test_prepare_d64_dense_carry_and_own_chunk():
-    """d = 64 (dense d x d carry, the own-chunk step in the prepare stage):
+@pytest.mark.parametrize("D,L", [(64, 333), (128, 200)])
+def test_prepare_dense_carry_and_own_chunk(D, L):
+    """The forward's prepare stage (dense d x d carry, the own-chunk step):
     K~, -M^T, the carried queries, the own chunk's row maximum and sum and
-    its probabilities, gate sums; L = 333 (ragged)."""
-    B, H, L, D = 1, 2, 333, 64
-    scale = 0.125
+    its probabilities, gate sums, and at d = 128 the V^T tiles; ragged L."""
+    B, H = 1, 2
+    scale = 1 / math.sqrt(D)
     s2 = scale * math.log2(math.e)
     inp = generate(B, H, L, D, dtype="bf16", gate=True, seed=402)
     ws, sec = _prepare(inp, scale, diag=True)
@@ -185,13 +216,17 @@ def test_prepare_d64_dense_carry_and_own_chunk():
     qt = _view(ws, sec, "qt", torch.bfloat16, (H, Lp, D))
     pd = _view(ws, sec, "pd", torch.bfloat16, (H, Lp, C))
     ml = _view(ws, sec, "ml", torch.float32, (H, Lp, 2))
+    vt = _view(ws, sec, "vt", torch.bfloat16, (H, N, D, C)) if D != 64 else None
+    pk_d = np.array([permk(r) for r in range(D)])
     worst_m = 0.0
     for h in range(H):
         for c in range(N):
             n = min(C, L - c * C)
             q, k, v, w, beta, lf = (_pad(x, C) for x in _chunk(inp, h, c, L))
             M = np.eye(D) - oracle.ut_product(w, beta)          # I - M = chunk product
-            _tile_close(mt[h, c], -M[:, PK].T, f"-M^T h={h} c={c}")
+            _tile_close(mt[h, c], -M[:, pk_d].T, f"-M^T h={h} c={c}")
+            if vt is not None:                                  # vt[rho][sigma] = V[permk(sigma)][permk(rho)]
+                np.testing.assert_array_equal(vt[h, c], v[PK][:, pk_d].T)
             U = oracle.ut_tinv(w, beta) @ w
             qc = (q - np.tril(q @ w.T) @ U) * s2
             got = qt[h, c * C:c * C + n]
