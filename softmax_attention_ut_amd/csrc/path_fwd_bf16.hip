@@ -183,6 +183,8 @@ struct WaveState {
     int offD[KSD];     // swizzled offsets of unit 2ks+hh in a D-wide row  (row = 32x + lane%32)
     int offC_[D == 64 ? 1 : 4];   // same in a 64-wide row, k-steps 0..3 (d = 64: equal to offD)
     unsigned voff[D == 64 ? 8 : 1]; // d = 64: transpose-load offsets of the PV operands
+    unsigned lb, lbv;  // d = 128: byte offset of the lane's k-step 0 unit in a 256-byte
+                       // (lb) and a 128-byte (lbv) row tile, rows 32x + lane%32
     __device__ __forceinline__ int offC(int ks) const { return D == 64 ? offD[ks] : offC_[ks]; }
 };
 
@@ -387,18 +389,30 @@ __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], 
 }
 
 // Vector phase of one wave: the carry of the query through the chunk,
-// Q^T += (-M^T) Q^T (operands opm from the matrix phase; the MFMAs go first
-// and run under the probabilities), the logits s turned into probabilities
-// pB (raising the running maximum when a row sum passes kRescaleTrigger),
-// and the carried query's new operand.
+// Q^T += (-M^T) Q^T (operands opm from the matrix phase), with four of the
+// probabilities exp2(z - m_run) of the logits s after each of its eight MFMAs
+// (so the exps issue while the other wave of the SIMD keeps the matrix pipe
+// busy), then the row sums (raising the running maximum and recomputing the
+// probabilities when a row sum passes kRescaleTrigger) and the carried
+// query's new operand.
 template <bool GATE>
 __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
                                           const bf16x8 opm[8]) {
 #pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ks = i >> 1, dt = i & 1;
+        st.qacc[dt] = mfma32(opm[4 * dt + ks], st.qB[ks], st.qacc[dt]);
+#pragma unroll
+        for (int e = 4 * i; e < 4 * i + 4; ++e) pB[e >> 3][e & 7] = static_cast<bf16>(fast_exp2(s[e >> 4][e & 15]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const bf16 one = static_cast<bf16>(1.f);
+    float psum = 0.f;
+#pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) st.qacc[dt] = mfma32(opm[4 * dt + ks], st.qB[ks], st.qacc[dt]);
-    float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
+        for (int t = 0; t < 8; t += 2)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pB[ks][t], pB[ks][t + 1]}, bf16x2{one, one}, psum, false);
     if (__any(!(psum <= kRescaleTrigger))) {
         const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
         raise_max<64, GATE>(st, shift);
@@ -726,74 +740,116 @@ struct Tiles128 {
     float loc[64 + 4];         // [64]: the chunk's gate sum
 };
 
+// The phases' MFMAs run as one software-pipelined sequence each: step i
+// issues the LDS read of step i + kAhead's A operand, then its own MFMA, and
+// a scheduling barrier closes the step, so at most kAhead + 1 operands are in
+// registers (the compiler would otherwise hoist every read of the phase and
+// run out of registers).
+constexpr int kAhead = 3;
+
+// A operand of k-step ks, rows 32 x + lane % 32, in a swizzled tile at byte
+// address t: the lane's unit in k-step ks is its k-step-0 unit XOR 2 ks (the
+// swizzle is an XOR of the unit index), i.e. byte offset lb ^ 32 ks.
+__device__ __forceinline__ bf16x8 tile_op(const void* t, unsigned lb, int ks, int xbytes) {
+    return lds8(reinterpret_cast<const bf16*>(static_cast<const char*>(t) + (lb ^ (32u * ks)) + xbytes));
+}
+
 // Matrix phase: O^T += V^T P^T for the pending probabilities pB (V^T tile
-// sv), then (QK) the logits of chunk ck in s as z - m_run, with the bias
-// k-step of the d = 64 kernel.
+// sv), then (QK) the logits of chunk ck in s as z - m_run.  Steps 0..15: PV
+// (k-step ks = i / 4, row tile dt = i % 4); 16, 17: the start of key tiles 0,
+// 1 (with the gate the bias k-step of the d = 64 kernel, else -m_run in
+// fp32); 18..33: the logits (k-step (i - 18) / 2, key tile (i - 18) % 2), the
+// carried query's operand packed from its fp32 accumulator at its first use.
 template <bool GATE, bool QK>
 __device__ __forceinline__ void pp128_mphase(WaveState<128, GATE>& st, f32x16 s[2], const bf16x8 pB[4],
                                              const Tiles128<GATE>& ck, const bf16* sv, int l32, int hh) {
     const bf16 one = static_cast<bf16>(1.f), nil = static_cast<bf16>(0.f);
-    const unsigned lower = hh ? 0u : ~0u;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            st.oacc[dt] = mfma32(lds8(sv + (32 * dt + l32) * 64 + st.offC(ks)), pB[ks], st.oacc[dt]);
-    if (!QK) return;
-    bf16x8 opg[2];
-    const float csum = GATE ? ck.loc[64] : 0.f;
-    if (GATE) {
-        opg[0] = lds8(ck.gb + l32 * 16 + 8 * hh);
-        opg[1] = lds8(ck.gb + (32 + l32) * 16 + 8 * hh);
-    } else {
-        opg[0] = opg[1] = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
-    }
-    bf16x8 bq;
-    {
+    // per-phase opaque copies: values derived from them (the operand
+    // addresses, the constant bias rows) are recomputed in the phase instead
+    // of being kept in registers across the loop
+    unsigned lower = hh ? 0u : ~0u, lb = st.lb, lbv = st.lbv;
+    asm volatile("" : "+v"(lower), "+v"(lb), "+v"(lbv));
+    constexpr int NSTEP = QK ? 34 : 16;
+    const float csum = (GATE && QK) ? ck.loc[64] : 0.f;
+    bf16x8 bq = {};
+    if (QK) {
         const float a_i = GATE ? st.loc_i + static_cast<float>(st.dab) : 0.f;
         bf16 h, m, l;
         split3(a_i - st.m_run, h, m, l);
         bq = mask8(bf16x8{one, one, one, h, m, l, nil, nil}, lower);
     }
+    const bf16x8 gconst = mask8(bf16x8{nil, nil, nil, one, one, one, nil, nil}, lower);
+    auto load = [&](int i) -> bf16x8 {
+        if (i < 16) return tile_op(sv, lbv, i >> 2, 4096 * (i & 3));
+        if (i < 18) return GATE ? lds8(ck.gb + (32 * (i - 16) + l32) * 16 + 8 * hh) : gconst;
+        const int j = i - 18;
+        return tile_op(ck.k, lb, j >> 1, 8192 * (j & 1));
+    };
+    bf16x8 buf[kAhead + 1];
 #pragma unroll
-    for (int kt2 = 0; kt2 < 2; ++kt2) {
+    for (int i = 0; i < kAhead; ++i) buf[i] = load(i);
+    bf16x8 qb = {};
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[kt2][v] = 0.f;
-        s[kt2] = mfma32(opg[kt2], bq, s[kt2]);
+    for (int i = 0; i < NSTEP; ++i) {
+        if (i + kAhead < NSTEP) buf[(i + kAhead) % (kAhead + 1)] = load(i + kAhead);
+        const bf16x8 op = buf[i % (kAhead + 1)];
+        if (i < 16) {
+            st.oacc[i & 3] = mfma32(op, pB[i >> 2], st.oacc[i & 3]);
+        } else if (i < 18) {
+            f32x16 z;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) z[v] = GATE ? 0.f : -st.m_run;
+            s[i - 16] = GATE ? mfma32(op, bq, z) : z;
+        } else {
+            const int j = i - 18;
+            if ((j & 1) == 0) qb = pack8(st.qacc[j >> 2], (j >> 1) & 1);
+            s[j & 1] = mfma32(op, qb, s[j & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
-    // the carried query's bf16 operand is packed from its fp32 accumulator
-    // per k-step (it is not kept between phases: registers)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 qb = pack8(st.qacc[ks >> 1], ks & 1);
-#pragma unroll
-        for (int kt2 = 0; kt2 < 2; ++kt2)
-            s[kt2] = mfma32(lds8(ck.k + (32 * kt2 + l32) * 128 + st.offD[ks]), qb, s[kt2]);
-    }
-    if (GATE) st.dab += static_cast<double>(csum);
+    if (GATE && QK) st.dab += static_cast<double>(csum);
 }
 
-// Vector phase: the probabilities pB of the logits s (raising the running
-// maximum when a row sum passes kRescaleTrigger), then the carry through the
-// chunk, Q^T += (-M^T) Q^T.
+// Vector phase: the carry through the chunk, Q^T += (-M^T) Q^T (32 steps,
+// k-step ks = i / 4, row tile dt = i % 4, the query's eight operands packed
+// before the first MFMA changes it), one probability exp2(z - m_run) of the
+// logits s per step, then the row sums (raising the running maximum and
+// recomputing the probabilities when a row sum passes kRescaleTrigger).
+// Spreading the exps over the carry lets them issue while the other wave of
+// the SIMD keeps the matrix pipe busy.
 template <bool GATE>
 __device__ __forceinline__ void pp128_vphase(WaveState<128, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
                                              const bf16* smt, int l32) {
-    float psum = tile_probs(s[0], pB[0], pB[1], 0.f) + tile_probs(s[1], pB[2], pB[3], 0.f);
+    unsigned lb = st.lb;
+    asm volatile("" : "+v"(lb));
+    auto load = [&](int i) -> bf16x8 { return tile_op(smt, lb, i >> 2, 8192 * (i & 3)); };
+    bf16x8 buf[kAhead + 1];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) buf[i] = load(i);
+    bf16x8 qb[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = pack8(st.qacc[ks >> 1], ks & 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        if (i + kAhead < 32) buf[(i + kAhead) % (kAhead + 1)] = load(i + kAhead);
+        st.qacc[i & 3] = mfma32(buf[i % (kAhead + 1)], qb[i >> 2], st.qacc[i & 3]);
+        pB[i >> 3][i & 7] = static_cast<bf16>(fast_exp2(s[i >> 4][i & 15]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const bf16 one = static_cast<bf16>(1.f);
+    float psum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; t += 2)
+            psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pB[ks][t], pB[ks][t + 1]}, bf16x2{one, one}, psum, false);
     if (__any(!(psum <= kRescaleTrigger))) {
         const float shift = fmaxf(pair_max(fmaxf(tile_max(s[0]), tile_max(s[1]))), 0.f);
         raise_max<128, GATE>(st, shift);
         psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
     }
     st.l_run += psum;
-    bf16x8 qb[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qb[ks] = pack8(st.qacc[ks >> 1], ks & 1);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-            st.qacc[dt] = mfma32(lds8(smt + (32 * dt + l32) * 128 + st.offD[ks]), qb[ks], st.qacc[dt]);
 }
 
 template <bool GATE>
@@ -828,18 +884,16 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d128pp_kernel(const FwdA
         const size_t row = (size_t)head * Lp + (active ? u.qi : 0);
         const bf16* qrow = static_cast<const bf16*>(a.qt) + row * D;
         const bf16* prow = static_cast<const bf16*>(a.pd) + row * C;
+        st.lb = static_cast<unsigned>(l32 * 256 + 16 * (hh ^ swz_g<D>(l32)));
+        st.lbv = static_cast<unsigned>(l32 * 128 + 16 * (hh ^ swz_g<C>(l32)));
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
             const bf16x8 q8 = lds8(qrow + 16 * ks + 8 * hh);
 #pragma unroll
             for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(q8[t]);
         }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            st.offC_[ks] = ((2 * ks + hh) ^ swz_g<C>(l32)) << 3;
-            pB[ks] = lds8(prow + 16 * ks + 8 * hh);
-        }
+        for (int ks = 0; ks < 4; ++ks) pB[ks] = lds8(prow + 16 * ks + 8 * hh);
         const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ml + 2 * row);
         st.m_run = ml[0];
         st.l_run = hh == 0 ? ml[1] : 0.f;   // the two lane halves' sums are added at the end
