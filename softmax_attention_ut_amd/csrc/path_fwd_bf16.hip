@@ -299,8 +299,9 @@ __device__ __forceinline__ void scan_store(const FwdArgs& a, const WaveState<D, 
 // ---------------------------------------------------------------------------
 
 // Matrix phase of one wave: O^T += V^T P^T for the pending probabilities pB
-// (V tile sv), then with QK the logits of the staged chunk sg (left in s as
-// z - m_run), and the -M^T operands of the chunk's carry read into opm (the
+// (V tile sv), then with QK the carried query's bf16 operand (packed from its
+// accumulator under the PV MFMAs), the logits of the staged chunk sg (left in
+// s as z - m_run), and the -M^T operands of the chunk's carry read into opm (the
 // carry's MFMAs are issued in the vector phase, where they fill the matrix
 // pipe while the other wave of the SIMD issues the next logits).
 //
@@ -336,6 +337,8 @@ __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], 
             for (int ks = 0; ks < KS; ++ks) st.oacc[dt] = mfma32(opv[KS * dt + ks], pB[ks], st.oacc[dt]);
         return;
     }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
     bf16x8 opg[2], opk[2 * KS];
     const float csum = GATE ? sg.loc[64] : 0.f;   // the chunk's gate sum, for dab
     if (GATE) {
@@ -393,8 +396,9 @@ __device__ __forceinline__ void pp_mphase(WaveState<64, GATE>& st, f32x16 s[2], 
 // probabilities exp2(z - m_run) of the logits s after each of its eight MFMAs
 // (so the exps issue while the other wave of the SIMD keeps the matrix pipe
 // busy), then the row sums (raising the running maximum and recomputing the
-// probabilities when a row sum passes kRescaleTrigger) and the carried
-// query's new operand.
+// probabilities when a row sum passes kRescaleTrigger).  The carried query's
+// new operand is packed at the start of the next matrix phase, under its PV
+// MFMAs.
 template <bool GATE>
 __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
                                           const bf16x8 opm[8]) {
@@ -419,8 +423,6 @@ __device__ __forceinline__ void pp_vphase(WaveState<64, GATE>& st, const f32x16 
         psum = tile_probs(s[0], pB[0], pB[1], shift) + tile_probs(s[1], pB[2], pB[3], shift);
     }
     st.l_run += psum;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) st.qB[ks] = pack8(st.qacc[ks >> 1], ks & 1);
 }
 
 // Workgroup barrier without a memory fence: stage copies stay in flight

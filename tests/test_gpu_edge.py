@@ -2,8 +2,8 @@
 
 * Logits far above a row's diagonal maximum, up to overflowing fp32 if they
   were exponentiated unshifted: the online softmax must raise its running
-  maximum (the row-sum trigger of the d = 64 scan, the lazy raise of the
-  d = 128 scan) and recover from an infinite row sum.
+  maximum (the scans' row-sum trigger) and recover from an infinite row
+  sum.
 * Forget gates that cut the past (log f = -1e4 at single tokens, inside a
   chunk and on a chunk boundary): every earlier key gets weight 0, the key at
   the cut keeps its weight (the product runs over s = j+1 .. i).
