@@ -99,7 +99,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // the probabilities of the chunk's own keys, with their maximum and sum.  U
 // and Y then stay on chip (they serve no other step).
 template <int D, bool WITH_Z, bool DIAG>
-__global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf16_kernel(const UtArgs a) {
+__global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : (DIAG ? 2 : 1)) void path_ut_bf16_kernel(const UtArgs a) {
     static_assert(!DIAG || !WITH_Z, "the own-chunk step is a forward stage");
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
@@ -112,12 +112,15 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
     __shared__ __attribute__((aligned(16))) bf16 sK[C * PW];     // K rows
     __shared__ __attribute__((aligned(16))) bf16 sWt[D * PT];    // W^T: [rho][sigma] = W[permk(sigma)][permk(rho)]
     constexpr bool VT = D != 64 && !WITH_Z;  // V^T tiles are written (d = 128 forward)
-    __shared__ __attribute__((aligned(16))) bf16 sV[VT ? C * PW : 8];  // V rows
     // G rows (p < m used), then X^T over its upper triangle (fp32); once X is
     // complete the same space holds T^{-1} rows with n in slots, hi and lo
     // (2 x C x PT bf16 = C x GP fp32)
     static_assert(2 * PT * 2 == GP * 4, "T^{-1} hi/lo tiles fill the G tile");
     __shared__ __attribute__((aligned(16))) float sG[C * GP];
+    // V rows (d = 128 forward) are staged in the G tile: they are written out
+    // as V^T before phase 1 forms G there
+    static_assert(!VT || C * PW * 2 <= C * GP * 4, "V rows fit in the G tile");
+    bf16* const sV = reinterpret_cast<bf16*>(sG);
     bf16* const sTh = reinterpret_cast<bf16*>(sG);
     bf16* const sTl = reinterpret_cast<bf16*>(sG) + C * PT;
     __shared__ __attribute__((aligned(16))) bf16 sZh[WITH_Z ? C * PT : 8];  // T^{-T} rows, m slots
@@ -184,6 +187,21 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
         if (tid < C) sB[tid] = bta;
     }
     __syncthreads();
+    if constexpr (VT) {
+        // V^T tile, 8 token slots per 16-byte store, out of the staged rows
+        bf16* vt = static_cast<bf16*>(a.vt) + chunkbase * D * C;
+#pragma unroll
+        for (int it = 0; it < D * (C / 8) / 256; ++it) {
+            const int u = tid + 256 * it;
+            const int rho = u / (C / 8), s0 = (u % (C / 8)) * 8;
+            const int e = permk(rho);
+            bf16x8 col;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) col[t] = sV[permk(s0 + t) * PW + e];
+            *reinterpret_cast<bf16x8*>(vt + (size_t)rho * C + s0) = col;
+        }
+        __syncthreads();
+    }
 
     // ---- phase 1: G tiles (m-block >= p-block), accumulator rows p, cols m ----
     if (wave < 3) {
@@ -231,16 +249,6 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : 1) void path_ut_bf1
         for (int q = 0; q < 4; ++q)
             *reinterpret_cast<f32x4*>(xrow + 4 * q) = f32x4{t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]};
     } else {
-        // waves 1-3: V^T tile, 8 token slots per 16-byte store
-        bf16* vt = static_cast<bf16*>(a.vt) + chunkbase * D * C;
-        for (int u = tid - 64; VT && u < D * (C / 8); u += 192) {
-            const int rho = u / (C / 8), s0 = (u % (C / 8)) * 8;
-            const int e = permk(rho);
-            bf16x8 col;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) col[t] = sV[permk(s0 + t) * PW + e];
-            *reinterpret_cast<bf16x8*>(vt + (size_t)rho * C + s0) = col;
-        }
         if (DIAG && wave == 1 && !a.loc) sLoc[lane] = 0.f;
         if (wave == 1 && a.loc) {
             // forget gate: chunk-local suffix sums in log2 units, fp64.  Lane s
