@@ -161,15 +161,30 @@ def test_bf16_odd_query_block_count():
     _check(lse, rl, "bf16", "bf16 BH=8 L=700 lse")
 
 
-def test_bf16_odd_query_block_count_paired():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_odd_query_block_count_paired(d):
     """N = 11 chunks and B*H = 96: 288 query blocks, more than the CUs, so
-    the blocks are dealt in pairs of equal weight, with the lone middle block
-    of each head (odd block count) dealt on its own."""
-    inp = generate(4, 24, 700, 64, dtype="bf16", gate=True, seed=47)
-    out, lse = _run_fwd(inp, 0.125)
-    ro, rl = _oracle_full(inp, 0.125)
-    _check(out, ro, "bf16", "bf16 BH=96 L=700 out")
-    _check(lse, rl, "bf16", "bf16 BH=96 L=700 lse")
+    the blocks are dealt in pairs of equal weight (each workgroup's heads in
+    one XCD group), with the lone middle block of each head (odd block count)
+    dealt on its own; L = 700 leaves a ragged last chunk."""
+    inp = generate(4, 24, 700, d, dtype="bf16", gate=True, seed=47)
+    s = 1 / math.sqrt(d)
+    out, lse = _run_fwd(inp, s)
+    ro, rl = _oracle_full(inp, s)
+    _check(out, ro, "bf16", f"bf16 d={d} BH=96 L=700 out")
+    _check(lse, rl, "bf16", f"bf16 d={d} BH=96 L=700 lse")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_paired_heads_not_multiple_of_8(d):
+    """B*H = 90 (not a multiple of 8) and N = 11: 270 query blocks, dealt in
+    pairs round-robin without the XCD grouping of heads."""
+    inp = generate(2, 45, 700, d, dtype="bf16", gate=False, seed=48)
+    s = 1 / math.sqrt(d)
+    out, lse = _run_fwd(inp, s)
+    ro, rl = _oracle_full(inp, s)
+    _check(out, ro, "bf16", f"bf16 d={d} BH=90 L=700 out")
+    _check(lse, rl, "bf16", f"bf16 d={d} BH=90 L=700 lse")
 
 
 def test_bf16_beta_zero_is_causal_attention():
