@@ -16,8 +16,8 @@
 //      (written over K~), and the group's product T_g = P_{start(g)} ...
 //      P_{end(g)}, whose rows are the d identity rows carried through the
 //      group (fp32);
-//   2. path_kcache_suffix_kernel, per head, right to left over the groups:
-//      R_{last} = I, R_g = T_{g+1} R_{g+1};
+//   2. path_kcache_suffix_kernel, per head (and row block of R, d = 128),
+//      right to left over the groups: R_{last} = I, R_g = T_{g+1} R_{g+1};
 //   3. path_kcache_apply_kernel, per (head, group): K_cache_b = Y_b R_g for
 //      the group's chunks, and V_cache = V.
 // The carry (step 1) uses the query transport's layout and MFMA orientation
@@ -174,34 +174,42 @@ __global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs
     }
 }
 
-// Step 2.  One workgroup per head.  Rp_g[rho][c] = sum_m Rp_{g+1}[rho][m]
-// T_{g+1}[c][m] is R_g[c][permk(rho)]: the A operand Rp_{g+1} (two bf16
-// terms, LDS) times the B operand T_{g+1} rows (fp32, split into two bf16
-// terms), three MFMAs per k-step (hi hi, hi lo, lo hi).  Wave w: output
-// columns c in tile w % (D/32), row tiles dt = w / (D/32) + i * 4 / (D/32)
-// (all (D/32)^2 tiles over the four waves).
+// Step 2.  Right to left over the groups, per head.  Rp_g[rho][c] = sum_m
+// Rp_{g+1}[rho][m] T_{g+1}[c][m] is R_g[c][permk(rho)]: the A operand
+// Rp_{g+1} (two bf16 terms, LDS) times the B operand T_{g+1} rows (fp32,
+// split into two bf16 terms), three MFMAs per k-step (hi hi, hi lo, lo hi).
+// A row block of Rp_g needs only the same rows of Rp_{g+1}, so the (D/32)^2
+// output tiles are split into row blocks over RB workgroups per head, one
+// tile per wave: workgroup rb holds rows RPB rb .. +RPB-1, wave w the tile
+// i = 4 rb + w (row tile i / (D/32), column tile i % (D/32)).
+// workgroups per head of the suffix kernel: one 32 x 32 output tile per wave
+constexpr int suffix_blocks(int D) { return (D / 32) * (D / 32) / 4; }
+
 template <int D>
 __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArgs a) {
-    constexpr int PR = D + 8, CT = D / 32, DTW = CT * CT / 4, STEP = 4 / CT, KSD = D / 16;
-    __shared__ __attribute__((aligned(16))) bf16 sRh[D * PR];
-    __shared__ __attribute__((aligned(16))) bf16 sRl[D * PR];
+    constexpr int PR = D + 8, CT = D / 32, KSD = D / 16;
+    constexpr int RB = suffix_blocks(D);  // workgroups per head
+    constexpr int RPB = D / RB;           // Rp rows per workgroup
+    __shared__ __attribute__((aligned(16))) bf16 sRh[RPB * PR];
+    __shared__ __attribute__((aligned(16))) bf16 sRl[RPB * PR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int head = blockIdx.x, NG = a.NG;
-    const int ct = wave % CT, dt0 = wave / CT;
+    const int head = blockIdx.x / RB, rb = blockIdx.x % RB, NG = a.NG;
+    const int tile = 4 * rb + wave, dt = tile / CT, ct = tile % CT;
+    const int r0 = RPB * rb;
     const int c = 32 * ct + l32;
     bf16* rg = static_cast<bf16*>(a.rg) + (size_t)head * NG * 2 * D * D;   // [g][hi, lo][rho][c]
 
-    // R_{NG-1} = I: Rp[rho][c] = (c == permk(rho))
-    for (int u = tid; u < D * D; u += 256) {
-        const int rho = u / D, cc = u % D;
+    // R_{NG-1} = I: Rp[rho][c] = (c == permk(rho)), this workgroup's rows
+    for (int u = tid; u < RPB * D; u += 256) {
+        const int rho = r0 + u / D, cc = u % D;
         const bf16 e = static_cast<bf16>(cc == permk(rho) ? 1.f : 0.f);
-        sRh[rho * PR + cc] = e;
-        sRl[rho * PR + cc] = static_cast<bf16>(0.f);
+        sRh[(rho - r0) * PR + cc] = e;
+        sRl[(rho - r0) * PR + cc] = static_cast<bf16>(0.f);
         bf16* out = rg + (size_t)(NG - 1) * 2 * D * D;
-        out[u] = e;
-        out[D * D + u] = static_cast<bf16>(0.f);
+        out[rho * D + cc] = e;
+        out[D * D + rho * D + cc] = static_cast<bf16>(0.f);
     }
     // B operand: row c of T_{g+1}, k = m = 16 ks + 8 hh .. +7 (fp32), loaded
     // one step ahead
@@ -214,6 +222,7 @@ __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArg
             for (int q = 0; q < 2; ++q) tv[ks][q] = *reinterpret_cast<const f32x4*>(trow + 16 * ks + 8 * hh + 4 * q);
     };
     if (NG >= 2) load_t(NG - 1);
+    const int rl = 32 * dt + l32 - r0;    // the lane's A row in the LDS block
     for (int g = NG - 2; g >= 0; --g) {
         __syncthreads();
         bf16x8 bh[KSD], bl[KSD];
@@ -226,38 +235,30 @@ __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArg
                 bl[ks][t] = static_cast<bf16>(x - static_cast<float>(bh[ks][t]));
             }
         if (g >= 1) load_t(g);
-        f32x16 acc[DTW];
+        f32x16 acc;
 #pragma unroll
-        for (int i = 0; i < DTW; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-#pragma unroll
-            for (int i = 0; i < DTW; ++i) {
-                const int rho = 32 * (dt0 + STEP * i) + l32;
-                const bf16x8 ah = ld8k(sRh + rho * PR + 16 * ks + 8 * hh);
-                const bf16x8 al = ld8k(sRl + rho * PR + 16 * ks + 8 * hh);
-                acc[i] = mfma32k(ah, bh[ks], acc[i]);
-                acc[i] = mfma32k(ah, bl[ks], acc[i]);
-                acc[i] = mfma32k(al, bh[ks], acc[i]);
-            }
+            const bf16x8 ah = ld8k(sRh + rl * PR + 16 * ks + 8 * hh);
+            const bf16x8 al = ld8k(sRl + rl * PR + 16 * ks + 8 * hh);
+            acc = mfma32k(ah, bh[ks], acc);
+            acc = mfma32k(ah, bl[ks], acc);
+            acc = mfma32k(al, bh[ks], acc);
         }
         __syncthreads();    // every wave has read Rp_{g+1}
 #pragma unroll
-        for (int i = 0; i < DTW; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rho = 32 * (dt0 + STEP * i) + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const float x = acc[i][v];
-                const bf16 h = static_cast<bf16>(x);
-                sRh[rho * PR + c] = h;
-                sRl[rho * PR + c] = static_cast<bf16>(x - static_cast<float>(h));
-            }
+        for (int v = 0; v < 16; ++v) {
+            const int rho = 32 * dt + 8 * (v >> 2) + 4 * hh + (v & 3);
+            const float x = acc[v];
+            const bf16 h = static_cast<bf16>(x);
+            sRh[(rho - r0) * PR + c] = h;
+            sRl[(rho - r0) * PR + c] = static_cast<bf16>(x - static_cast<float>(h));
+        }
         __syncthreads();
-        // Rp_g to global memory in 16-byte units
-        bf16* out = rg + (size_t)g * 2 * D * D;
-        for (int u = tid; u < D * D / 8; u += 256) {
+        // this workgroup's rows of Rp_g to global memory in 16-byte units
+        bf16* out = rg + (size_t)g * 2 * D * D + (size_t)r0 * D;
+        for (int u = tid; u < RPB * D / 8; u += 256) {
             const int rho = u / (D / 8), c8 = (u % (D / 8)) * 8;
             *reinterpret_cast<bf16x8*>(out + (size_t)u * 8) = ld8k(sRh + rho * PR + c8);
             *reinterpret_cast<bf16x8*>(out + D * D + (size_t)u * 8) = ld8k(sRl + rho * PR + c8);
@@ -341,12 +342,12 @@ hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s) {
     if (D == 64) {
         constexpr int NP = (kKcacheGroup + 1 + 3) / 4;
         hipLaunchKernelGGL(path_kcache_group_kernel<64>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
-        hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH * suffix_blocks(64)), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<64>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else if (D == 128) {
         constexpr int NP = (kKcacheGroup + 2 + 3) / 4;
         hipLaunchKernelGGL(path_kcache_group_kernel<128>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
-        hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH * suffix_blocks(128)), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<128>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;

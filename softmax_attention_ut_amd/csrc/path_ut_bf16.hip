@@ -99,7 +99,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // the probabilities of the chunk's own keys, with their maximum and sum.  U
 // and Y then stay on chip (they serve no other step).
 template <int D, bool WITH_Z, bool DIAG>
-__global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : (DIAG ? 2 : 1)) void path_ut_bf16_kernel(const UtArgs a) {
+__global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : ((DIAG || WITH_Z) ? 2 : 1)) void path_ut_bf16_kernel(const UtArgs a) {
     static_assert(!DIAG || !WITH_Z, "the own-chunk step is a forward stage");
     constexpr int C = 64;
     constexpr int PW = D + 8;     // pitch of [token][d] tiles
@@ -123,8 +123,19 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : (DIAG ? 2 : 1)) voi
     bf16* const sV = reinterpret_cast<bf16*>(sG);
     bf16* const sTh = reinterpret_cast<bf16*>(sG);
     bf16* const sTl = reinterpret_cast<bf16*>(sG) + C * PT;
-    __shared__ __attribute__((aligned(16))) bf16 sZh[WITH_Z ? C * PT : 8];  // T^{-T} rows, m slots
-    __shared__ __attribute__((aligned(16))) bf16 sZl[WITH_Z ? C * PT : 8];
+    // T^{-T} rows, m slots, hi and lo.  d = 128 (ZK): formed after phase 3
+    // over the K rows, which are no longer read then, as unpadded 64-wide rows
+    // with their 16-byte units XOR-swizzled (so LDS fits two workgroups per CU)
+    constexpr bool ZK = WITH_Z && D == 128;
+    static_assert(!ZK || 2 * C * C <= C * PW, "the T^{-T} tiles fit over the K rows");
+    __shared__ __attribute__((aligned(16))) bf16 sZh_[(WITH_Z && !ZK) ? C * PT : 8];
+    __shared__ __attribute__((aligned(16))) bf16 sZl_[(WITH_Z && !ZK) ? C * PT : 8];
+    bf16* const sZh = ZK ? sK : sZh_;
+    bf16* const sZl = ZK ? sK + C * C : sZl_;
+    // 16-byte unit u of T^{-T} row r
+    auto zunit = [&](bf16* t, int r, int u) -> bf16* {
+        return ZK ? t + r * C + ((u ^ ((r ^ (r >> 3)) & 7)) << 3) : t + r * PT + 8 * u;
+    };
     __shared__ float sB[C];
     __shared__ __attribute__((aligned(16))) float sLoc[DIAG ? C : 4];   // -local log2 gate prefix (0 without gate)
 
@@ -363,11 +374,33 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : (DIAG ? 2 : 1)) voi
                 hi[e] = static_cast<bf16>(zs[it][e]);
                 lo[e] = static_cast<bf16>(zs[it][e] - static_cast<float>(hi[e]));
             }
-            *reinterpret_cast<bf16x8*>(sZh + row * PT + s0) = hi;
-            *reinterpret_cast<bf16x8*>(sZl + row * PT + s0) = lo;
+            if (!ZK) {
+                *reinterpret_cast<bf16x8*>(zunit(sZh, row, s0 >> 3)) = hi;
+                *reinterpret_cast<bf16x8*>(zunit(sZl, row, s0 >> 3)) = lo;
+            }
         }
     }
     __syncthreads();
+    // Z[n][e] = sum_m T^{-1}[m][n] W[m][e] for the columns e of W^T row tile et
+    auto zpart = [&](int et) {
+        const int e = 32 * et + l32;         // W^T row rho: d = permk(rho)
+        const bf16* bw = sWt + e * PT + 8 * hh;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x16 zacc;
+            zero(zacc);
+#pragma unroll
+            for (int ks = 2 * nt; ks < 4; ++ks) {   // T^{-T}[n][m] = 0 for m < n
+                const bf16x8 w8 = ld8(bw + 16 * ks);
+                zacc = mfma(ld8(zunit(sZh, 32 * nt + l32, 2 * ks + hh)), w8, zacc);
+                zacc = mfma(ld8(zunit(sZl, 32 * nt + l32, 2 * ks + hh)), w8, zacc);
+            }
+            bf16* zrow = static_cast<bf16*>(a.zt) + (chunkbase * D + e) * C;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                *reinterpret_cast<bf16x8*>(zrow + 32 * nt + 16 * s2 + 8 * hh) = cvt8(zacc, s2, -1.f);
+        }
+    };
 
     // ---- phase 3 ----
     // DIAG: the Y^T rows (waves 0, 1) and -U^T rows (waves 2, 3: d / 64 row
@@ -510,27 +543,27 @@ __global__ __launch_bounds__(256, (D == 64 && !WITH_Z) ? 3 : (DIAG ? 2 : 1)) voi
                         *reinterpret_cast<bf16x8*>(mrow + 32 * ot + 16 * s2 + 8 * hh) = cvt8(macc, s2, -1.f);
                 }
             }
-            if (WITH_Z) {
-                // Z[n][e] = sum_m T^{-1}[m][n] W[m][e]
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x16 zacc;
-                    zero(zacc);
-                    const bf16* zh = sZh + (32 * nt + l32) * PT + 8 * hh;
-                    const bf16* zl = sZl + (32 * nt + l32) * PT + 8 * hh;
-#pragma unroll
-                    for (int ks = 2 * nt; ks < 4; ++ks) {   // T^{-T}[n][m] = 0 for m < n
-                        const bf16x8 w8 = ld8(bw + 16 * ks);
-                        zacc = mfma(ld8(zh + 16 * ks), w8, zacc);
-                        zacc = mfma(ld8(zl + 16 * ks), w8, zacc);
-                    }
-                    bf16* zrow = static_cast<bf16*>(a.zt) + (chunkbase * D + e) * C;
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-                        *reinterpret_cast<bf16x8*>(zrow + 32 * nt + 16 * s2 + 8 * hh) = cvt8(zacc, s2, -1.f);
-                }
-            }
+            if (WITH_Z && !ZK) zpart(et);
         }
+    }
+    if constexpr (ZK) {
+        // the T^{-T} tiles over the K rows (read by phase 3 until here), then
+        // Z on all four waves, one W^T row tile each
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int u = tid + 256 * it, row = u >> 3, s0 = (u & 7) * 8;
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                hi[e] = static_cast<bf16>(zs[it][e]);
+                lo[e] = static_cast<bf16>(zs[it][e] - static_cast<float>(hi[e]));
+            }
+            *reinterpret_cast<bf16x8*>(zunit(sZh, row, s0 >> 3)) = hi;
+            *reinterpret_cast<bf16x8*>(zunit(sZl, row, s0 >> 3)) = lo;
+        }
+        __syncthreads();
+        zpart(wave);
     }
     if constexpr (DIAG) {
         // ---- phase 4: the chunk's own-chunk step for its 64 queries ----
