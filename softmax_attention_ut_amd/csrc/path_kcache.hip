@@ -19,7 +19,8 @@
 //   2. path_kcache_suffix_kernel, per head (and row block of R, d = 128),
 //      right to left over the groups: R_{last} = I, R_g = T_{g+1} R_{g+1};
 //   3. path_kcache_apply_kernel, per (head, group): K_cache_b = Y_b R_g for
-//      the group's chunks, and V_cache = V.
+//      the group's chunks.
+// V_cache = V is copied by extra workgroups of the suffix launch.
 // The carry (step 1) uses the query transport's layout and MFMA orientation
 // (the key rides in fp32 accumulators, K^T -= Z^T X^T with X^T = W K^T; -Z^T
 // comes from path_ut with its token axis in k-slot order and its d rows
@@ -184,6 +185,42 @@ __global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs
 // i = 4 rb + w (row tile i / (D/32), column tile i % (D/32)).
 // workgroups per head of the suffix kernel: one 32 x 32 output tile per wave
 constexpr int suffix_blocks(int D) { return (D / 32) * (D / 32) / 4; }
+// further workgroups of the suffix launch copy the values into the cache
+// while the suffix chains run (those leave most of the chip idle)
+constexpr int kValueCopyBlocks = 512;
+
+// V_cache = V for the L prefill slots of every head: workgroup cb of nb, a
+// grid-stride loop over rows with D/8 lanes per row (16 bytes each), NF rows
+// in flight per lane (the launch's register allocation, sized for the suffix
+// products, leaves about one such workgroup per CU: it needs many loads in
+// flight to keep up with HBM).
+template <int D>
+__device__ __forceinline__ void copy_values(const KcacheArgs& a, int cb, int nb) {
+    constexpr int UPR = D / 8;                       // 16-byte units per row
+    constexpr int RPP = 256 / UPR;                   // rows per workgroup pass
+    const int tid = threadIdx.x, unit = tid % UPR;
+    const int rows = a.BH * a.L;                     // < 2^31 (checked by the caller's shape limits)
+    const int stride = nb * RPP;
+    constexpr int NF = 16;
+    for (int r0 = cb * RPP + tid / UPR; r0 < rows; r0 += NF * stride) {
+        bf16x8 v[NF];
+        long long dst[NF];
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            const int r = r0 + i * stride;
+            dst[i] = -1;
+            if (r < rows) {
+                const int head = r / a.L, j = r - head * a.L;
+                v[i] = ld8k(static_cast<const bf16*>(a.v) + (size_t)r * D + 8 * unit);
+                dst[i] = cache_row(a.map, head, j);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+            if (dst[i] >= 0)
+                *reinterpret_cast<bf16x8*>(static_cast<bf16*>(a.v_cache) + dst[i] * D + 8 * unit) = v[i];
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArgs a) {
@@ -193,6 +230,10 @@ __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArg
     __shared__ __attribute__((aligned(16))) bf16 sRh[RPB * PR];
     __shared__ __attribute__((aligned(16))) bf16 sRl[RPB * PR];
 
+    if (static_cast<int>(blockIdx.x) >= a.BH * RB) {  // the value-copy workgroups
+        copy_values<D>(a, blockIdx.x - a.BH * RB, gridDim.x - a.BH * RB);
+        return;
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int head = blockIdx.x / RB, rb = blockIdx.x % RB, NG = a.NG;
@@ -268,9 +309,10 @@ __global__ __launch_bounds__(256) void path_kcache_suffix_kernel(const KcacheArg
 
 // Step 3.  One workgroup per (head, group): K_cache^T = Rp_g Y^T for the
 // group's chunks (A: Rp_g, hi and lo, in LDS; B: Y rows, exact bf16), one key
-// tile of 32 per wave pair and d tiles split between the pair; values copied.
+// tile of 32 per wave pair and d tiles split between the pair (the values
+// are copied by the suffix launch).
 template <int D>
-__global__ __launch_bounds__(256) void path_kcache_apply_kernel(const KcacheArgs a) {
+__global__ __launch_bounds__(256, 2) void path_kcache_apply_kernel(const KcacheArgs a) {
     constexpr int C = 64, PR = D + 8, DT = D / 32, KSD = D / 16, DTW = DT / 2;
     __shared__ __attribute__((aligned(16))) bf16 sRh[D * PR];
     __shared__ __attribute__((aligned(16))) bf16 sRl[D * PR];
@@ -288,7 +330,6 @@ __global__ __launch_bounds__(256) void path_kcache_apply_kernel(const KcacheArgs
     }
     __syncthreads();
     const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
-    const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
     const int jloc = (wave & 1) * 32 + l32, dtb = (wave >> 1) * DTW;
     const int cend = min(c1, (L - 1) / C);        // chunks past it are padding
     // Y rows as the B operand (k = c = 16 ks + 8 hh .. +7), one chunk ahead
@@ -329,11 +370,6 @@ __global__ __launch_bounds__(256) void path_kcache_apply_kernel(const KcacheArgs
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
                 *reinterpret_cast<bf16x8*>(kout + 32 * (dtb + i) + 16 * s2 + 8 * hh) = pack8k(acc[i], s2);
-        // values copied unchanged: each wave of the pair a quarter of the row per lane half
-        const bf16* vrow = vin + (size_t)j * D;
-        bf16* vout = static_cast<bf16*>(a.v_cache) + row * D;
-        for (int e = 8 * (2 * (wave >> 1) + hh); e < D; e += 32)
-            *reinterpret_cast<bf16x8*>(vout + e) = ld8k(vrow + e);
     }
 }
 
@@ -342,12 +378,12 @@ hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s) {
     if (D == 64) {
         constexpr int NP = (kKcacheGroup + 1 + 3) / 4;
         hipLaunchKernelGGL(path_kcache_group_kernel<64>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
-        hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH * suffix_blocks(64)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH * suffix_blocks(64) + kValueCopyBlocks), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<64>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else if (D == 128) {
         constexpr int NP = (kKcacheGroup + 2 + 3) / 4;
         hipLaunchKernelGGL(path_kcache_group_kernel<128>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
-        hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH * suffix_blocks(128)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH * suffix_blocks(128) + kValueCopyBlocks), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<128>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else {
         return hipErrorInvalidValue;
