@@ -821,7 +821,7 @@ __device__ __forceinline__ void pp128_mphase(WaveState<128, GATE>& st, f32x16 s[
 // the SIMD keeps the matrix pipe busy.
 template <bool GATE>
 __device__ __forceinline__ void pp128_vphase(WaveState<128, GATE>& st, const f32x16 s[2], bf16x8 pB[4],
-                                             const bf16* smt, int l32) {
+                                             const bf16* smt) {
     unsigned lb = st.lb;
     asm volatile("" : "+v"(lb));
     auto load = [&](int i) -> bf16x8 { return tile_op(smt, lb, i >> 2, 8192 * (i & 3)); };
@@ -856,7 +856,7 @@ __device__ __forceinline__ void pp128_vphase(WaveState<128, GATE>& st, const f32
 
 template <bool GATE>
 __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d128pp_kernel(const FwdArgs a) {
-    constexpr int C = 64, D = 128, NT = 512;
+    constexpr int C = 64, D = 128;
     constexpr int KT = C * D;          // K~ and V^T tile elements
     constexpr int MT = D * D;          // -M^T tile elements
     __shared__ __attribute__((aligned(1024))) Tiles128<GATE> km0;
@@ -979,7 +979,7 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d128pp_kernel(const FwdA
             wait_copies(n);
             phase_barrier();
             n = leader ? issue_b(k) : issue_a(k - 1);
-            if (go) pp128_vphase<GATE>(st, s, pB, ck.m, l32);
+            if (go) pp128_vphase<GATE>(st, s, pB, ck.m);
             wait_copies(n);
             phase_barrier();
         };
