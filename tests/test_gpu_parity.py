@@ -125,13 +125,17 @@ def test_bf16_L1k_config_full():
 
 @pytest.mark.parametrize("L", [1, 5, 64, 65, 127, 129, 777])
 @pytest.mark.parametrize("gate", [False, True])
-def test_bf16_ragged_lengths(L, gate):
-    inp = generate(1, 3, L, 64, dtype="bf16", gate=gate, seed=30 + L)
-    s = 0.125
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_ragged_lengths(L, gate, d):
+    """One chunk of one token up to thirteen chunks with a ragged last one:
+    the scan's single-chunk start (no left chunk), a last chunk of one key,
+    and blocks of fewer than four query chunks."""
+    inp = generate(1, 3, L, d, dtype="bf16", gate=gate, seed=30 + L)
+    s = 1 / math.sqrt(d)
     out, lse = _run_fwd(inp, s)
     ro, rl = _oracle_full(inp, s)
-    _check(out, ro, "bf16", f"bf16 L={L} gate={gate} out")
-    _check(lse, rl, "bf16", f"bf16 L={L} gate={gate} lse")
+    _check(out, ro, "bf16", f"bf16 d={d} L={L} gate={gate} out")
+    _check(lse, rl, "bf16", f"bf16 d={d} L={L} gate={gate} lse")
 
 
 @pytest.mark.parametrize("gate", [False, True])
@@ -196,15 +200,17 @@ def test_bf16_beta_zero_is_causal_attention():
     _check(out, ref.double().numpy(), "bf16", "beta=0 vs causal SDPA (fp32 CPU)")
 
 
-def test_bf16_first_transition_never_enters():
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_first_transition_never_enters(d):
     """H_0, beta_0 and f_0 do not enter any logit: perturbing them leaves the
     GPU result bit-identical."""
-    inp = generate(1, 2, 200, 64, dtype="bf16", gate=True, seed=43)
-    a, la = _run_fwd(inp, 0.125)
+    inp = generate(1, 2, 200, d, dtype="bf16", gate=True, seed=43)
+    s = 1 / math.sqrt(d)
+    a, la = _run_fwd(inp, s)
     inp.w[:, :, 0] = inp.w[:, :, 0].flip(-1)
     inp.beta[:, :, 0] = 1.9
     inp.log_f[:, :, 0] = -30.0
-    b, lb = _run_fwd(inp, 0.125)
+    b, lb = _run_fwd(inp, s)
     np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(la, lb)
 
