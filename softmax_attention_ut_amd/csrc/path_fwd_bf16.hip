@@ -295,7 +295,10 @@ __device__ __forceinline__ void scan_store(const FwdArgs& a, const WaveState<D, 
 // the other wave's vector instructions issue.
 //
 // Staging: a key chunk's K~, -M^T, V, gate rows and sums sit in stage set
-// k % 2 and are copied two phases before their first use.
+// k % 2 and are copied two phases before their first use.  A workgroup's
+// next query block is known in advance: its starting state (each wave's 32
+// query rows) and its first key step's tiles are copied into LDS during the
+// current block's last phases, so a block starts without a trip to memory.
 // ---------------------------------------------------------------------------
 
 // Matrix phase of one wave: O^T += V^T P^T for the pending probabilities pB
@@ -467,17 +470,76 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         bf16 gb[GATE ? C * 16 : 8];
         float loc[C + 4];
     };
-    __shared__ __attribute__((aligned(1024))) ChunkTiles km0;
-    __shared__ __attribute__((aligned(1024))) ChunkTiles km1;
+    // The starting state of a query block, one part per wave (its 32 query
+    // rows): the carried query and the pending probabilities (128-byte rows,
+    // swizzled like the K~ tile), (m, l) per row, and with the gate each row's
+    // loc and the query chunk's sum.  It is copied during the previous block.
+    struct BlockState {
+        bf16 q[8][32 * D];
+        bf16 p[8][32 * C];
+        float ml[8][64];
+        float loc[8][64];
+    };
+    // one LDS object, the stage sets first: the loop's reads of them then
+    // take their offsets from the instruction's 16-bit offset field
+    struct Shared {
+        ChunkTiles km0, km1;
+        BlockState bs;
+    };
+    __shared__ __attribute__((aligned(1024))) Shared sh;
 
     const int wave_u = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const bool leader = wave_u >= 4;
     const int nqb = (a.N + 3) / 4;
 
-    // One query block (head, qb): query chunks 4qb .. 4qb+3 of one head.  The
-    // arguments and the lane id come in through opaque copies, so that
-    // nothing derived from them is kept live from one block to the next.
-    auto item = [&](const int head, const int qb, const FwdArgs& a, const int lane_in) {
+    // Copies that a query block (head, qb) needs before its first key step,
+    // each wave issuing its share: its rows' starting state, the tiles of
+    // chunk ktop-1 (set (ktop-1) % 2) and, when ktop is odd and chunk ktop
+    // full, V(ktop) (set 1).  Issued during the previous block, after the
+    // last reads of these buffers (V(ktop) of an even ktop would overwrite
+    // V(0), which that block still reads, so the block copies it itself).
+    auto prefetch = [=](const FwdArgs& a, const int lane, const int head, const int qb) {
+        const int L = a.L, N = a.N, Lp = N * C;
+        const int qc = 4 * qb + (leader ? 7 - wave_u : wave_u);
+        const bool active = qc < N;
+        const size_t row0 = (size_t)head * Lp + (active ? qc * C + (wave_u >> 2) * 32 : 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const unsigned off = tile64_lane_offset(j, lane);
+            dma_lds16(static_cast<const bf16*>(a.qt) + row0 * D, off, sh.bs.q[wave_u] + 512 * j);
+            dma_lds16(static_cast<const bf16*>(a.pd) + row0 * C, off, sh.bs.p[wave_u] + 512 * j);
+        }
+        dma_lds4(a.ml + 2 * row0, lane * 4, sh.bs.ml[wave_u]);
+        if (GATE) {
+            if (lane < 32) dma_lds4(a.loc + row0, lane * 4, sh.bs.loc[wave_u]);
+            if (lane == 0) dma_lds4(a.csum + (size_t)head * N + (active ? qc : 0), 0, sh.bs.loc[wave_u] + 32);
+        }
+        const int ktop = min(4 * qb + 3, N - 1);
+        if (ktop >= 1) {
+            ChunkTiles& sg = (ktop & 1) ? sh.km0 : sh.km1;
+            const int kc = ktop - 1;
+            const unsigned loff = tile64_lane_offset(wave_u, lane);
+            dma_lds16(static_cast<const bf16*>(a.kt) + ((size_t)head * Lp + kc * C) * D, loff, sg.k + wave_u * 512);
+            dma_lds16(static_cast<const bf16*>(a.mt) + ((size_t)head * N + kc) * D * D, loff, sg.m + wave_u * 512);
+            if (GATE && wave_u < 2)
+                dma_lds16(static_cast<const bf16*>(a.gb) + ((size_t)head * Lp + kc * C) * 16 + wave_u * 512,
+                          lane * 16, sg.gb + wave_u * 512);
+            if (GATE && wave_u == 2) {
+                dma_lds4(a.loc + (size_t)head * Lp + kc * C, lane * 4, sg.loc);
+                if (lane == 0) dma_lds4(a.csum + (size_t)head * N + kc, 0, sg.loc + C);
+            }
+        }
+        if ((ktop & 1) && (ktop + 1) * C <= L)
+            dma_lds16(static_cast<const bf16*>(a.v) + ((size_t)head * L + (size_t)ktop * C) * D,
+                      vtile_lane_offset(wave_u, lane), sh.km1.v + wave_u * 512);
+    };
+
+    // One query block (head, qb): query chunks 4qb .. 4qb+3 of one head; the
+    // block (nhead, nqb_) follows when has_next.  The arguments and the lane
+    // id come in through opaque copies, so that nothing derived from them is
+    // kept live from one block to the next.
+    auto item = [&](const int head, const int qb, const int nhead, const int nqb_, const bool has_next,
+                    const FwdArgs& a, const int lane_in) {
     const int lane = lane_in & 63;
     const int tid = wave_u * 64 + lane;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -495,32 +557,6 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     u.head = head; u.qb = qb; u.qc = qc; u.iloc = iloc; u.active = active;
     u.qi = qc * C + iloc;
     u.qvalid = active && u.qi < L;
-    {
-        // the state after the query's own chunk, from the prepare stage: the
-        // query carried to its chunk start (scaled by scale*log2(e)), the
-        // pending probabilities of its own keys, their maximum and sum
-        const size_t row = (size_t)head * Lp + (active ? u.qi : 0);
-        const bf16* qrow = static_cast<const bf16*>(a.qt) + row * D;
-        const bf16* prow = static_cast<const bf16*>(a.pd) + row * C;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
-            st.qB[ks] = lds8(qrow + 16 * ks + 8 * hh);
-            pB[ks] = lds8(prow + 16 * ks + 8 * hh);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(st.qB[ks][t]);
-        }
-        const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ml + 2 * row);
-        st.m_run = ml[0];
-        st.l_run = hh == 0 ? ml[1] : 0.f;   // the two lane halves' sums are added at the end
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
-        st.loc_i = GATE ? a.loc[row] : 0.f;
-        st.dab = GATE ? static_cast<double>(a.csum[(size_t)head * N + (active ? qc : 0)]) : 0.0;
-    }
-    vtr_offsets(st.voff, lane);
 
     const bf16* kt = static_cast<const bf16*>(a.kt) + (size_t)head * Lp * D;
     const bf16* vin = static_cast<const bf16*>(a.v) + (size_t)head * L * D;
@@ -529,66 +565,69 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const float* csg = GATE ? a.csum + (size_t)head * N : nullptr;
     const bf16* gbg = GATE ? static_cast<const bf16*>(a.gb) + (size_t)head * Lp * 16 : nullptr;
 
-    const Stage<D> set0{km0.k, km0.v, km0.m, km0.loc, km0.gb};
-    const Stage<D> set1{km1.k, km1.v, km1.m, km1.loc, km1.gb};
+    const Stage<D> set0{sh.km0.k, sh.km0.v, sh.km0.m, sh.km0.loc, sh.km0.gb};
+    const Stage<D> set1{sh.km1.k, sh.km1.v, sh.km1.m, sh.km1.loc, sh.km1.gb};
 
-    // every [64][64] tile: wave w copies its 1 KB block w (rows 8w .. 8w+7)
-    auto tile = [&](bf16* lds, const bf16* g) {
-        __builtin_amdgcn_global_load_lds((gbl_void*)(reinterpret_cast<const char*>(g) + loff),
-                                         (lds_void*)(reinterpret_cast<char*>(lds) + wave_u * 1024), 16, 0, 0);
-    };
-    auto issue_km = [&](const Stage<D>& sg, int kc) {   // K~, -M^T, bias rows, gate terms
-        tile(sg.k, kt + (size_t)kc * TILE);
-        tile(sg.mt, mtg + (size_t)kc * TILE);
-        if (GATE && wave_u < 2)
-            __builtin_amdgcn_global_load_lds((gbl_void*)(gbg + (size_t)kc * C * 16 + wave_u * 512 + lane * 8),
-                                             (lds_void*)(sg.gb + wave_u * 512), 16, 0, 0);
-        if (GATE && wave_u == 2) {
-            __builtin_amdgcn_global_load_lds((gbl_void*)(locg + kc * C + lane), (lds_void*)sg.loc, 4, 0, 0);
-            if (lane == 0)
-                __builtin_amdgcn_global_load_lds((gbl_void*)(csg + kc), (lds_void*)(sg.loc + C), 4, 0, 0);
-        }
-    };
-    auto issue_v = [&](const Stage<D>& sg, int kc) {
-        if ((kc + 1) * C <= L)
+    // ---- the block's first copies (the previous block, or the workgroup's
+    // start, issued them); V(ktop) is copied here when it was not.  ktop =
+    // the block's top chunk; chunk k's K~/-M^T/gate terms sit in set k % 2,
+    // its V tile in that set's V tile. ----
+    const int ktop = min(4 * qb + 3, N - 1);
+    wait_vmem();
+    if (!((ktop & 1) && (ktop + 1) * C <= L)) {
+        bf16* const vtop = (ktop & 1) ? sh.km1.v : sh.km0.v;
+        if ((ktop + 1) * C <= L) {
             __builtin_amdgcn_global_load_lds(
-                (gbl_void*)(reinterpret_cast<const char*>(vin + (size_t)kc * TILE) + vloff),
-                (lds_void*)(reinterpret_cast<char*>(sg.v) + wave_u * 1024), 16, 0, 0);
-        else
-            copy_guarded<C, D, NT, true>(sg.v, vin + (size_t)kc * TILE, L - kc * C, tid);   // ragged: zero rows
-    };
+                (gbl_void*)(reinterpret_cast<const char*>(vin + (size_t)ktop * TILE) + vloff),
+                (lds_void*)(reinterpret_cast<char*>(vtop) + wave_u * 1024), 16, 0, 0);
+            wait_vmem();
+        } else {
+            copy_guarded<C, D, NT, true>(vtop, vin + (size_t)ktop * TILE, L - ktop * C, tid);   // ragged: zero rows
+        }
+    }
+    __syncthreads();
+    {
+        // the state after the query's own chunk, from the prepare stage: the
+        // query carried to its chunk start (scaled by scale*log2(e)), the
+        // pending probabilities of its own keys, their maximum and sum
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            st.offD[ks] = ((2 * ks + hh) ^ swz_g<D>(l32)) << 3;
+            st.qB[ks] = lds8(sh.bs.q[wave_u] + l32 * D + st.offD[ks]);
+            pB[ks] = lds8(sh.bs.p[wave_u] + l32 * C + st.offD[ks]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) st.qacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(st.qB[ks][t]);
+        }
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(sh.bs.ml[wave_u] + 2 * l32);
+        st.m_run = ml[0];
+        st.l_run = hh == 0 ? ml[1] : 0.f;   // the two lane halves' sums are added at the end
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) st.oacc[dt][v] = 0.f;
+        st.loc_i = GATE ? sh.bs.loc[wave_u][l32] : 0.f;
+        st.dab = GATE ? static_cast<double>(sh.bs.loc[wave_u][32]) : 0.0;
+    }
+    vtr_offsets(st.voff, lane);
 
-    // ---- key chunks ktop-1 .. 0 in phases; ktop = the block's top chunk.
-    // Chunk k's K~/-M^T/gate terms sit in set k % 2, its V tile in that set's
-    // V tile.  A wave works on chunk k only when k < qc (its own chunk was
-    // done by the prepare stage, whose probabilities are pending against
-    // V(qc)); the other waves of the block keep the copies and barriers.
-    // Every wave runs
+    // ---- key chunks ktop-1 .. 0 in phases.  A wave works on chunk k only
+    // when k < qc (its own chunk was done by the prepare stage, whose
+    // probabilities are pending against V(qc)); the other waves of the block
+    // keep the copies and barriers.  Every wave runs
     //     for k = ktop-1 .. 0:  M(k); barrier; V(k); barrier        then PV(0)
     // where M(k) = PV(k+1), logits and carry of k, and V(k) = the
     // probabilities of k.  The followers (waves 0..3) enter one barrier late,
     // so between two barriers one wave of each SIMD is in a matrix phase and
     // the other in a vector phase.  Copies: at the start of its M(k) a leader
     // issues its blocks of chunk k-1 (K~/-M^T) and V(k); at the start of its
-    // V(k) a follower issues its blocks of chunk k-2 and V(k-1) -- the same
+    // V(k) a follower issues its blocks of chunk k-2 and V(k-1), and before
+    // the first barrier those of chunk ktop-2 and V(ktop-1) -- the same
     // moment, one phase after the buffers' last reads.  Leaders wait for their
     // copies at the end of V(k), followers at the end of M(k): two phases
     // later, and before the barrier that opens the first phase reading them.
-    // The prologue stages V(ktop), and chunk ktop-1 with V(ktop-1), whole. ----
-    const int ktop = min(4 * qb + 3, N - 1);
-    if (ktop & 1) {
-        issue_v(set1, ktop);
-        issue_km(set0, ktop - 1);
-        issue_v(set0, ktop - 1);
-    } else {
-        issue_v(set0, ktop);
-        if (ktop >= 1) {
-            issue_km(set1, ktop - 1);
-            issue_v(set1, ktop - 1);
-        }
-    }
-    wait_vmem();
-    __syncthreads();
+    // The next block's copies are issued once this block's last M(0) is done
+    // (by followers at the start of V(0), by leaders after it); then only
+    // V(0) is still read. ----
     f32x16 s[2];
     bf16x8 opm[8];
     if (ktop > 0) {
@@ -610,14 +649,15 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
         };
         if (!leader) {
             if (ktop >= 2) kissue((ktop & 1) ? set1 : set0, ktop - 2);
+            dma_lds16(vin + (size_t)(ktop - 1) * TILE, vloff, ((ktop & 1) ? sh.km0.v : sh.km1.v) + wave_u * 512);
             phase_barrier();
         }
-        auto iter = [&](int k, const Stage<D>& ck, const Stage<D>& cn) {
+        auto iter = [&](int k, const Stage<D>& ck, const Stage<D>& cn, auto last) {
             // ck: chunk k and V(k); cn: chunk k +- 1 and V(k +- 1).  Chunks
             // below ktop are full, so V is copied without a guard.
             if (leader) {
                 if (k >= 1) kissue(cn, k - 1);
-                if (k < ktop - 1) dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
+                dma_lds16(vin + (size_t)k * TILE, vloff, ck.v + wave_u * 512);
             }
             const bool go = active && k < qc;
             if (go) pp_mphase<GATE, true>(st, s, pB, opm, ck, cn.v, l32, hh);
@@ -626,20 +666,34 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
             if (!leader) {
                 if (k >= 2) kissue(ck, k - 2);
                 if (k >= 1) dma_lds16(vin + (size_t)(k - 1) * TILE, vloff, cn.v + wave_u * 512);
+                if (decltype(last)::value && has_next) prefetch(a, lane, nhead, nqb_);
             }
             if (go) pp_vphase<GATE>(st, s, pB, opm);
             if (leader) wait_vmem();
             phase_barrier();
         };
+        // the last step (k = 0) is its own copy: only there do followers
+        // issue the next block's copies
+        const std::false_type mid;
+        const std::true_type last;
         int k = ktop - 1;
-        if ((k & 1) == 0) {           // k even: one step to reach the odd/even pairs
-            iter(k, set0, set1);
-            --k;
+        if (k == 0) {
+            iter(0, set0, set1, last);
+        } else {
+            if ((k & 1) == 0) {       // k even: one step to reach the odd/even pairs
+                iter(k, set0, set1, mid);
+                --k;
+            }
+            for (; k >= 3; k -= 2) {  // k odd, then k - 1 even
+                iter(k, set1, set0, mid);
+                iter(k - 1, set0, set1, mid);
+            }
+            iter(1, set1, set0, mid);
+            iter(0, set0, set1, last);
         }
-        for (; k >= 0; k -= 2) {     // k odd, then k - 1 even
-            iter(k, set1, set0);
-            iter(k - 1, set0, set1);
-        }
+        if (leader && has_next) prefetch(a, lane, nhead, nqb_);
+    } else if (has_next) {
+        prefetch(a, lane, nhead, nqb_);
     }
     // PV(0) with the pending probabilities (the own chunk's, for qc = 0)
     if (active) pp_mphase<GATE, false>(st, s, pB, opm, set0, set0.v, l32, hh);
@@ -666,26 +720,40 @@ __global__ __launch_bounds__(512, 1) void path_fwd_bf16_d64pp_kernel(const FwdAr
     const int xcd = by_xcd ? blockIdx.x % 8 : 0;
     const int npairs = (by_xcd ? a.BH / 8 : a.BH) * P;
     const bool single = a.single != 0;
-    for (int t = 0;; ++t) {                      // t-th block of this workgroup: pair r + R (t / 2), heavy half first
-        int i, qb;
-        if (single) {                            // block r of this workgroup's heads, heaviest first
-            if (t > 0) break;
-            i = r / nqb;
-            qb = nqb - 1 - r % nqb;
-        } else {
-            const int j = r + R * (t >> 1);
-            if (j >= npairs) break;
-            const int pr = j % P;
-            i = j / P;
-            qb = (t & 1) ? pr : nqb - 1 - pr;
-            if ((t & 1) && qb == nqb - 1 - pr) continue;   // the lone middle block of an odd nqb
+    // the t-th block of this workgroup, t advanced past the lone middle block
+    // of an odd nqb: pair r + R (t / 2), heavy half first
+    auto deal = [&](int& t, int& head, int& qb) -> bool {
+        for (;; ++t) {
+            int i;
+            if (single) {                        // block r of this workgroup's heads, heaviest first
+                if (t > 0) return false;
+                i = r / nqb;
+                qb = nqb - 1 - r % nqb;
+            } else {
+                const int j = r + R * (t >> 1);
+                if (j >= npairs) return false;
+                const int pr = j % P;
+                i = j / P;
+                qb = (t & 1) ? pr : nqb - 1 - pr;
+                if ((t & 1) && qb == nqb - 1 - pr) continue;
+            }
+            head = by_xcd ? xcd + 8 * i : i;
+            return true;
         }
+    };
+    int t = 0, head = 0, qb = 0;
+    bool have = deal(t, head, qb);
+    if (have) prefetch(a, static_cast<int>(threadIdx.x & 63), head, qb);
+    while (have) {
+        int t2 = t + 1, nhead = 0, nqb_ = 0;
+        const bool has_next = deal(t2, nhead, nqb_);
         __syncthreads();                         // the previous block's tiles are no longer read
         typedef const __attribute__((address_space(4))) FwdArgs* ArgPtr;
         ArgPtr ap = (ArgPtr)__builtin_amdgcn_kernarg_segment_ptr();
         int ln = static_cast<int>(threadIdx.x & 63);
         asm volatile("" : "+s"(ap), "+v"(ln));
-        item(by_xcd ? xcd + 8 * i : i, qb, *(const FwdArgs*)ap, ln);
+        item(head, qb, nhead, nqb_, has_next, *(const FwdArgs*)ap, ln);
+        t = t2; head = nhead; qb = nqb_; have = has_next;
     }
 }
 
