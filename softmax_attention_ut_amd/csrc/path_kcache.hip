@@ -81,7 +81,7 @@ __device__ __forceinline__ void stage_tile_k(bf16* dst, const bf16* src, int tid
 // from the first one any of its row chunks passes; a row chunk is carried
 // through those after its own chunk.
 template <int D>
-__global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs a) {
+__global__ __launch_bounds__(512, 2) void path_kcache_group_kernel(const KcacheArgs a) {
     constexpr int C = 64, PK = D + 8, PC = C + 8, G = kKcacheGroup, NID = D / 64, NT = 512;
     constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
     constexpr int NP = (G + NID + 3) / 4;
@@ -105,28 +105,24 @@ __global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs
     const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
     const bf16* zt = static_cast<const bf16*>(a.zt) + (size_t)head * N * D * C;
 
-    // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t
+    // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t; the
+    // carried key's bf16 B operand of k-step ks is packed from kacc where it
+    // is used (the input rows are bf16, so the first packing is exact)
     f32x16 kacc[DT];
-    bf16x8 kB[KSD];
     if (rc >= 0 && active) {
         const bf16* krow = kt + ((size_t)kc * C + jloc) * D;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
-            kB[ks] = ld8k(krow + 16 * ks + 8 * hh);
+            const bf16x8 k8 = ld8k(krow + 16 * ks + 8 * hh);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) kacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(kB[ks][t]);
+            for (int t = 0; t < 8; ++t) kacc[ks >> 1][8 * (ks & 1) + t] = static_cast<float>(k8[t]);
         }
     } else {
         const int r = (rc + NID) * C + jloc;      // identity row r
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) {
+        for (int ks = 0; ks < KSD; ++ks)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float e = (16 * ks + 8 * hh + t == r) ? 1.f : 0.f;
-                kacc[ks >> 1][8 * (ks & 1) + t] = e;
-                kB[ks][t] = static_cast<bf16>(e);
-            }
-        }
+            for (int t = 0; t < 8; ++t) kacc[ks >> 1][8 * (ks & 1) + t] = (16 * ks + 8 * hh + t == r) ? 1.f : 0.f;
     }
     for (int c = cfirst; c <= c1; ++c) {
         __syncthreads();
@@ -136,12 +132,15 @@ __global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs
         if (!active || c < start) continue;
         f32x16 x[2];
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
             for (int v = 0; v < 16; ++v) x[k2][v] = 0.f;
-            const bf16* aw = sW + (32 * k2 + l32) * PK + 8 * hh;
 #pragma unroll
-            for (int ks = 0; ks < KSD; ++ks) x[k2] = mfma32k(ld8k(aw + 16 * ks), kB[ks], x[k2]);
+        for (int ks = 0; ks < KSD; ++ks) {
+            const bf16x8 kb = pack8k(kacc[ks >> 1], ks & 1);
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+                x[k2] = mfma32k(ld8k(sW + (32 * k2 + l32) * PK + 8 * hh + 16 * ks), kb, x[k2]);
         }
         bf16x8 xB[KSC];
 #pragma unroll
@@ -152,15 +151,14 @@ __global__ __launch_bounds__(512) void path_kcache_group_kernel(const KcacheArgs
 #pragma unroll
             for (int ks = 0; ks < KSC; ++ks) kacc[dt] = mfma32k(ld8k(az + 16 * ks), xB[ks], kacc[dt]);
         }
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) kB[ks] = pack8k(kacc[ks >> 1], ks & 1);
     }
     if (!active) return;
     if (rc >= 0) {
         // Y_b over K~_b (the key rows are read once, at the start, by their own waves)
         bf16* yrow = kt + ((size_t)kc * C + jloc) * D;
 #pragma unroll
-        for (int ks = 0; ks < KSD; ++ks) *reinterpret_cast<bf16x8*>(yrow + 16 * ks + 8 * hh) = kB[ks];
+        for (int ks = 0; ks < KSD; ++ks)
+            *reinterpret_cast<bf16x8*>(yrow + 16 * ks + 8 * hh) = pack8k(kacc[ks >> 1], ks & 1);
     } else {
         // row r of T_g in fp32
         float* trow = a.tg + (((size_t)head * NG + g) * D + (rc + NID) * C + jloc) * D;
