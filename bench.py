@@ -492,7 +492,9 @@ def kcache_bytes_flops(B, H, L, d, C=64, G=8):
 def bench_kcache(args, cfg, torch, pa, inputs):
     """The prefill -> decode hand-off of a prefill + decode workload: the key
     cache H_{L-1} ... H_{j+1} k_j and the value cache after a prefill of L
-    tokens, one path_kcache_from_prefill per step."""
+    tokens, one path_kcache_from_prefill per step (the line's value), and the
+    same caches by path_kcache_from_forward from the prefill forward's
+    workspace (reported beside it)."""
     inp = inputs.generate_config(cfg)
     B, H, L, d, T = cfg.B, cfg.H, cfg.L, cfg.d, cfg.L_total
     g = {k: (None if t is None else t[:, :, :L].contiguous().cuda()) for k, t in vars(inp).items()}
@@ -520,6 +522,34 @@ def bench_kcache(args, cfg, torch, pa, inputs):
     ev_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     nbytes, flops = kcache_bytes_flops(B, H, L, d)
     gbs = nbytes / (ev_ms * 1e-3) / 1e9
+
+    # the same caches from the workspace of the prefill's forward pass (its K~
+    # and per-chunk -M^T): one forward fills the workspace, then the timed
+    # calls read it
+    fws = torch.empty(pa.path_attn_fwd_workspace_bytes(B, H, L, d, pa.PATH_BF16, 0),
+                      dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(g["q"])
+    lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    pa.path_attn_fwd(g["q"], g["k"], g["v"], g["w"], g["beta"], g["log_f"], out, lse, cfg.scale,
+                     0, fws, stream)
+    del out, lse
+
+    def step_fwd():
+        pa.path_kcache_from_forward(fws, g["v"], kc, vc, ws, stream)
+    for _ in range(args.warmup):
+        step_fwd()
+    torch.cuda.synchronize()
+    evf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for e in evf:
+        e[0].record(stream)
+        step_fwd()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ff_ms = sum(a.elapsed_time(b) for a, b in evf) / args.steps
+    # algorithmic bytes: K~ and -M^T read from the workspace, v read, both caches' L slots written
+    N = (L + 63) // 64
+    ff_bytes = B * H * (L * d * 2 * 4 + N * d * d * 2)
     res = {
         "metric": "PaTH prefill -> decode key-cache hand-off: ms and HBM GB/s",
         "value": ev_ms, "unit": "ms per hand-off (HIP events)",
@@ -538,6 +568,10 @@ def bench_kcache(args, cfg, torch, pa, inputs):
                                  if cfg.name == "d128_L8k_decode" else None),
                      "algorithmic_bytes_per_launch": nbytes,
                      "algorithmic_flops_per_launch": flops},
+        "from_forward": {"entry": "path_kcache_from_forward (after path_attn_fwd on the same inputs)",
+                         "ms": ff_ms, "achieved_GBps": ff_bytes / (ff_ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": ff_bytes / (ff_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_launch": ff_bytes},
     }
     return res, None
 

@@ -199,6 +199,29 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w,
                              void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * The same caches from the workspace of a path_attn_fwd (bf16, d in {64,
+ * 128}, default chunk) that has just run on the same k, w, beta (Dutch
+ * summary section 3, "Inferentie": the cache as above).  The forward's
+ * workspace holds every key carried to its chunk end and each chunk's whole
+ * product, so the keys' per-chunk transform is not computed again.
+ *
+ *   fwd_workspace  the forward's workspace, fwd_ws_bytes >=
+ *                  path_attn_fwd_workspace_bytes(B,H,L,d,dtype,0); read
+ *                  only.  Its contents must be those the forward wrote
+ *                  (the gate does not matter); nothing checks this.
+ *   v              [B][H][L][d] dtype, copied into v_cache.
+ *   k_cache, v_cache, T_max, B, H, L, d, dtype: as path_kcache_from_prefill.
+ *   workspace      >= path_kcache_workspace_bytes(B,H,L,d,dtype) bytes.
+ * Errors as path_kcache_from_prefill; a forward workspace that is null,
+ * too small or not 256-byte aligned: PATH_ERR_WORKSPACE.  The results agree
+ * with path_kcache_from_prefill to bf16 rounding (the chunk products enter
+ * as d x d bf16 tiles instead of W and T^-T W).
+ */
+int path_kcache_from_forward(const void* fwd_workspace, size_t fwd_ws_bytes, const void* v,
+                             void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                             int d, int dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Workspace size in bytes for path_decode_step, or 0 if invalid.
  */
 size_t path_decode_workspace_bytes(int B, int H, int T_max, int d, int dtype);

@@ -31,7 +31,8 @@ EXPORTS = ("path_status_string", "path_version", "path_attn_fwd_workspace_bytes"
            "path_decode_workspace_bytes", "path_decode_step", "path_fcache_from_prefill",
            "path_decode_step_gated", "path_transition_prep",
            "path_kcache_from_prefill_paged", "path_decode_step_paged",
-           "path_decode_step_noalloc", "path_attn_bwd_workspace_bytes", "path_attn_bwd")
+           "path_decode_step_noalloc", "path_attn_bwd_workspace_bytes", "path_attn_bwd",
+           "path_kcache_from_forward")
 
 
 class PathError(RuntimeError):
@@ -75,6 +76,8 @@ def load_library(path: str = LIB_PATH):
     lib.path_kcache_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.path_kcache_from_prefill.restype = I
     lib.path_kcache_from_prefill.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, S, P]
+    lib.path_kcache_from_forward.restype = I
+    lib.path_kcache_from_forward.argtypes = [P, S, P, P, P, I, I, I, I, I, I, P, S, P]
     lib.path_decode_workspace_bytes.restype = S
     lib.path_decode_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.path_decode_step.restype = I
@@ -208,6 +211,21 @@ def path_kcache_from_prefill(k, v, w, beta, k_cache, v_cache, workspace=None, st
                                       _p(v_cache), B, H, L, T_max, d, _dt(k),
                                       _p(workspace), ws_bytes, _stream(stream))
     _check(st, "path_kcache_from_prefill")
+
+
+def path_kcache_from_forward(fwd_workspace, v, k_cache, v_cache, workspace=None, stream=None):
+    """The caches from the workspace of a bf16 path_attn_fwd on the same k, w,
+    beta: v [B,H,L,d]; k_cache, v_cache [B,H,T_max,d]."""
+    lib = load_library()
+    _require_cuda(fwd_workspace, v, k_cache, v_cache, workspace)
+    B, H, L, d = v.shape
+    T_max = k_cache.shape[2]
+    fws_bytes = fwd_workspace.numel() * fwd_workspace.element_size()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.path_kcache_from_forward(_p(fwd_workspace), fws_bytes, _p(v), _p(k_cache),
+                                      _p(v_cache), B, H, L, T_max, d, _dt(v),
+                                      _p(workspace), ws_bytes, _stream(stream))
+    _check(st, "path_kcache_from_forward")
 
 
 def path_decode_workspace_bytes(B, H, T_max, d, dtype) -> int:
@@ -370,6 +388,20 @@ def kcache_from_prefill(k, v, w, beta, T_max, stream=None):
     kc = torch.zeros(B, H, T_max, d, dtype=k.dtype, device=k.device)
     vc = torch.zeros(B, H, T_max, d, dtype=k.dtype, device=k.device)
     path_kcache_from_prefill(k, v, w, beta, kc, vc, ws, stream)
+    return kc, vc
+
+
+def kcache_from_forward(fwd_workspace, v, T_max, stream=None):
+    """Key and value caches from the workspace of a bf16 forward on the same
+    k, w, beta (v is needed for the value cache)."""
+    B, H, L, d = v.shape
+    n = path_kcache_workspace_bytes(B, H, L, d, _dt(v))
+    if n == 0:
+        raise PathError(-2, "path_kcache_workspace_bytes")
+    ws = _workspace(n, v.device)
+    kc = torch.zeros(B, H, T_max, d, dtype=v.dtype, device=v.device)
+    vc = torch.zeros(B, H, T_max, d, dtype=v.dtype, device=v.device)
+    path_kcache_from_forward(fwd_workspace, v, kc, vc, ws, stream)
     return kc, vc
 
 

@@ -253,7 +253,7 @@ static int kcache_from_prefill(const void* k, const void* v, const void* w, cons
     u.zt = at(workspace, ws.zt);            // the hand-off needs K~ and Z only
     if (launch_path_ut_bf16(u, s) != hipSuccess) return PATH_ERR_HIP;
     KcacheArgs c{};
-    c.kt = u.kt; c.w = w; c.zt = u.zt; c.v = v;
+    c.kt = u.kt; c.kt_in = u.kt; c.w = w; c.zt = u.zt; c.v = v;
     c.k_cache = k_cache; c.v_cache = v_cache;
     c.BH = BH; c.L = L; c.N = N; c.T_max = T_max;
     c.NG = (N + kKcacheGroup - 1) / kKcacheGroup;
@@ -261,6 +261,42 @@ static int kcache_from_prefill(const void* k, const void* v, const void* w, cons
     c.rg = at(workspace, ws.rg);
     c.map = map;
     return launch_path_kcache(c, d, s) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
+}
+
+static int kcache_from_forward(const void* fwd_workspace, size_t fwd_ws_bytes, const void* v,
+                               void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                               int d, int dtype, void* workspace, size_t ws_bytes, void* stream,
+                               const CacheMap& map) {
+    int chunk = kBf16Chunk;
+    if (!valid_dtype(dtype)) return PATH_ERR_INVALID;
+    if (dtype != PATH_BF16) return PATH_ERR_UNSUPPORTED;
+    int st = check_fwd_shape(B, H, L, d, dtype, chunk);
+    if (st != PATH_OK) return st;
+    if (T_max < L) return PATH_ERR_INVALID;
+    if (!v || !k_cache || !v_cache) return PATH_ERR_INVALID;
+    // the forward's workspace: K~ and -M^T sit before the sections that the
+    // gate adds, so their offsets do not depend on it
+    const Workspace fw = fwd_plan(B, H, L, d, dtype, chunk, false, false);
+    const size_t fw_need = fwd_plan(B, H, L, d, dtype, chunk, true, false).total;   // path_attn_fwd_workspace_bytes
+    if (!fwd_workspace || !fw.mt || fwd_ws_bytes < fw_need) return PATH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(fwd_workspace) & 255) return PATH_ERR_WORKSPACE;
+    const Workspace ws = fwd_plan(B, H, L, d, dtype, chunk, false, true);
+    if (!workspace || ws_bytes < ws.total) return PATH_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255) return PATH_ERR_WORKSPACE;
+    const int BH = B * H, N = (L + chunk - 1) / chunk;
+    void* fwsp = const_cast<void*>(fwd_workspace);
+    KcacheArgs c{};
+    c.kt = at(workspace, ws.kt);
+    c.kt_in = at(fwsp, fw.kt);
+    c.mt = at(fwsp, fw.mt);
+    c.v = v;
+    c.k_cache = k_cache; c.v_cache = v_cache;
+    c.BH = BH; c.L = L; c.N = N; c.T_max = T_max;
+    c.NG = (N + kKcacheGroup - 1) / kKcacheGroup;
+    c.tg = reinterpret_cast<float*>(at(workspace, ws.tg));
+    c.rg = at(workspace, ws.rg);
+    c.map = map;
+    return launch_path_kcache(c, d, static_cast<hipStream_t>(stream)) == hipSuccess ? PATH_OK : PATH_ERR_HIP;
 }
 
 // 0 = ok: a page pool of num_blocks pages of `page` slots (a multiple of
@@ -283,6 +319,14 @@ int path_kcache_from_prefill(const void* k, const void* v, const void* w, const 
     const CacheMap map{nullptr, 0, 0, 0, H, T_max};
     return kcache_from_prefill(k, v, w, beta, k_cache, v_cache, B, H, L, T_max, d, dtype,
                                workspace, ws_bytes, stream, map);
+}
+
+int path_kcache_from_forward(const void* fwd_workspace, size_t fwd_ws_bytes, const void* v,
+                             void* k_cache, void* v_cache, int B, int H, int L, int T_max,
+                             int d, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    const CacheMap map{nullptr, 0, 0, 0, H, T_max};
+    return kcache_from_forward(fwd_workspace, fwd_ws_bytes, v, k_cache, v_cache, B, H, L, T_max,
+                               d, dtype, workspace, ws_bytes, stream, map);
 }
 
 int path_kcache_from_prefill_paged(const void* k, const void* v, const void* w,

@@ -64,53 +64,9 @@ __device__ __forceinline__ bf16x8 lds8(const bf16* p) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// PV A operands from a V tile kept as it is ([64 tokens][64 d], 16-byte units
-// swizzled by swz_v) with LDS transpose loads.  Within each
-// group of 16 lanes, ds_read_b64_tr_b16 gives lane i, element t, the element
-// i % 4 of the 8 bytes read by lane 4t + i/4.  So lane 4t + q reads 4
-// consecutive d of one token, and every lane receives one d column of four
-// tokens.  The permutations of the token (k-slot) and d (row) axes act on
-// blocks of four, which this access respects.  The operand of k-step ks, rows
-// dt, takes two loads (slots 0-3 and 4-7); a lane's 8 byte offsets depend
-// on (ks & 1, load, dt), the rows 32 (ks >> 1) further on add 4096 bytes.
-//
-// One transpose load reads 8 bytes per lane: lanes 0-31 cover 64 bytes of each
-// of 4 consecutive token rows, lanes 32-63 the next 4 rows (two 256-byte
-// halves; by quarters, 16 lanes cover 32 bytes of each of 4 rows).  The V
-// tile's swizzle gv(r) takes row bits 2, 0, 1 as unit bits 0, 1, 2: rows r
-// and r + 2 then differ in unit bit 2, so the four rows' pieces of either
-// half, or of any quarter, fall on distinct LDS banks (64 banks of 4 bytes
-// for a 32-lane half, 32 for a 16-lane quarter).  The swizzle of the other
-// tiles, made for 16-byte row reads, puts rows r and r + 2 on the same banks
-// here.
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
-__device__ __forceinline__ int swz_v(int r) {
-    return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2);
-}
-__device__ __forceinline__ void vtr_offsets(unsigned off[8], int lane) {
-    const int hh = lane >> 5, hp = (lane >> 4) & 1, j = lane & 15;
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-#pragma unroll
-        for (int ins = 0; ins < 2; ++ins)
-#pragma unroll
-            for (int dt = 0; dt < 2; ++dt) {
-                const int tok = permk(16 * par + 8 * hh + 4 * ins + (j >> 2));
-                const int d = permk(32 * dt + 16 * hp + 4 * (j & 3));
-                off[(par * 2 + ins) * 2 + dt] =
-                    static_cast<unsigned>((tok * 64 + (((d >> 3) ^ swz_v(tok)) << 3) + (d & 7)) * 2);
-            }
-}
-__device__ __forceinline__ bf16x8 pv_operand(const bf16* sv, const unsigned off[8], int dt, int ks) {
-    const char* base = reinterpret_cast<const char*>(sv) + 4096 * (ks >> 1);
-    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 0) * 2 + dt]));
-    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 1) * 2 + dt]));
-    const v4s both[2] = {lo, hi};
-    bf16x8 r;
-    __builtin_memcpy(&r, both, sizeof(r));
-    return r;
-}
+// The PV A operands of the d = 64 V tile (kept as it is, [64 tokens][64 d])
+// come from LDS transpose loads: swz_v, vtr_offsets and pv_operand in
+// path_internal.h.
 typedef __attribute__((address_space(1))) const void gbl_void;
 
 // Swizzled tile: 16-byte unit u of row r sits at unit u ^ g(r).  g keeps the

@@ -182,9 +182,11 @@ __device__ __forceinline__ long long cache_row(const CacheMap& c, int bh, int j)
 }
 
 struct KcacheArgs {
-    void* kt;              // keys carried to their chunk end (bf16), then to their group's end
-    const void* w;         // input w [BH][L][D]
-    const void* zt;
+    void* kt;              // keys carried to their group's end (bf16), Y
+    const void* kt_in;     // keys carried to their chunk end, K~ (the same buffer as kt, or the forward's)
+    const void* w;         // input w [BH][L][D] (rank-C form)
+    const void* zt;        // -Z^T tiles (rank-C form)
+    const void* mt;        // the forward's -M^T tiles [BH][N][D][D] (dense form), else null
     const void* v;         // input values [BH][L][D]
     void* k_cache;         // contiguous [BH][T_max][D] or a page pool (see map)
     void* v_cache;
@@ -296,5 +298,59 @@ constexpr size_t kDecodeScratchBytes = size_t(8) << 20;
 hipError_t decode_scratch(void** ptr);
 hipError_t launch_path_fcache(const FcacheArgs& a, hipStream_t s);
 hipError_t launch_path_transition(TransArgs a, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// A operands of a 32x32x16 bf16 MFMA that are the transpose of a tile kept
+// as it is: a [rows][64] bf16 tile T in LDS (rows of 128 bytes, 16-byte units
+// swizzled by swz_v) gives A[r][s] = T[permk(s)][permk(r)] for output row r
+// (32 dt + lane % 32) and k-slot s of k-step ks.  The d = 64 scan takes its
+// PV operand V^T this way from the V tile ([token][d]), and the key-cache
+// hand-off its -M operand from the -M^T tiles of the forward's workspace.
+//
+// Within each group of 16 lanes, ds_read_b64_tr_b16 gives lane i, element t,
+// the element i % 4 of the 8 bytes read by lane 4t + i/4.  So lane 4t + q
+// reads 4 consecutive columns of one row, and every lane receives one column
+// of four rows.  The permutations of the row (k-slot) and column (output row)
+// axes act on blocks of four, which this access respects.  The operand of
+// k-step ks, rows dt, takes two loads (slots 0-3 and 4-7); a lane's 8 byte
+// offsets depend on (ks & 1, load, dt), the rows 32 (ks >> 1) further on add
+// 4096 bytes.
+//
+// One transpose load reads 8 bytes per lane: lanes 0-31 cover 64 bytes of each
+// of 4 consecutive rows, lanes 32-63 the next 4 rows (two 256-byte halves; by
+// quarters, 16 lanes cover 32 bytes of each of 4 rows).  The swizzle gv(r)
+// takes row bits 2, 0, 1 as unit bits 0, 1, 2: rows r and r + 2 then differ
+// in unit bit 2, so the four rows' pieces of either half, or of any quarter,
+// fall on distinct LDS banks (64 banks of 4 bytes for a 32-lane half, 32 for
+// a 16-lane quarter).  The swizzle made for 16-byte row reads would put rows
+// r and r + 2 on the same banks here.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+__device__ __forceinline__ int swz_v(int r) {
+    return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2);
+}
+__device__ __forceinline__ void vtr_offsets(unsigned off[8], int lane) {
+    const int hh = lane >> 5, hp = (lane >> 4) & 1, j = lane & 15;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+#pragma unroll
+        for (int ins = 0; ins < 2; ++ins)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+                const int tok = permk(16 * par + 8 * hh + 4 * ins + (j >> 2));
+                const int d = permk(32 * dt + 16 * hp + 4 * (j & 3));
+                off[(par * 2 + ins) * 2 + dt] =
+                    static_cast<unsigned>((tok * 64 + (((d >> 3) ^ swz_v(tok)) << 3) + (d & 7)) * 2);
+            }
+}
+__device__ __forceinline__ bf16x8 pv_operand(const bf16* sv, const unsigned off[8], int dt, int ks) {
+    const char* base = reinterpret_cast<const char*>(sv) + 4096 * (ks >> 1);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 0) * 2 + dt]));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off[((ks & 1) * 2 + 1) * 2 + dt]));
+    const v4s both[2] = {lo, hi};
+    bf16x8 r;
+    __builtin_memcpy(&r, both, sizeof(r));
+    return r;
+}
 
 }  // namespace path

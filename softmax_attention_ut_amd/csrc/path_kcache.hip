@@ -7,6 +7,11 @@
 // acts on a key as
 //     k^T <- k^T P_c,   P_c = I - W_c^T Z_c,   Z_c = T_c^{-T} W_c
 // (the chunk's UT form), so the cached key is k~_j^T P_{b+1} ... P_{N-1}.
+// W_c^T Z_c = M_c^T with M_c = W_c^T T_c^{-1} W_c, the matrix whose I - M_c
+// carries the queries through chunk c in the forward: after a bf16 forward
+// on the same inputs its workspace holds K~ and -M_c^T for every chunk, and
+// path_kcache_from_forward starts from those (the dense form below) instead
+// of running path_ut again.
 //
 // The product of the later chunks is formed by suffix products over groups of
 // G = 8 chunks, O(L d^2) work in all (instead of carrying every key through
@@ -24,7 +29,10 @@
 // The carry (step 1) uses the query transport's layout and MFMA orientation
 // (the key rides in fp32 accumulators, K^T -= Z^T X^T with X^T = W K^T; -Z^T
 // comes from path_ut with its token axis in k-slot order and its d rows
-// permuted, so the key's registers hold d in natural order).  Steps 2 and 3
+// permuted, so the key's registers hold d in natural order).  In the dense
+// form it is K^T += (-M_c) K^T, 2 d^2 flops per key and chunk (the rank-C
+// form's 4 C d at d = 2C), with the A operand -M_c read as the transpose of
+// the stored -M_c^T tile by LDS transpose loads.  Steps 2 and 3
 // keep R_g as R_g^T with permuted rows, Rp[rho][c] = R_g[c][permk(rho)], in
 // two bf16 terms (hi, lo): Rp is the A operand of both products, which then
 // carry ~16 significant bits, and the output registers again hold d in
@@ -80,13 +88,16 @@ __device__ __forceinline__ void stage_tile_k(bf16* dst, const bf16* src, int tid
 // before the group's first chunk).  The workgroup walks the group's chunks
 // from the first one any of its row chunks passes; a row chunk is carried
 // through those after its own chunk.
-template <int D>
+template <int D, bool DENSE>
 __global__ __launch_bounds__(512, 2) void path_kcache_group_kernel(const KcacheArgs a) {
     constexpr int C = 64, PK = D + 8, PC = C + 8, G = kKcacheGroup, NID = D / 64, NT = 512;
     constexpr int DT = D / 32, KSD = D / 16, KSC = C / 16;
     constexpr int NP = (G + NID + 3) / 4;
-    __shared__ __attribute__((aligned(16))) bf16 sW[C * PK];
-    __shared__ __attribute__((aligned(16))) bf16 sZ[D * PC];
+    // rank-C form: W rows and Z^T; dense form: the chunk's -M^T as D / 64
+    // tiles [D][64] of its columns 64 h .. 64 h + 63 (rows swizzled by swz_v)
+    __shared__ __attribute__((aligned(16))) bf16 sW[DENSE ? 8 : C * PK];
+    __shared__ __attribute__((aligned(16))) bf16 sZ[DENSE ? 8 : D * PC];
+    __shared__ __attribute__((aligned(16))) bf16 sM[DENSE ? D * D : 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -101,16 +112,20 @@ __global__ __launch_bounds__(512, 2) void path_kcache_group_kernel(const KcacheA
     const int start = rc < 0 ? c0 : kc + 1;       // first chunk this row chunk passes
     const int cfirst = c0 + max(-NID + 4 * p + 1, 0);   // first chunk the workgroup needs
 
-    bf16* kt = static_cast<bf16*>(a.kt) + (size_t)head * Lp * D;
-    const bf16* win = static_cast<const bf16*>(a.w) + (size_t)head * L * D;
-    const bf16* zt = static_cast<const bf16*>(a.zt) + (size_t)head * N * D * C;
+    const bf16* kin = static_cast<const bf16*>(a.kt_in) + (size_t)head * Lp * D;   // K~ rows
+    bf16* kt = static_cast<bf16*>(a.kt) + (size_t)head * Lp * D;                   // Y rows
+    const bf16* win = DENSE ? nullptr : static_cast<const bf16*>(a.w) + (size_t)head * L * D;
+    const bf16* zt = DENSE ? nullptr : static_cast<const bf16*>(a.zt) + (size_t)head * N * D * C;
+    const bf16* mtg = DENSE ? static_cast<const bf16*>(a.mt) + (size_t)head * N * D * D : nullptr;
+    unsigned voff[8];
+    if (DENSE) vtr_offsets(voff, lane);
 
     // register 8s+t of kacc[dt] holds d = 32 dt + 16 s + 8 hh + t; the
     // carried key's bf16 B operand of k-step ks is packed from kacc where it
     // is used (the input rows are bf16, so the first packing is exact)
     f32x16 kacc[DT];
     if (rc >= 0 && active) {
-        const bf16* krow = kt + ((size_t)kc * C + jloc) * D;
+        const bf16* krow = kin + ((size_t)kc * C + jloc) * D;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
             const bf16x8 k8 = ld8k(krow + 16 * ks + 8 * hh);
@@ -126,10 +141,50 @@ __global__ __launch_bounds__(512, 2) void path_kcache_group_kernel(const KcacheA
     }
     for (int c = cfirst; c <= c1; ++c) {
         __syncthreads();
-        stage_rows_k<C, D, PK, NT>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
-        stage_tile_k<D, C, PC, NT>(sZ, zt + (size_t)c * D * C, tid);
+        if constexpr (DENSE) {
+            // every load first, then the stores (the loads' latencies overlap)
+            constexpr int UM = D * D / 8 / NT;
+            static_assert(UM * NT * 8 == D * D, "whole 16-byte units per thread");
+            const bf16* src = mtg + (size_t)c * D * D;
+            uint4 m[UM];
+#pragma unroll
+            for (int i = 0; i < UM; ++i) m[i] = *reinterpret_cast<const uint4*>(src + (size_t)(tid + NT * i) * 8);
+#pragma unroll
+            for (int i = 0; i < UM; ++i) {
+                const int u = tid + NT * i, r = u / (D / 8), cu = u % (D / 8);
+                *reinterpret_cast<uint4*>(sM + (cu >> 3) * D * 64 + r * 64 + (((cu & 7) ^ swz_v(r)) << 3)) = m[i];
+            }
+        } else {
+            stage_rows_k<C, D, PK, NT>(sW, win + (size_t)c * C * D, min(C, L - c * C), tid);
+            stage_tile_k<D, C, PC, NT>(sZ, zt + (size_t)c * D * C, tid);
+        }
         __syncthreads();
         if (!active || c < start) continue;
+        if constexpr (DENSE) {
+            // K^T += (-M) K^T with the old K^T as the B operand; the A operand
+            // A[rho][c] = -M[permk(rho)][c] = mt[permk(c)][permk(rho)] is the
+            // transpose of the stored tile (rows rho of the accumulators hold
+            // d = permk(rho), i.e. natural d in register order)
+            bf16x8 kb[KSD];
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                kb[ks] = pack8k(kacc[ks >> 1], ks & 1);
+                // packed here, before the first product overwrites kacc (the
+                // compiler would otherwise pack each one at its first use and
+                // keep a second copy of the accumulators live until then)
+                asm volatile("" : "+v"(kb[ks]));
+            }
+#pragma unroll
+            for (int ks = 0; ks < KSD; ++ks) {
+                bf16x8 am[DT];
+#pragma unroll
+                for (int rt = 0; rt < DT; ++rt) am[rt] = pv_operand(sM + (rt >> 1) * D * 64, voff, rt & 1, ks);
+#pragma unroll
+                for (int rt = 0; rt < DT; ++rt) kacc[rt] = mfma32k(am[rt], kb[ks], kacc[rt]);
+                __builtin_amdgcn_sched_barrier(0);      // one k-step's operands live at a time
+            }
+            continue;
+        }
         f32x16 x[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2)
@@ -373,14 +428,17 @@ __global__ __launch_bounds__(256, 2) void path_kcache_apply_kernel(const KcacheA
 
 hipError_t launch_path_kcache(const KcacheArgs& a, int D, hipStream_t s) {
     const int NG = a.NG;
+    const bool dense = a.mt != nullptr;
     if (D == 64) {
         constexpr int NP = (kKcacheGroup + 1 + 3) / 4;
-        hipLaunchKernelGGL(path_kcache_group_kernel<64>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        if (dense) hipLaunchKernelGGL((path_kcache_group_kernel<64, true>), dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((path_kcache_group_kernel<64, false>), dim3(a.BH * NG * NP), dim3(512), 0, s, a);
         hipLaunchKernelGGL(path_kcache_suffix_kernel<64>, dim3(a.BH * suffix_blocks(64) + kValueCopyBlocks), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<64>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else if (D == 128) {
         constexpr int NP = (kKcacheGroup + 2 + 3) / 4;
-        hipLaunchKernelGGL(path_kcache_group_kernel<128>, dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        if (dense) hipLaunchKernelGGL((path_kcache_group_kernel<128, true>), dim3(a.BH * NG * NP), dim3(512), 0, s, a);
+        else hipLaunchKernelGGL((path_kcache_group_kernel<128, false>), dim3(a.BH * NG * NP), dim3(512), 0, s, a);
         hipLaunchKernelGGL(path_kcache_suffix_kernel<128>, dim3(a.BH * suffix_blocks(128) + kValueCopyBlocks), dim3(256), 0, s, a);
         hipLaunchKernelGGL(path_kcache_apply_kernel<128>, dim3(a.BH * NG), dim3(256), 0, s, a);
     } else {

@@ -165,6 +165,23 @@ def test_kcache_argument_errors_before_launch():
                                         p, ws - 1, None) == -4
 
 
+def test_kcache_from_forward_argument_errors_before_launch():
+    lib = pa.load_library()
+    p = ctypes.c_void_p(4096)
+    ws = lib.path_kcache_workspace_bytes(1, 1, 128, 64, pa.PATH_BF16)
+    fws = lib.path_attn_fwd_workspace_bytes(1, 1, 128, 64, pa.PATH_BF16, 0)
+    f = lib.path_kcache_from_forward
+    assert f(p, fws, p, p, p, 1, 1, 128, 100, 64, pa.PATH_BF16, p, ws, None) == -1   # T_max < L
+    assert f(p, fws, p, p, p, 1, 1, 128, 200, 64, pa.PATH_F32, p, ws, None) == -2
+    assert f(p, fws, p, p, p, 1, 1, 128, 200, 32, pa.PATH_BF16, p, ws, None) == -2   # d = 32
+    assert f(p, fws, None, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16, p, ws, None) == -1
+    assert f(None, fws, p, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16, p, ws, None) == -4
+    assert f(p, fws - 1, p, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16, p, ws, None) == -4
+    assert f(ctypes.c_void_p(4096 + 16), fws, p, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16, p, ws,
+             None) == -4                                                            # not 256-aligned
+    assert f(p, fws, p, p, p, 1, 1, 128, 200, 64, pa.PATH_BF16, p, ws - 1, None) == -4
+
+
 def test_transition_argument_errors_before_launch():
     """Every call here is rejected on the host (fake pointers are never
     dereferenced): null pointers and sizes below 1 are invalid, shapes outside

@@ -266,10 +266,15 @@ def _prefill_decode_whole(cfg):
     fut = _oracle_bg(inp, cfg.scale, Lcache=L)
     out, lse = _run_fwd(inp, cfg.scale, L=L)
     dec = _decode_gpu(inp, cfg.scale, L, T)
+    kf, vf = _kcache_from_forward(inp, cfg.scale, L, T)
     ro, rl, rkc, used = fut.result()
     BH, d = cfg.B * cfg.H, cfg.d
     ro, rl = ro.reshape(BH, T, d), rl.reshape(BH, T)
     print(f"{cfg.name}: oracle on {used} threads", flush=True)
+    _check_cache(kf[:, :L], rkc.reshape(BH, L, d), inp.k.double().numpy().reshape(BH, -1, d)[:, :L],
+                 f"{cfg.name} kcache from the forward's workspace (every key)", (L + 63) // 64 + 2)
+    assert np.array_equal(vf[:, :L], dec["vc_pre"])
+    del kf, vf
     _check(out.reshape(BH, L, d), ro[:, :L], "bf16", f"{cfg.name} prefill whole out")
     _check(lse.reshape(BH, L), rl[:, :L], "bf16", f"{cfg.name} prefill whole lse")
     del out, lse
@@ -287,6 +292,54 @@ def test_fox_d128_prefill_kcache_and_gated_decode():
     """The PaTH-FoX variant of the d=128 workload (forget gate): gated
     prefill, key cache, gate cache and 256 gated decode steps, whole."""
     _prefill_decode_whole(CONFIGS["fox_d128_L8k_decode"])
+
+
+def _kcache_from_forward(inp, scale, L, T):
+    """A bf16 forward over the first L tokens with an explicit workspace, then
+    path_kcache_from_forward from that workspace.  Returns the key and value
+    caches (host, [B*H][T][d])."""
+    g = _dev(inp)
+    B, H, _, d = inp.q.shape
+    pre = lambda t: None if t is None else t[:, :, :L].contiguous()
+    n = pa.path_attn_fwd_workspace_bytes(B, H, L, d, pa.PATH_BF16, 0)
+    fws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, H, L, d, dtype=g["q"].dtype, device="cuda")
+    lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
+    pa.path_attn_fwd(pre(g["q"]), pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]),
+                     pre(g["log_f"]), out, lse, scale, 0, fws)
+    kc, vc = pa.kcache_from_forward(fws, pre(g["v"]), T)
+    torch.cuda.synchronize()
+    return (kc.double().cpu().numpy().reshape(B * H, T, d),
+            vc.double().cpu().numpy().reshape(B * H, T, d))
+
+
+@pytest.mark.parametrize("L", [64, 700, 1100])
+@pytest.mark.parametrize("gate", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_kcache_from_forward_workspace(L, gate, d):
+    """path_kcache_from_forward after a bf16 forward on the same inputs: every
+    cached key against the oracle's transported keys (the bound of the
+    prefill hand-off), the values copied exactly, the slots past L untouched,
+    and the keys of path_kcache_from_prefill for comparison.  L = 1100: 18
+    chunks, a ragged last chunk and a partial last group of eight chunks."""
+    B, H, T = 1, 3, L + 40
+    inp = generate(B, H, L, d, dtype="bf16", gate=gate, seed=50 + L + d)
+    BH = B * H
+    kf, vf = _kcache_from_forward(inp, 1 / math.sqrt(d), L, T)
+    g = _dev(inp)
+    kcp, _ = pa.kcache_from_prefill(g["k"], g["v"], g["w"], g["beta"], T)
+    kp = kcp.double().cpu().numpy().reshape(BH, T, d)
+    hi = np.repeat(np.arange(BH), L)
+    ki = np.tile(np.arange(L), BH)
+    ref = oracle.transported_keys(inp.k, inp.w, inp.beta, L - 1, hi, ki).reshape(BH, L, d)
+    k_in = inp.k.double().numpy().reshape(BH, L, d)
+    n_chunks = (L + 63) // 64
+    _check_cache(kf[:, :L], ref, k_in, f"kcache from the forward, d={d} L={L} gate={gate}",
+                 n_chunks + 2)
+    _check_cache(kp[:, :L], ref, k_in, f"kcache from the prefill, d={d} L={L} gate={gate}",
+                 n_chunks + 2)
+    assert np.array_equal(vf[:, :L], inp.v.double().numpy().reshape(BH, L, d))
+    assert not np.any(kf[:, L:]) and not np.any(vf[:, L:])
 
 
 def _decode_gpu(inp, scale, L, T):
