@@ -296,8 +296,8 @@ def test_fox_d128_prefill_kcache_and_gated_decode():
 
 def _kcache_from_forward(inp, scale, L, T):
     """A bf16 forward over the first L tokens with an explicit workspace, then
-    path_kcache_from_forward from that workspace.  Returns the key and value
-    caches (host, [B*H][T][d])."""
+    path_kcache_from_forward from that workspace, which must leave it as it
+    was.  Returns the key and value caches (host, [B*H][T][d])."""
     g = _dev(inp)
     B, H, _, d = inp.q.shape
     pre = lambda t: None if t is None else t[:, :, :L].contiguous()
@@ -307,8 +307,10 @@ def _kcache_from_forward(inp, scale, L, T):
     lse = torch.empty(B, H, L, dtype=torch.float32, device="cuda")
     pa.path_attn_fwd(pre(g["q"]), pre(g["k"]), pre(g["v"]), pre(g["w"]), pre(g["beta"]),
                      pre(g["log_f"]), out, lse, scale, 0, fws)
+    fws_before = fws.clone()
     kc, vc = pa.kcache_from_forward(fws, pre(g["v"]), T)
     torch.cuda.synchronize()
+    assert torch.equal(fws, fws_before), "the forward's workspace was modified"
     return (kc.double().cpu().numpy().reshape(B * H, T, d),
             vc.double().cpu().numpy().reshape(B * H, T, d))
 
